@@ -1,0 +1,170 @@
+"""Seeded synthetic inputs for the Gated Delta Rule (shared by tests and bench).
+
+This module draws inputs only; it contains none of the operator's arithmetic.
+Both the fp64 oracle and the GPU path receive the *same* host tensors (the
+GPU side copies them to the device), so parity compares like with like.
+
+Recipe (numpy PCG64, seeded): values are drawn in fp64 and cast once to the
+storage dtype (bf16 or fp32) with torch's round-to-nearest-even conversion.
+Distributions follow the pages' workloads:
+  * prefill ("Qwen3Next Samples" page, Parameter Description / Supported
+    Configurations): q, k, v ~ N(0,1); beta = sigmoid(N(0,1)); gate
+    g = -U(0.001, 0.1) per token and value head; initial state zeros or
+    N(0, 0.02^2); D = 128.
+  * decode ("lite_boost.ops.recurrent_gated_delta_rule" page, example):
+    q, k drawn N(0,1) and L2-normalised in fp64 before the bf16 cast (the
+    operator requires unit-norm q and k from its caller); v ~ N(0,1);
+    beta = U(0.05, 0.95); g = -U(0.01, 1.01); gk = -U(0.01, 1.01);
+    state pool ~ N(0, 0.02^2).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+SCALE_128 = 1.0 / math.sqrt(128.0)
+
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+
+
+def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(x)).to(_TORCH_DTYPE[dtype]).contiguous()
+
+
+def _normal_blocks(rng, shape, std=1.0, dtype="bf16", block_rows=8192):
+    """N(0, std^2) of `shape`, drawn in fp64 block by block along axis 0 (to
+    bound host memory for the long-context workload), cast per block."""
+    out = torch.empty(shape, dtype=_TORCH_DTYPE[dtype])
+    for r0 in range(0, shape[0], block_rows):
+        r1 = min(shape[0], r0 + block_rows)
+        out[r0:r1] = _cast(rng.standard_normal((r1 - r0,) + tuple(shape[1:])) * std, dtype)
+    return out
+
+
+def _sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128, act: str = "bf16",
+                   init_state: str = "randn", scale: float | None = None):
+    """Packed varlen prefill inputs.
+
+    Returns a dict of CPU tensors: q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv]
+    (act dtype); g [T,Nv] fp32; state_in [B,Nv,D,D] fp32 or None;
+    cu_seqlens [B+1] int32; plus scale, T, B, Nqk, Nv, D, act.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seq_lens = [int(x) for x in seq_lens]
+    B = len(seq_lens)
+    T = int(sum(seq_lens))
+    cu = np.zeros(B + 1, np.int32)
+    cu[1:] = np.cumsum(seq_lens)
+    q = _normal_blocks(rng, (T, Nqk, D), dtype=act)
+    k = _normal_blocks(rng, (T, Nqk, D), dtype=act)
+    v = _normal_blocks(rng, (T, Nv, D), dtype=act)
+    beta = _cast(_sigmoid(rng.standard_normal((T, Nv))), act)
+    g = _cast(-rng.uniform(0.001, 0.1, (T, Nv)), "fp32")
+    if init_state == "zeros":
+        state_in = None
+    elif init_state == "randn":
+        state_in = _normal_blocks(rng, (B, Nv, D, D), std=0.02, dtype="fp32", block_rows=1)
+    else:
+        raise ValueError(init_state)
+    return dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in,
+                cu_seqlens=torch.from_numpy(cu), scale=SCALE_128 if scale is None else scale,
+                T=T, B=B, Nqk=Nqk, Nv=Nv, D=D, act=act)
+
+
+def _unit_rows(rng, shape):
+    x = rng.standard_normal(shape)
+    return x / np.linalg.norm(x, axis=-1, keepdims=True)
+
+
+def decode_inputs(seed: int, B: int, S: int, Nk: int, Nv: int, Dk: int, Dv: int, num_slots: int,
+                  with_gk: bool = False, lens: str = "full", routing: str = "one_slot",
+                  act: str = "bf16", state: str = "bf16", scale: float | None = None):
+    """Recurrent-decode inputs over a slot pool.
+
+    lens:    "full" (every row has S valid tokens) or "random" (U{1..S}).
+    routing: "one_slot"  -- row b uses one slot for all its tokens, the first
+                            B entries of a seeded permutation of the slots;
+             "two_slots" -- row b owns slots {pi[2b], pi[2b+1]} of a seeded
+                            permutation and each valid token picks one of the
+                            two at random (collision-free across rows).
+    Padded token positions (t >= len_b) get index -1 and zero-valued inputs.
+    Returns a dict of CPU tensors: q, k [B,Nk,S,Dk]; v [B,Nv,S,Dv];
+    beta [B,Nv,S]; g [B,Nv,S] fp32; gk [B,Nv,S,Dk] fp32 or None;
+    pool [slots,Nv,Dk,Dv]; idx [B*S] int32; lens [B] int32; scale.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q = _cast(_unit_rows(rng, (B, Nk, S, Dk)), act)
+    k = _cast(_unit_rows(rng, (B, Nk, S, Dk)), act)
+    v = _cast(rng.standard_normal((B, Nv, S, Dv)), act)
+    beta = _cast(rng.uniform(0.05, 0.95, (B, Nv, S)), act)
+    g = _cast(-rng.uniform(0.01, 1.01, (B, Nv, S)), "fp32")
+    gk = _cast(-rng.uniform(0.01, 1.01, (B, Nv, S, Dk)), "fp32") if with_gk else None
+    pool = _normal_blocks(rng, (num_slots, Nv, Dk, Dv), std=0.02, dtype=state, block_rows=1)
+    if lens == "full":
+        ln = np.full(B, S, np.int32)
+    elif lens == "random":
+        ln = rng.integers(1, S + 1, B).astype(np.int32)
+    else:
+        raise ValueError(lens)
+    perm = rng.permutation(num_slots).astype(np.int32)
+    idx = np.full((B, S), -1, np.int32)
+    if routing == "one_slot":
+        if num_slots < B:
+            raise ValueError("one_slot routing needs num_slots >= B")
+        for b in range(B):
+            idx[b, :ln[b]] = perm[b]
+    elif routing == "two_slots":
+        if num_slots < 2 * B:
+            raise ValueError("two_slots routing needs num_slots >= 2B")
+        pick = rng.integers(0, 2, (B, S))
+        for b in range(B):
+            idx[b, :ln[b]] = perm[2 * b + pick[b, :ln[b]]]
+    else:
+        raise ValueError(routing)
+    # padded tokens carry zero-valued inputs (they are never read)
+    for b in range(B):
+        if ln[b] < S:
+            q[b, :, ln[b]:] = 0
+            k[b, :, ln[b]:] = 0
+            v[b, :, ln[b]:] = 0
+            beta[b, :, ln[b]:] = 0
+            g[b, :, ln[b]:] = 0
+            if gk is not None:
+                gk[b, :, ln[b]:] = 0
+    return dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, pool=pool,
+                idx=torch.from_numpy(idx.reshape(-1).copy()), lens=torch.from_numpy(ln),
+                scale=SCALE_128 if scale is None else scale,
+                B=B, S=S, Nk=Nk, Nv=Nv, Dk=Dk, Dv=Dv, num_slots=num_slots, act=act, state=state)
+
+
+# The five workloads the operator is measured on.  configs 1 and 2 (and the
+# decode ones) are small enough for full parity; 5 is parity-checked on
+# sampled heads.
+def config_inputs(n: int):
+    if n == 1:
+        return prefill_inputs(1, [256], Nqk=2, Nv=4, act="fp32", init_state="zeros")
+    if n == 2:
+        return prefill_inputs(2, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16")
+    if n == 3:
+        return decode_inputs(3, B=256, S=1, Nk=16, Nv=32, Dk=128, Dv=128, num_slots=512)
+    if n == 4:
+        return decode_inputs(4, B=64, S=4, Nk=64, Nv=64, Dk=64, Dv=512, num_slots=128,
+                             with_gk=True, lens="random", routing="two_slots")
+    if n == 5:
+        return prefill_inputs(5, [131072], Nqk=16, Nv=32, act="bf16")
+    raise ValueError(n)
+
+
+CONFIG_NAMES = {
+    1: "prefill T=256 Nqk=2 Nv=4 D=128 fp32",
+    2: "prefill varlen B=4 lens=[1000,4096,300,2796] T=8192 Nqk=16 Nv=32 D=128 bf16",
+    3: "decode B=256 S=1 Nk=16 Nv=32 Dk=Dv=128 bf16 pool 512 slots",
+    4: "decode B=64 S=4 (lens U{1..4}) Nk=Nv=64 Dk=64 Dv=512 gk, bf16 pool 128 slots",
+    5: "prefill long-context B=1 T=131072 Nqk=16 Nv=32 D=128 bf16",
+}
