@@ -125,7 +125,7 @@ def test_decode_out_of_range_indices_stay_in_bounds():
     ref_pool[0] = 0   # row 0 starts from zeros: emulate with a zero slot 0 and index 0
     ref.update(pool=ref_pool, idx=torch.tensor([0, 1, 2, 2], dtype=torch.int32))
     out_ref, pool_ref = run_oracle(ref)
-    assert_out_close(out, out_ref, False, "oob out", tol=1e-5)
+    assert_out_close(out, out_ref, True, "oob out")
     assert_state_close(pool[1], pool_ref[1], "oob state slot 1", tol=1e-5)
 
 
