@@ -1,0 +1,285 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated Delta Rule hot path on one MI355X (gfx950).
+
+One step = one gdr_chunk_prefill call (chunk map, intra-chunk kernel, state
+scan, output kernel) on the varlen prefill workload B=4, lengths
+[1000, 4096, 300, 2796] (T = 8192), Nqk = 16, Nv = 32, D = 128, bf16
+activations, fp32 states.  `value` is prefill tokens per second with inputs
+resident in HBM.  The same run also times gdr_recurrent_decode on the decode
+workload B=256 x 1 token, Nk=16, Nv=32, Dk=Dv=128, bf16 pool of 512 slots
+(reported under "decode").
+
+Timing: W untimed warm-up steps, then K steps bracketed by
+torch.cuda.synchronize() on both sides, wall clock.  Inputs rotate over
+--sets device copies (default 4, about 0.9 GB for prefill and 2 GiB of
+pools for decode) so that the 256 MB Infinity Cache cannot hold one step's
+inputs until the next.  Per-kernel durations come from hipEvents that the
+library records around each kernel on the launch stream over the timed
+region (gdr_timing_*).
+
+Roofline: algorithmic flops per kernel (MFMA-bound kernels, fp16 dense peak
+2.5 PFLOP/s) or algorithmic bytes (HBM-bound decode, 8 TB/s); the formulas
+are in flops_prefill() / bytes_decode() below.  `traffic` is the HBM byte
+count of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
+runs recorded in profiles/counters.json, reported only while the kernel's
+source file is unchanged since those counters were taken.
+
+cpu_baseline: the fp64 oracle (test infrastructure, one call on the full
+workload, timed on this host's cores) -- a reported baseline, not a target.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+MFMA_PEAK_FP16 = 2.5e15     # MI355X dense fp16/bf16 MFMA, FLOP/s
+HBM_PEAK = 8.0e12           # MI355X HBM3E, B/s
+D = 128
+L = 128
+KERNEL_SOURCES = {
+    "gdr_chunkmap": "gated_delta_rule_chunk_amd/csrc/gdr_prefill.hip",
+    "gdr_intra": "gated_delta_rule_chunk_amd/csrc/gdr_prefill.hip",
+    "gdr_scan": "gated_delta_rule_chunk_amd/csrc/gdr_prefill.hip",
+    "gdr_output": "gated_delta_rule_chunk_amd/csrc/gdr_prefill.hip",
+    "gdr_decode": "gated_delta_rule_chunk_amd/csrc/gdr_decode.hip",
+}
+
+
+def chunk_rows(seq_lens):
+    """Valid rows r of every 128-token chunk."""
+    rows = []
+    for n in seq_lens:
+        rows += [min(L, n - s) for s in range(0, n, L)]
+    return rows
+
+
+def flops_prefill(seq_lens, Nqk, Nv):
+    """Algorithmic flops of each prefill kernel, per call.
+
+    Per chunk of r rows: intra  = Nv (2 r^2 D + r^3 / 3) + Nqk r^2 D
+                                  (u, w: triangular r x r by r x D; the solve;
+                                  lower half of the shared Gram k^ k^T)
+                         scan   = Nv 4 r D^2   (w S and k^T v_new)
+                         output = Nv (2 r D^2 + r^2 D) + Nqk r^2 D
+                                  ((q^ e^g) S, P v_new, lower half of q^ k^T)
+    Their sum is 6 r D^2 + 3 r^2 D + r^3/3 per value head plus 2 r^2 D per
+    qk head.
+    """
+    f = {"gdr_chunkmap": 0.0, "gdr_intra": 0.0, "gdr_scan": 0.0, "gdr_output": 0.0}
+    for r in chunk_rows(seq_lens):
+        f["gdr_intra"] += Nv * (2 * r * r * D + r ** 3 / 3) + Nqk * r * r * D
+        f["gdr_scan"] += Nv * 4 * r * D * D
+        f["gdr_output"] += Nv * (2 * r * D * D + r * r * D) + Nqk * r * r * D
+    return f
+
+
+def bytes_prefill(T, B, Nqk, Nv, act_bytes=2):
+    """Algorithmic HBM bytes of a prefill call: q, k, v, beta, out in the
+    activation dtype, g fp32, state in and out fp32."""
+    return (T * (2 * Nqk + 2 * Nv) * D + T * Nv) * act_bytes + T * Nv * 4 + 2 * B * Nv * D * D * 4
+
+
+def bytes_decode(inp):
+    """Algorithmic HBM bytes of a decode call: every read slab once, every
+    distinct written slab once, plus the valid tokens' activations."""
+    import numpy as np
+    B, S, Nk, Nv, Dk, Dv = (inp[k] for k in ("B", "S", "Nk", "Nv", "Dk", "Dv"))
+    sb = 2 if inp["state"] == "bf16" else 4
+    ab = 2 if inp["act"] == "bf16" else 4
+    idx = inp["idx"].numpy().reshape(B, S)
+    lens = inp["lens"].numpy()
+    slab = Nv * Dk * Dv * sb
+    state = sum(slab * (1 + len(set(idx[b, :lens[b]].tolist()))) for b in range(B) if lens[b] > 0)
+    ntok = int(lens.sum())
+    act = ntok * (2 * Nk * Dk * ab + Nv * Dv * ab + Nv * ab + Nv * 4 + Nv * Dv * ab)
+    if inp["gk"] is not None:
+        act += ntok * Nv * Dk * 4
+    return state + act + B * 4 + B * S * 4
+
+
+def source_hash(path):
+    return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch from the committed counter runs, or None if the
+    kernel's source changed since they were taken."""
+    p = os.path.join(ROOT, "profiles", "counters.json")
+    if not os.path.exists(p):
+        return None
+    rec = json.load(open(p)).get(kernel)
+    if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def timed(fn, steps, warmup, gdr, torch):
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    gdr.timing_read()            # discard warm-up records
+    gdr.timing_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    dt = time.perf_counter() - t0
+    gdr.timing_enable(False)
+    per_kernel = gdr.timing_read()
+    return dt, per_kernel
+
+
+def roofline(name, avg_s, flops=None, nbytes=None):
+    if flops is not None:
+        a = flops / avg_s
+        return {"bound": "mfma", "achieved": a / 1e12, "peak": MFMA_PEAK_FP16 / 1e12, "unit": "TFLOP/s",
+                "frac": a / MFMA_PEAK_FP16, "traffic": counter_traffic(name), "kernel": name}
+    a = nbytes / avg_s
+    return {"bound": "hbm", "achieved": a / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": a / HBM_PEAK,
+            "traffic": counter_traffic(name), "kernel": name}
+
+
+def bench_prefill(args, gdr, torch, workloads):
+    inp = workloads.config_inputs(2)
+    dev = "cuda:0"
+    base = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    names = ("q", "k", "v", "g", "beta", "state_in")
+    sets = [base] + [dict(base, **{n: base[n].clone() for n in names}) for _ in range(args.sets - 1)]
+    T, B, Nqk, Nv = inp["T"], inp["B"], inp["Nqk"], inp["Nv"]
+    out = torch.empty((T, Nv, D), dtype=torch.bfloat16, device=dev)
+    st = torch.empty((B, Nv, D, D), dtype=torch.float32, device=dev)
+    ws = torch.empty(gdr.chunk_prefill_workspace_size(T, B, Nqk, Nv), dtype=torch.uint8, device=dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        gdr.chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"], s["scale"],
+                          state_in=s["state_in"], out=out, state_out=st, workspace=ws)
+
+    dt, per = timed(step, args.steps, args.warmup, gdr, torch)
+    seq_lens = [1000, 4096, 300, 2796]
+    fl = flops_prefill(seq_lens, Nqk, Nv)
+    kernels = {}
+    for name in fl:
+        ms, n = per[name]
+        avg = ms / 1e3 / max(n, 1)
+        kernels[name] = {"avg_us": avg * 1e6, "launches": n, "alg_gflop": fl[name] / 1e9,
+                         "mfma_frac": (fl[name] / avg / MFMA_PEAK_FP16) if avg > 0 and fl[name] else None}
+    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
+    dom_avg = kernels[dominant]["avg_us"] / 1e6
+    step_s = dt / args.steps
+    f_total = sum(fl.values())
+    b_total = bytes_prefill(T, B, Nqk, Nv)
+    return dict(inp=inp, step_s=step_s, tok_s=T / step_s, kernels=kernels,
+                roofline=roofline(dominant, dom_avg, flops=fl[dominant]),
+                path={"alg_gflop": f_total / 1e9, "mfma_frac": f_total / step_s / MFMA_PEAK_FP16,
+                      "alg_bytes_mb": b_total / 1e6, "hbm_frac": b_total / step_s / HBM_PEAK})
+
+
+def bench_decode(args, gdr, torch, workloads):
+    inp = workloads.config_inputs(3)
+    dev = "cuda:0"
+    base = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    names = ("q", "k", "v", "g", "beta", "pool")
+    sets = [base] + [dict(base, **{n: base[n].clone() for n in names}) for _ in range(args.sets - 1)]
+    out = torch.empty((inp["B"], inp["Nv"], inp["S"], inp["Dv"]), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        gdr.recurrent_decode(s["q"], s["k"], s["v"], s["g"], s["gk"], s["beta"], s["pool"], s["idx"],
+                             s["lens"], s["scale"], out=out)
+
+    steps = max(args.steps * 4, 20)
+    dt, per = timed(step, steps, args.warmup, gdr, torch)
+    ms, n = per["gdr_decode"]
+    avg = ms / 1e3 / max(n, 1)
+    nb = bytes_decode(inp)
+    ntok = int(inp["lens"].sum())
+    return dict(inp=inp, step_s=dt / steps, steps=steps, tok_s=ntok / (dt / steps), kernel_avg_us=avg * 1e6,
+                roofline=roofline("gdr_decode", avg, nbytes=nb), alg_bytes_mb=nb / 1e6)
+
+
+def cpu_baseline_prefill(inp):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["state_in"], inp["cu_seqlens"],
+                   inp["scale"])
+    dt = time.perf_counter() - t0
+    return {"value": inp["T"] / dt, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one fp64 oracle call on the whole workload (T={inp['T']}, all {inp['Nv']} value "
+                      f"heads): {dt:.2f} s wall"}
+
+
+def cpu_baseline_decode(inp):
+    import oracle
+    t0 = time.perf_counter()
+    oracle.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["gk"], inp["beta"], inp["pool"], inp["idx"],
+                  inp["lens"], inp["scale"], round_state_bf16=True)
+    dt = time.perf_counter() - t0
+    ntok = int(inp["lens"].sum())
+    return {"value": ntok / dt, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"one fp64 oracle call on the whole workload ({ntok} tokens x {inp['Nv']} heads): "
+                      f"{dt:.2f} s wall"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4, help="rotating device copies of the inputs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this operator is measured on one GPU only (got --gpus {args.gpus}); "
+              "run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import gated_delta_rule_chunk_amd as gdr
+    import workloads
+
+    gdr.lib()
+    pre = bench_prefill(args, gdr, torch, workloads)
+    dec = bench_decode(args, gdr, torch, workloads)
+    inp = pre["inp"]
+    line = {
+        "metric": "GDR prefill tok/s (T=8192) + decode tok/s; % MFMA / % HBM peak",
+        "value": pre["tok_s"],
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["step_s"] * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 MFMA operands, fp32 accumulate/state (bf16 I/O)",
+        "data": "synthetic",
+        "config": {"workload": workloads.CONFIG_NAMES[2], "global_batch": inp["B"], "seq_len": inp["T"],
+                   "parallelism": "single GPU", "input_sets_rotated": args.sets},
+        "roofline": pre["roofline"],
+        "path": pre["path"],
+        "kernels": pre["kernels"],
+        "decode": {"metric": "GDR decode tok/s", "value": dec["tok_s"], "unit": "tok/s",
+                   "workload": workloads.CONFIG_NAMES[3], "steps": dec["steps"],
+                   "ms_per_call": dec["step_s"] * 1e3, "kernel_avg_us": dec["kernel_avg_us"],
+                   "alg_bytes_mb": dec["alg_bytes_mb"], "roofline": dec["roofline"]},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(inp)
+        line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec["inp"])
+    else:
+        line["cpu_baseline"] = None
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -49,7 +49,12 @@ SIGNATURES = {
     "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                             ctypes.c_int, ctypes.c_int, _vp, _vp]),
+    "gdr_timing_enable": (ctypes.c_int, [ctypes.c_int]),
+    "gdr_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
+                                       _i32]),
+    "gdr_timing_kernel_name": (ctypes.c_char_p, [_i32]),
 }
+TIMING_KERNELS = 5
 
 _lib = None
 
@@ -106,6 +111,19 @@ def _ptr(t):
 
 def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
+
+
+def timing_enable(on: bool = True) -> None:
+    """Record hipEvents around every kernel the library enqueues (see gdr.h)."""
+    check(lib().gdr_timing_enable(1 if on else 0), "gdr_timing_enable")
+
+
+def timing_read() -> dict:
+    """{kernel name: (summed ms, launches)} since the previous read."""
+    ms = (ctypes.c_double * TIMING_KERNELS)()
+    n = (ctypes.c_int32 * TIMING_KERNELS)()
+    check(lib().gdr_timing_read(ms, n, TIMING_KERNELS), "gdr_timing_read")
+    return {lib().gdr_timing_kernel_name(i).decode(): (ms[i], n[i]) for i in range(TIMING_KERNELS)}
 
 
 def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128) -> int:

@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(HERE, "libgdr.so")
-SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_prefill.hip"]
+SOURCES = ["gdr_api.hip", "gdr_decode.hip", "gdr_prefill.hip", "gdr_timing.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

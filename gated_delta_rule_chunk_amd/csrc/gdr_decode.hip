@@ -183,7 +183,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 template <int DK, int CW, typename ActT, typename StT>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const size_t nwg = (size_t)a.B * a.Nv * (a.Dv / CW);
+    timing_begin(kDecode, stream);
     hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    timing_end(kDecode, stream);
     return hipGetLastError();
 }
 

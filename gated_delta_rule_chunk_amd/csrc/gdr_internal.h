@@ -12,6 +12,12 @@ constexpr int kMaxDecodeTokens = 8;   // the decode page limits S to 8
 constexpr int kChunk = 128;           // L, fixed by the prefill page
 constexpr int kHeadDim = 128;         // D, fixed by the prefill page
 
+// Kernel ids for the opt-in per-kernel timing (gdr_timing_*).
+enum KernelId { kChunkmap = 0, kIntra = 1, kScan = 2, kOutput = 3, kDecode = 4, kKernelCount = 5 };
+void timing_begin(int id, hipStream_t s);
+void timing_end(int id, hipStream_t s);
+const char* kernel_name(int id);
+
 struct DecodeArgs {
     const void* q;
     const void* k;

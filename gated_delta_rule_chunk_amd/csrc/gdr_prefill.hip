@@ -665,23 +665,31 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
     p.ST = reinterpret_cast<_Float16*>(a.ws + lay.off_ST);
     p.T = a.T; p.nc = lay.nc; p.B = a.B; p.Nqk = a.Nqk; p.Nv = a.Nv; p.scale = a.scale;
 
+    timing_begin(kChunkmap, stream);
     hipLaunchKernelGGL(chunkmap_kernel, dim3(1), dim3(256), 0, stream, a.cu, p);
+    timing_end(kChunkmap, stream);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t nwg = (size_t)lay.nc * a.Nv;
     if (nwg > 0) {
+        timing_begin(kIntra, stream);
         if (act_bf16) hipLaunchKernelGGL(intra_kernel<uint16_t>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
         else hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
+        timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     constexpr int DS = 32;
     const size_t nstream = (size_t)a.B * a.Nv;
     const size_t nscan = (nstream + 7) / 8 * 8 * (128 / DS);
+    timing_begin(kScan, stream);
     hipLaunchKernelGGL(scan_kernel<DS>, dim3((unsigned)nscan), dim3(256), 0, stream, p);
+    timing_end(kScan, stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nwg > 0) {
+        timing_begin(kOutput, stream);
         if (act_bf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3((unsigned)nwg), dim3(256), 0, stream, p);
         else hipLaunchKernelGGL(output_kernel<float>, dim3((unsigned)nwg), dim3(256), 0, stream, p);
+        timing_end(kOutput, stream);
         e = hipGetLastError();
     }
     return e;
