@@ -236,6 +236,11 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4, help="rotating device copies of the inputs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
+                    help="time one path only (for counter runs)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a plain 1 GiB device copy (3 launches), the reference for scaling "
+                         "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this operator is measured on one GPU only (got --gpus {args.gpus}); "
@@ -246,7 +251,20 @@ def main():
     import gated_delta_rule_chunk_amd as gdr
     import workloads
 
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
+        return
     gdr.lib()
+    if args.only != "all":
+        res = (bench_prefill if args.only == "prefill" else bench_decode)(args, gdr, torch, workloads)
+        print(json.dumps({"only": args.only, "ms_per_step": res["step_s"] * 1e3, "tok_s": res["tok_s"]}))
+        return
     pre = bench_prefill(args, gdr, torch, workloads)
     dec = bench_decode(args, gdr, torch, workloads)
     inp = pre["inp"]

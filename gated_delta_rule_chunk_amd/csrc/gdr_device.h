@@ -51,6 +51,20 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// 4-element vector load: bf16 one 8-byte access, fp32 one 16-byte access.
+__device__ __forceinline__ void load4(const uint16_t* p, float (&x)[4]) {
+    const u32x2 r = *reinterpret_cast<const u32x2*>(p);
+    x[0] = __uint_as_float(r[0] << 16);
+    x[1] = __uint_as_float(r[0] & 0xffff0000u);
+    x[2] = __uint_as_float(r[1] << 16);
+    x[3] = __uint_as_float(r[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = a[i];
+}
+
 // Scalar load of one element of either dtype.
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }

@@ -52,7 +52,6 @@ namespace gdr {
 namespace {
 
 constexpr int LD16 = 136;   // fp16 LDS row stride (elements): 272 B, 16-byte aligned rows
-constexpr int LD32 = 132;   // fp32 LDS row stride (elements): 528 B
 constexpr int TILE = 128 * 128;
 constexpr float kNormEps = 1e-6f;
 
@@ -83,6 +82,9 @@ struct PrefillDev {
 __device__ __forceinline__ f32x4 mma(half8 a, half8 b, f32x4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
 }
+__device__ __forceinline__ f32x4 mma16(half4 a, half4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+}
 __device__ __forceinline__ half8 ld_h8(const _Float16* p) { return *reinterpret_cast<const half8*>(p); }
 __device__ __forceinline__ void st_h8(_Float16* p, half8 v) { *reinterpret_cast<half8*>(p) = v; }
 __device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
@@ -99,23 +101,6 @@ __device__ __forceinline__ half4 to_h4(f32x4 x) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) h[e] = (_Float16)x[e];
     return h;
-}
-// x = hi + lo with hi, lo fp16: the product of two such splits keeps ~22 bits.
-__device__ __forceinline__ void split8(const float (&x)[8], half8& hi, half8& lo) {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const _Float16 hh = (_Float16)x[e];
-        hi[e] = hh;
-        lo[e] = (_Float16)(x[e] - (float)hh);
-    }
-}
-__device__ __forceinline__ f32x4 mma_split(const float (&a)[8], const float (&b)[8], f32x4 acc) {
-    half8 ah, al, bh, bl;
-    split8(a, ah, al);
-    split8(b, bh, bl);
-    acc = mma(al, bh, acc);
-    acc = mma(ah, bl, acc);
-    return mma(ah, bh, acc);
 }
 __device__ __forceinline__ void lds_row8(const float* p, float (&x)[8]) {
     const f32x4 a = *reinterpret_cast<const f32x4*>(p);
@@ -182,14 +167,31 @@ __device__ __forceinline__ void tri_tile(int n, int& I, int& J) {
     J = n - I * (I + 1) / 2;
 }
 
+// Transposed fp16 tiles ([col][tok] or [dk][tok]) are stored with the 16-byte
+// group index XOR-swizzled by the row's 8-row block, so that both the
+// transposing 16-byte writes and the MFMA fragment reads are free of LDS bank
+// conflicts.  Element (r, c) of such a tile:
+__device__ __forceinline__ int sw(int r, int c) {
+    return r * LD16 + ((((c >> 3) ^ (r >> 3)) & 15) << 3) + (c & 7);
+}
+
 // ------------------------------------------------------------------ K1: intra-chunk
+// 8 waves; LDS < 80 KiB so that two workgroups share a CU.
+//   sA  fp16 [128][LD16]: k^ [tok][dk] (Gram) -> k^T [dk][tok] (swizzled, copied out)
+//                         -> (k^ beta e^gcum)^T -> (v beta)^T [col][tok] (swizzled)
+//   sL  fp16 [128][LD16]: L (strictly lower, zero above), then T = (I + L)^-1
+//   sD  fp32 8 x [16][17]: the diagonal 16x16 blocks L_bb, then T_bb
+// T is found by forward substitution over 16-row blocks, one column block per
+// wave: X_j = T_jj, X_b = T_bb (-sum_{j<=a<b} L_ba X_a).  The 16x16x16 MFMA's
+// accumulator layout equals its B-operand layout, so each solved block feeds
+// the next product straight from registers; no barrier is needed inside the
+// solve.  Operands are plain fp16 with fp32 accumulation.
 template <typename ActT>
-__global__ __launch_bounds__(512) void intra_kernel(PrefillDev p) {
-    __shared__ __align__(16) _Float16 sK[128 * LD16];   // k^ [tok][dk]; after the Gram: k^T [dk][tok]
-    __shared__ __align__(16) float sT[128 * LD32];      // L, then T = (I + L)^-1, row-major
-    __shared__ __align__(16) _Float16 sV[128 * LD16];   // merge scratch X; then (v beta)^T [col][tok]
+__global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
+    __shared__ __align__(16) _Float16 sA[128 * LD16];
+    __shared__ __align__(16) _Float16 sL[128 * LD16];
+    __shared__ float sD[8 * 16 * 17];
     __shared__ float sGc[128], sBeta[128], sBE[128];
-    float* sX = reinterpret_cast<float*>(sV);
 
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
     const int c = blockIdx.x / Nv, h = blockIdx.x % Nv, hq = h / G;
@@ -201,10 +203,21 @@ __global__ __launch_bounds__(512) void intra_kernel(PrefillDev p) {
     const ActT* BETA = static_cast<const ActT*>(p.beta);
     const size_t ch = (size_t)c * Nv + h;
     const size_t cq = (size_t)c * Nqk + hq;
-    const bool writes_keys = (h % G) == 0;   // one value head per group stores k^ for K2/K3
+    const bool writes_keys = (h % G) == 0;   // one value head per group stores k^ and k^T
+    const int c4 = tid & 31, tg = tid >> 5;   // transposing layout: tokens 8*tg.., columns 4*c4..
 
-    // ---- 1a. gate cumulative sum and beta (wave 0; each lane owns rows 2l, 2l+1)
-    if (wave == 0) {
+    // ---- 1. loads: v rows, gate, beta, k rows (normalised -> sA, row-major)
+    float vv[8][4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = 8 * tg + i;
+        if (row < r) load4(V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4, vv[i]);
+        else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) vv[i][e] = 0.f;
+        }
+    }
+    if (wave == 0) {   // gate cumulative sum and beta; lane owns rows 2l, 2l+1
         const int i0 = 2 * lane, i1 = i0 + 1;
         const float g0 = i0 < r ? p.g[(size_t)(t0 + i0) * Nv + h] : 0.f;
         const float g1 = i1 < r ? p.g[(size_t)(t0 + i1) * Nv + h] : 0.f;
@@ -225,14 +238,11 @@ __global__ __launch_bounds__(512) void intra_kernel(PrefillDev p) {
         if (i1 >= r) gc1 = glast;
         sGc[i0] = gc0; sGc[i1] = gc1;
         sBeta[i0] = b0; sBeta[i1] = b1;
-        sBE[i0] = b0 * expf(gc0); sBE[i1] = b1 * expf(gc1);
+        sBE[i0] = b0 * __expf(gc0); sBE[i1] = b1 * __expf(gc1);
         p.gc[ch * 128 + i0] = gc0;
         p.gc[ch * 128 + i1] = gc1;
     }
-
-    // ---- 1b. k^ rows 16*wave + lr (A-fragment layout), L2-normalised
-    half8 kh[4];
-    {
+    {   // k^ rows 16*wave + lr in A-fragment layout, L2-normalised
         const int row = 16 * wave + lr;
         float kx[4][8];
 #pragma unroll
@@ -255,143 +265,152 @@ __global__ __launch_bounds__(512) void intra_kernel(PrefillDev p) {
         for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) kx[ks][e] *= rinv;
-            kh[ks] = to_h8(kx[ks]);
-            st_h8(&sK[row * LD16 + 32 * ks + 8 * lq], kh[ks]);
-            if (writes_keys) st_h8(p.khat + cq * TILE + (size_t)row * 128 + 32 * ks + 8 * lq, kh[ks]);
-        }
-    }
-    // ---- 1c. prefetch this head's v rows (16-byte pieces: row = e/16, cols 8*(e%16))
-    float vv[4][8];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
-        if (row < r) load8(V + ((size_t)(t0 + row) * Nv + h) * 128 + 8 * cc, vv[n]);
-        else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) vv[n][e] = 0.f;
+            const half8 kh = to_h8(kx[ks]);
+            st_h8(&sA[row * LD16 + 32 * ks + 8 * lq], kh);
+            if (writes_keys) st_h8(p.khat + cq * TILE + (size_t)row * 128 + 32 * ks + 8 * lq, kh);
         }
     }
     __syncthreads();
 
-    // ---- 2. Gram k^ k^T on the lower tiles -> L (fp32); zero the upper tiles
+    // ---- 2. Gram k^ k^T on the lower 16-tiles -> L (fp16 in sL, diagonal
+    //         blocks also fp32 in sD); zeros above the block diagonal of sL;
+    //         k^ read back transposed (8 tokens x 4 dk per thread)
     for (int n = wave; n < 36; n += 8) {
         int I, J;
         tri_tile(n, I, J);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
-            acc = mma(ld_h8(&sK[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
-                      ld_h8(&sK[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+            acc = mma(ld_h8(&sA[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
+                      ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
         const int j = 16 * J + lr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * lq + e;
-            sT[i * LD32 + j] = i > j ? sBeta[i] * acc[e] * expf(sGc[i] - sGc[j]) : 0.f;
+            const float Lij = i > j ? sBeta[i] * acc[e] * __expf(sGc[i] - sGc[j]) : 0.f;
+            sL[i * LD16 + j] = (_Float16)Lij;
+            if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
         }
     }
-    for (int n = wave; n < 28; n += 8) {   // upper tiles (J > I)
-        int I, J;
-        tri_tile(n, I, J);   // enumerate pairs J' <= I' and map to (J', I' + 1)
-        const int ui = J, uj = I + 1;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sT[(16 * ui + 4 * lq + e) * LD32 + 16 * uj + lr] = 0.f;
+    {
+        const int i = tid >> 2, I = i >> 4;
+        const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int gg = 2 * (I + 1) + (tid & 3); gg < 16; gg += 4) st_h8(&sL[i * LD16 + 8 * gg], z);
     }
+    half4 kt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kt[i] = ld_h4(&sA[(8 * tg + i) * LD16 + 4 * c4]);
     __syncthreads();
 
-    // ---- 2b. sK now holds k^T [dk][tok] (the Gram no longer reads it)
+    // ---- 3. k^T into sA; inverses of the diagonal blocks T_bb = (I + L_bb)^-1
+    //         (one column per lane, forward substitution in fp32)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int e = 0; e < 4; ++e) {
+        half8 col;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) sK[(32 * ks + 8 * lq + e) * LD16 + 16 * wave + lr] = kh[ks][e];
-
-    // ---- 3. inverses of the eight 16x16 diagonal blocks: T_bb = (I + L_bb)^-1,
-    //         one column per lane, forward substitution in fp32
+        for (int i = 0; i < 8; ++i) col[i] = kt[i][e];
+        st_h8(&sA[sw(4 * c4 + e, 8 * tg)], col);
+    }
     if (tid < 128) {
         const int bb = tid >> 4, j = tid & 15;
-        float* Lb = &sT[(16 * bb) * LD32 + 16 * bb];
+        float* Lb = &sD[bb * 16 * 17];
         float t[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
             float acc = (i == j) ? 1.f : 0.f;
 #pragma unroll
-            for (int kk = 0; kk < i; ++kk) acc = fmaf(-Lb[i * LD32 + kk], t[kk], acc);
+            for (int kk = 0; kk < i; ++kk) acc = fmaf(-Lb[i * 17 + kk], t[kk], acc);
             t[i] = acc;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Lb[i * LD32 + j] = t[i];
+        for (int i = 0; i < 16; ++i) Lb[i * 17 + j] = t[i];
     }
     __syncthreads();
 
-    // k^T -> workspace (coalesced copy of sK)
+    // ---- 4. unscaled k^T -> workspace; column block j = wave of T by forward substitution
     if (writes_keys) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-            const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
-            st_h8(p.khatT + cq * TILE + (size_t)row * 128 + 8 * cc, ld_h8(&sK[row * LD16 + 8 * cc]));
+            const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
+            st_h8(p.khatT + cq * TILE + (size_t)row * 128 + 8 * gg, ld_h8(&sA[sw(row, 8 * gg)]));
         }
     }
-
-    // ---- 4. block doubling: for blocks of size s = 16, 32, 64, merge pairs
-    //         [[T11, 0], [L21, T22]] -> T21 = -T22 (L21 T11)
-    for (int s = 16; s <= 64; s *= 2) {
-        const int ts = s / 16, tpm = ts * ts, nt = (64 / s) * tpm, ldx = s + 4;
-        for (int n = wave; n < nt; n += 8) {
-            const int m = n / tpm, tt = n % tpm, ti = tt / ts, tj = tt % ts, pb = 2 * s * m;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < s; kk += 32) {
-                const int kc = kk + 8 * lq;
-                float a[8], bfr[8];
-                if (kc < s) {
-                    lds_row8(&sT[(pb + s + 16 * ti + lr) * LD32 + pb + kc], a);
+    half4 xh[8];
+    {
+        const int j = wave;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) bfr[e] = sT[(pb + kc + e) * LD32 + pb + 16 * tj + lr];
-                } else {
+        for (int b = 0; b < 8; ++b) {
+            if (b < j) continue;
+            f32x4 x;
+            if (b == j) {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) { a[e] = 0.f; bfr[e] = 0.f; }
+                for (int e = 0; e < 4; ++e) x[e] = sD[(16 * b + 4 * lq + e) * 17 + lr];
+            } else {
+                f32x4 acc = zero;
+#pragma unroll
+                for (int a = 0; a < b; ++a) {
+                    if (a < j) continue;
+                    acc = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq]), xh[a], acc);
                 }
-                acc = mma_split(a, bfr, acc);
+                half4 tb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tb[e] = (_Float16)sD[(16 * b + lr) * 17 + 4 * lq + e];
+                x = mma16(tb, to_h4(-acc), zero);
             }
-            float* X = sX + m * s * ldx;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) X[(16 * ti + 4 * lq + e) * ldx + 16 * tj + lr] = acc[e];
+            xh[b] = to_h4(x);
         }
-        __syncthreads();
-        for (int n = wave; n < nt; n += 8) {
-            const int m = n / tpm, tt = n % tpm, ti = tt / ts, tj = tt % ts, pb = 2 * s * m;
-            const float* X = sX + m * s * ldx;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int kk = 0; kk < s; kk += 32) {
-                const int kc = kk + 8 * lq;
-                float a[8], bfr[8];
-                if (kc < s) {
-                    lds_row8(&sT[(pb + s + 16 * ti + lr) * LD32 + pb + s + kc], a);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) bfr[e] = X[(kc + e) * ldx + 16 * tj + lr];
-                } else {
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) { a[e] = 0.f; bfr[e] = 0.f; }
-                }
-                acc = mma_split(a, bfr, acc);
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) sT[(pb + s + 16 * ti + 4 * lq + e) * LD32 + pb + 16 * tj + lr] = -acc[e];
-        }
-        __syncthreads();
-    }
-
-    // ---- 5. (v beta)^T [col][tok] into sV (the merge scratch is dead now)
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
-        const float bt = sBeta[row];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sV[(8 * cc + e) * LD16 + row] = (_Float16)(vv[n][e] * bt);
     }
     __syncthreads();
 
-    // ---- 6. u = T (v beta) -> uT [col][tok];  w^T = (k^ beta e^g)^T T^T -> w [tok][dk]
-    //         lower-triangular K ranges; waves take row tiles {pr, 7 - pr} (balanced)
+    // ---- 5. T (fp16) into sL over L (zeros above the block diagonal stay);
+    //         sA scaled in place to (k^ beta e^gcum)^T
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        if (b < wave) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sL[(16 * b + 4 * lq + e) * LD16 + 16 * wave + lr] = xh[b][e];
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
+        _Float16* pk = &sA[sw(row, 8 * gg)];
+        half8 x = ld_h8(pk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * sBE[8 * gg + e]);
+        st_h8(pk, x);
+    }
+    __syncthreads();
+
+    // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk]  (lower-triangular K
+    //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
     const int pr = wave & 3, hsel = wave >> 2;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const int Jt = which ? 7 - pr : pr;
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+            const int It = 4 * hsel + ii;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int ks = 0; ks <= Jt / 2; ++ks)
+                acc = mma(ld_h8(&sA[sw(16 * It + lr, 32 * ks + 8 * lq)]),
+                          ld_h8(&sL[(16 * Jt + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+            st_h4(p.w + ch * TILE + (size_t)(16 * Jt + lr) * 128 + 16 * It + 4 * lq, to_h4(acc));
+        }
+    }
+    __syncthreads();
+
+    // ---- 7. (v beta)^T [col][tok] into sA
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        half8 col;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) col[i] = (_Float16)(vv[i][e] * sBeta[8 * tg + i]);
+        st_h8(&sA[sw(4 * c4 + e, 8 * tg)], col);
+    }
+    __syncthreads();
+
+    // ---- 8. u = T (v beta) -> uT [col][tok]
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const int I = which ? 7 - pr : pr;
@@ -399,37 +418,100 @@ __global__ __launch_bounds__(512) void intra_kernel(PrefillDev p) {
         for (int jj = 0; jj < 4; ++jj) {
             const int J = 4 * hsel + jj;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= I / 2; ++ks) {
-                float a[8];
-                lds_row8(&sT[(16 * I + lr) * LD32 + 32 * ks + 8 * lq], a);
-                acc = mma(to_h8(a), ld_h8(&sV[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
-            }
+            for (int ks = 0; ks <= I / 2; ++ks)
+                acc = mma(ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
+                          ld_h8(&sA[sw(16 * J + lr, 32 * ks + 8 * lq)]), acc);
             st_h4(p.uT + ch * TILE + (size_t)(16 * J + lr) * 128 + 16 * I + 4 * lq, to_h4(acc));
-        }
-    }
-#pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const int Jt = which ? 7 - pr : pr;          // token tile (output columns of w^T)
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int It = 4 * hsel + ii;             // dk tile (output rows of w^T)
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= Jt / 2; ++ks) {
-                const half8 kt = ld_h8(&sK[(16 * It + lr) * LD16 + 32 * ks + 8 * lq]);
-                float a[8], b[8];
-#pragma unroll
-                for (int e = 0; e < 8; ++e) a[e] = (float)kt[e] * sBE[32 * ks + 8 * lq + e];
-                lds_row8(&sT[(16 * Jt + lr) * LD32 + 32 * ks + 8 * lq], b);
-                acc = mma(to_h8(a), to_h8(b), acc);
-            }
-            st_h4(p.w + ch * TILE + (size_t)(16 * Jt + lr) * 128 + 16 * It + 4 * lq, to_h4(acc));
         }
     }
 }
 
 // ------------------------------------------------------------------ K2: state scan
+// 8 waves; wave wv owns rows 16*wv .. 16*wv+15 of w (tokens) and of k^T
+// (key dims), i.e. one 16-row MFMA tile of each product, for DS columns.
+// One chunk's operands for a scan wave:
+template <int CT>
+struct ScanOps {
+    half8 aw[4], ak[4];
+    half4 u4[CT];
+    f32x4 gcr;
+    float glast;
+};
+
+// Per-lane element offsets inside a chunk's tiles, fixed for the whole scan;
+// each chunk only moves the (uniform) tile base pointers.
+struct ScanLane {
+    uint32_t a;    // row 16*wv + lr of w / k^T, columns 8*lq
+    uint32_t u;    // u^T: column col0 + lr, tokens 16*wv + 4*lq
+    uint32_t g;    // g_cum: tokens 16*wv + 4*lq
+};
+
+template <int CT>
+__device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, int c, int h, int hq,
+                                          const ScanLane& ln) {
+    const size_t ch = (size_t)c * p.Nv + h;
+    const _Float16* W = p.w + ch * TILE;
+    const _Float16* KT = p.khatT + ((size_t)c * p.Nqk + hq) * TILE;
+    const _Float16* UT = p.uT + ch * TILE;
+    const float* GC = p.gc + ch * 128;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        o.aw[ks] = ld_h8(W + ln.a + 32 * ks);
+        o.ak[ks] = ld_h8(KT + ln.a + 32 * ks);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) o.u4[ct] = ld_h4(UT + ln.u + 16 * 128 * ct);
+    o.gcr = *reinterpret_cast<const f32x4*>(GC + ln.g);
+    o.glast = GC[127];
+}
+
+// One chunk of the scan: record S_c and v_new for the output kernel, then
+// S <- exp(g_last) S + k^T (v_new exp(g_last - g_cum)).
 template <int DS>
-__global__ __launch_bounds__(256) void scan_kernel(PrefillDev p) {
+__device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[DS / 16], const PrefillDev& p,
+                                          int c, int h, _Float16* sST, _Float16* sVn, int tid, int wv, int lr,
+                                          int lq, int col0) {
+    constexpr int CT = DS / 16;
+    const size_t ch = (size_t)c * p.Nv + h;
+    // the state at the start of this chunk, for the output kernel
+#pragma unroll
+    for (int n = 0; n < (DS * 16 + 511) / 512; ++n) {
+        const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
+        if (DS * 16 >= 512 || e_ < DS * 16)
+            st_h8(p.ST + ch * TILE + (size_t)(col0 + row) * 128 + 8 * cc, ld_h8(&sST[row * LD16 + 8 * cc]));
+    }
+    // v_new = u - w S for tokens 16*wv + 4*lq + e
+    const int tok = 16 * wv + 4 * lq;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        f32x4 vp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) vp = mma(o.aw[ks], ld_h8(&sST[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), vp);
+        f32x4 vn, vs;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            vn[e] = (float)o.u4[ct][e] - vp[e];
+            vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
+        }
+        const int col = 16 * ct + lr;
+        st_h4(p.vnT + ch * TILE + (size_t)(col0 + col) * 128 + tok, to_h4(vn));
+        st_h4(&sVn[col * LD16 + tok], to_h4(vs));
+    }
+    __syncthreads();
+    const float dec = __expf(o.glast);
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        f32x4 acc = S[ct] * dec;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mma(o.ak[ks], ld_h8(&sVn[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+        S[ct] = acc;
+        st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(acc));
+    }
+    __syncthreads();
+}
+
+template <int DS>
+__global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     constexpr int NS = 128 / DS, CT = DS / 16;
     __shared__ __align__(16) _Float16 sST[DS * LD16];   // S^T [col][dk] (fp16), current chunk's start state
     __shared__ __align__(16) _Float16 sVn[DS * LD16];   // scaled v_new^T [col][tok]
@@ -445,106 +527,67 @@ __global__ __launch_bounds__(256) void scan_kernel(PrefillDev p) {
     const int col0 = slice * DS;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
 
-    f32x4 S[2][CT];
+    // S rows 16*wv + 4*lq + e (key dims), columns col0 + 16*ct + lr
+    f32x4 S[CT];
     const size_t sbase = (size_t)stream * TILE;
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int e = 0; e < 4; ++e) {
+            const int dk = 16 * wv + 4 * lq + e, col = col0 + 16 * ct + lr;
+            S[ct][e] = p.state_in ? p.state_in[sbase + (size_t)dk * 128 + col] : 0.f;
+        }
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int dk = 32 * wv + 16 * rt + 4 * lq + e, col = col0 + 16 * ct + lr;
-                S[rt][ct][e] = p.state_in ? p.state_in[sbase + (size_t)dk * 128 + col] : 0.f;
-            }
-#pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-            st_h4(&sST[(16 * ct + lr) * LD16 + 32 * wv + 16 * rt + 4 * lq], to_h4(S[rt][ct]));
-    __syncthreads();
+    for (int ct = 0; ct < CT; ++ct) st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(S[ct]));
 
     const int c0 = p.meta[b], c1 = p.meta[b + 1];
-    for (int c = c0; c < c1; ++c) {
-        const size_t ch = (size_t)c * Nv + h;
-        const _Float16* W = p.w + ch * TILE;
-        const _Float16* KT = p.khatT + ((size_t)c * Nqk + hq) * TILE;
-        const _Float16* UT = p.uT + ch * TILE;
-        const float* GC = p.gc + ch * 128;
-        half8 aw[2][4], ak[2][4];
-        half4 u4[2][CT];
-        float gcr[2][4];
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt) {
-            const int row = 32 * wv + 16 * rt + lr;
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                aw[rt][ks] = ld_h8(W + (size_t)row * 128 + 32 * ks + 8 * lq);
-                ak[rt][ks] = ld_h8(KT + (size_t)row * 128 + 32 * ks + 8 * lq);
-            }
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct)
-                u4[rt][ct] = ld_h4(UT + (size_t)(col0 + 16 * ct + lr) * 128 + 32 * wv + 16 * rt + 4 * lq);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) gcr[rt][e] = GC[32 * wv + 16 * rt + 4 * lq + e];
-        }
-        const float glast = GC[127];
-
-        // the state at the start of this chunk, for the output kernel
-        for (int e_ = tid; e_ < DS * 16; e_ += 256) {
-            const int row = e_ >> 4, cc = e_ & 15;
-            st_h8(p.ST + ch * TILE + (size_t)(col0 + row) * 128 + 8 * cc, ld_h8(&sST[row * LD16 + 8 * cc]));
-        }
-        // v_new = u - w S
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                f32x4 vp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    vp = mma(aw[rt][ks], ld_h8(&sST[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), vp);
-                f32x4 vn, vs;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vn[e] = (float)u4[rt][ct][e] - vp[e];
-                    vs[e] = vn[e] * expf(glast - gcr[rt][e]);
-                }
-                const int tok = 32 * wv + 16 * rt + 4 * lq, col = 16 * ct + lr;
-                st_h4(p.vnT + ch * TILE + (size_t)(col0 + col) * 128 + tok, to_h4(vn));
-                st_h4(&sVn[col * LD16 + tok], to_h4(vs));
-            }
-        __syncthreads();
-        // S <- exp(g_last) S + k^T (v_new exp(g_last - g_cum))
-        const float dec = expf(glast);
-#pragma unroll
-        for (int rt = 0; rt < 2; ++rt)
-#pragma unroll
-            for (int ct = 0; ct < CT; ++ct) {
-                f32x4 acc = S[rt][ct] * dec;
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    acc = mma(ak[rt][ks], ld_h8(&sVn[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), acc);
-                S[rt][ct] = acc;
-                st_h4(&sST[(16 * ct + lr) * LD16 + 32 * wv + 16 * rt + 4 * lq], to_h4(acc));
-            }
-        __syncthreads();
+    const ScanLane ln{(uint32_t)((16 * wv + lr) * 128 + 8 * lq), (uint32_t)((col0 + lr) * 128 + 16 * wv + 4 * lq),
+                      (uint32_t)(16 * wv + 4 * lq)};
+    // Two register sets, A and B, alternate between the chunk being computed
+    // and the one being fetched (no copies between them, so each chunk's
+    // compute waits only for its own operands).
+    ScanOps<CT> A, B;
+    if (c0 < c1) scan_load(A, p, c0, h, hq, ln);
+    __syncthreads();
+    for (int c = c0; c < c1; c += 2) {
+        if (c + 1 < c1) scan_load(B, p, c + 1, h, hq, ln);
+        scan_step<DS>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0);
+        if (c + 1 >= c1) break;
+        if (c + 2 < c1) scan_load(A, p, c + 2, h, hq, ln);
+        scan_step<DS>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0);
     }
 #pragma unroll
-    for (int rt = 0; rt < 2; ++rt)
+    for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int dk = 32 * wv + 16 * rt + 4 * lq + e, col = col0 + 16 * ct + lr;
-                p.state_out[sbase + (size_t)dk * 128 + col] = S[rt][ct][e];
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int dk = 16 * wv + 4 * lq + e, col = col0 + 16 * ct + lr;
+            p.state_out[sbase + (size_t)dk * 128 + col] = S[ct][e];
+        }
 }
 
 // ------------------------------------------------------------------ K3: output
+// 8 waves; wave w owns output rows 16w .. 16w+15.  The three 32 KiB operand
+// tiles (k^, S_c^T, v_new^T) pass one after another through one LDS buffer,
+// each fetched into registers while the previous one is in use.
+__device__ __forceinline__ void tile_fetch(u32x4 (&rg)[4], const _Float16* src, int tid) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
+        rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)row * 128 + 8 * gg);
+    }
+}
+__device__ __forceinline__ void tile_store(const u32x4 (&rg)[4], _Float16* dst, int tid) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
+        *reinterpret_cast<u32x4*>(dst + row * LD16 + 8 * gg) = rg[n];
+    }
+}
+
 template <typename ActT>
-__global__ __launch_bounds__(256) void output_kernel(PrefillDev p) {
+__global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
+    __shared__ __align__(16) _Float16 sBuf[128 * LD16];
     __shared__ __align__(16) _Float16 sP[128 * LD16];
-    __shared__ __align__(16) float sO[4][16 * LD32];
 
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
     const int c = blockIdx.x / Nv, h = blockIdx.x % Nv, hq = h / G;
@@ -555,15 +598,14 @@ __global__ __launch_bounds__(256) void output_kernel(PrefillDev p) {
     ActT* OUT = static_cast<ActT*>(p.out);
     const size_t ch = (size_t)c * Nv + h;
     const float* GC = p.gc + ch * 128;
-    const _Float16* KH = p.khat + ((size_t)c * Nqk + hq) * TILE;
-    const _Float16* STc = p.ST + ch * TILE;
-    const _Float16* VNT = p.vnT + ch * TILE;
+    const int I = wv;
 
-    // q^ (scaled) and q^ e^{g_cum} for this wave's row tiles {wv, 7 - wv}
-    half8 qh[2][4], qe[2][4];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int I = it ? 7 - wv : wv, row = 16 * I + lr;
+    u32x4 stage[4];
+    tile_fetch(stage, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
+    // q^ (scaled) and q^ e^{g_cum} for rows 16 I + lr
+    half8 qh[4], qe[4];
+    {
+        const int row = 16 * I + lr;
         float x[4][8];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
@@ -581,70 +623,76 @@ __global__ __launch_bounds__(256) void output_kernel(PrefillDev p) {
         ssq += __shfl_xor(ssq, 16);
         ssq += __shfl_xor(ssq, 32);
         const float rinv = p.scale / sqrtf(ssq + kNormEps);
-        const float eg = expf(GC[row]);
+        const float eg = __expf(GC[row]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             float y[8], z[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) { y[e] = x[ks][e] * rinv; z[e] = y[e] * eg; }
-            qh[it][ks] = to_h8(y);
-            qe[it][ks] = to_h8(z);
+            qh[ks] = to_h8(y);
+            qe[ks] = to_h8(z);
         }
     }
-    // P = (q^ k^T) . D on the inclusive lower triangle -> sP (fp16)
+    tile_store(stage, sBuf, tid);
+    tile_fetch(stage, p.ST + ch * TILE, tid);
+    __syncthreads();
+
+    // P = (q^ k^T) . D on the inclusive lower triangle -> sP rows of this wave
+    for (int J = 0; J <= I; ++J) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int I = it ? 7 - wv : wv;
-        for (int J = 0; J <= I; ++J) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 4; ++ks) acc = mma(qh[ks], ld_h8(&sBuf[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+        const int j = 16 * J + lr;
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mma(qh[it][ks], ld_h8(KH + (size_t)(16 * J + lr) * 128 + 32 * ks + 8 * lq), acc);
-            const int j = 16 * J + lr;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + 4 * lq + e;
-                sP[i * LD16 + j] = (_Float16)(i >= j ? acc[e] * expf(GC[i] - GC[j]) : 0.f);
-            }
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * lq + e;
+            sP[i * LD16 + j] = (_Float16)(i >= j ? acc[e] * __expf(GC[i] - GC[j]) : 0.f);
         }
-        if ((I & 1) == 0) {
+    }
+    if ((I & 1) == 0) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) sP[(16 * I + 4 * lq + e) * LD16 + 16 * (I + 1) + lr] = (_Float16)0.f;
-        }
+        for (int e = 0; e < 4; ++e) sP[(16 * I + 4 * lq + e) * LD16 + 16 * (I + 1) + lr] = (_Float16)0.f;
     }
     __syncthreads();
-    // o = (q^ e^g) S_c + P v_new, then rows < r -> out
+    tile_store(stage, sBuf, tid);   // S_c^T [col][dk]
+    tile_fetch(stage, p.vnT + ch * TILE, tid);
+    __syncthreads();
+
+    f32x4 o[8];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
-        const int I = it ? 7 - wv : wv;
-        f32x4 o[8];
+    for (int ct = 0; ct < 8; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks < 4; ++ks) acc = mma(qe[ks], ld_h8(&sBuf[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+        o[ct] = acc;
+    }
+    __syncthreads();
+    tile_store(stage, sBuf, tid);   // v_new^T [col][tok]
+    __syncthreads();
+    for (int ks = 0; ks <= I / 2; ++ks) {
+        const half8 a = ld_h8(&sP[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mma(qe[it][ks], ld_h8(STc + (size_t)(16 * ct + lr) * 128 + 32 * ks + 8 * lq), acc);
-            for (int ks = 0; ks <= I / 2; ++ks)
-                acc = mma(ld_h8(&sP[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
-                          ld_h8(VNT + (size_t)(16 * ct + lr) * 128 + 32 * ks + 8 * lq), acc);
-            o[ct] = acc;
-        }
-        float* so = sO[wv];
+        for (int ct = 0; ct < 8; ++ct) o[ct] = mma(a, ld_h8(&sBuf[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), o[ct]);
+    }
+    // rows < r -> out, staged through this wave's own rows of sP, 64 columns at a time
+    float* so = reinterpret_cast<float*>(&sP[16 * I * LD16]);   // 16 x 68 floats
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct)
+    for (int hx = 0; hx < 2; ++hx) {
+        __syncthreads();
 #pragma unroll
-            for (int e = 0; e < 4; ++e) so[(4 * lq + e) * LD32 + 16 * ct + lr] = o[ct][e];
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) so[(4 * lq + e) * 68 + 16 * ct + lr] = o[4 * hx + ct][e];
         __syncthreads();
         const int row = lane >> 2, seg = lane & 3, tok = 16 * I + row;
         if (tok < r) {
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
+            for (int n = 0; n < 2; ++n) {
                 float y[8];
-                lds_row8(&so[row * LD32 + 32 * seg + 8 * n], y);
-                store8(OUT + ((size_t)(t0 + tok) * Nv + h) * 128 + 32 * seg + 8 * n, y);
+                lds_row8(&so[row * 68 + 16 * seg + 8 * n], y);
+                store8(OUT + ((size_t)(t0 + tok) * Nv + h) * 128 + 64 * hx + 16 * seg + 8 * n, y);
             }
         }
-        __syncthreads();
     }
 }
 
@@ -678,17 +726,24 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
         timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    constexpr int DS = 32;
+    // State columns are split over NS = 128 / DS workgroups per (sequence,
+    // head) stream, so that streams x NS fills the chip (about 256 groups).
     const size_t nstream = (size_t)a.B * a.Nv;
-    const size_t nscan = (nstream + 7) / 8 * 8 * (128 / DS);
+    const int ns = nstream >= 256 ? 1 : nstream >= 128 ? 2 : nstream >= 64 ? 4 : 8;
+    const size_t nscan = (nstream + 7) / 8 * 8 * ns;
     timing_begin(kScan, stream);
-    hipLaunchKernelGGL(scan_kernel<DS>, dim3((unsigned)nscan), dim3(256), 0, stream, p);
+    switch (ns) {
+        case 1: hipLaunchKernelGGL(scan_kernel<128>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL(scan_kernel<64>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        case 4: hipLaunchKernelGGL(scan_kernel<32>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        default: hipLaunchKernelGGL(scan_kernel<16>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+    }
     timing_end(kScan, stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nwg > 0) {
         timing_begin(kOutput, stream);
-        if (act_bf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3((unsigned)nwg), dim3(256), 0, stream, p);
-        else hipLaunchKernelGGL(output_kernel<float>, dim3((unsigned)nwg), dim3(256), 0, stream, p);
+        if (act_bf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL(output_kernel<float>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
         timing_end(kOutput, stream);
         e = hipGetLastError();
     }

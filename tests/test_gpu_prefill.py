@@ -134,3 +134,12 @@ def test_prefill_is_deterministic():
     o1, s1 = run_gpu(inp)
     o2, s2 = run_gpu(inp)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("B,Nqk,Nv", [(1, 1, 4), (2, 16, 32), (4, 8, 32), (8, 16, 32)])
+def test_prefill_every_scan_slice_width(B, Nqk, Nv):
+    """B * Nv value-head streams pick the scan's column split (16, 32, 64 or
+    128 state columns per workgroup); each split is checked."""
+    lens = [150 + 37 * i for i in range(B)]
+    inp = workloads.prefill_inputs(60 + B, lens, Nqk=Nqk, Nv=Nv, act="bf16")
+    check_parity(inp, f"B={B} Nv={Nv} ({B * Nv} streams)")
