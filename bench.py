@@ -198,12 +198,26 @@ def bench_decode(args, gdr, torch, workloads):
 
     steps = max(args.steps * 4, 20)
     dt, per = timed(step, steps, args.warmup, gdr, torch)
+    # reference: a plain device copy moving the same number of bytes (half read, half written)
+    nb_copy = (bytes_decode(inp) // 2 + 255) // 256 * 256
+    src = torch.empty(nb_copy, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(20):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * nb_copy * 20 / (e0.elapsed_time(e1) / 1e3) / 1e9
+    del src, dst
     ms, n = per["gdr_decode"]
     avg = ms / 1e3 / max(n, 1)
     nb = bytes_decode(inp)
     ntok = int(inp["lens"].sum())
     return dict(inp=inp, step_s=dt / steps, steps=steps, tok_s=ntok / (dt / steps), kernel_avg_us=avg * 1e6,
-                roofline=roofline("gdr_decode", avg, nbytes=nb), alg_bytes_mb=nb / 1e6)
+                roofline=roofline("gdr_decode", avg, nbytes=nb), alg_bytes_mb=nb / 1e6, copy_gbs=copy_gbs)
 
 
 def cpu_baseline_prefill(inp):
@@ -289,7 +303,8 @@ def main():
         "decode": {"metric": "GDR decode tok/s", "value": dec["tok_s"], "unit": "tok/s",
                    "workload": workloads.CONFIG_NAMES[3], "steps": dec["steps"],
                    "ms_per_call": dec["step_s"] * 1e3, "kernel_avg_us": dec["kernel_avg_us"],
-                   "alg_bytes_mb": dec["alg_bytes_mb"], "roofline": dec["roofline"]},
+                   "alg_bytes_mb": dec["alg_bytes_mb"], "roofline": dec["roofline"],
+                   "device_copy_reference_GBps": dec["copy_gbs"]},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(inp)

@@ -15,7 +15,8 @@
 //     wave covers whole contiguous rows -- fully coalesced 128-bit traffic;
 //   * the whole slab is loaded up front (RPT independent 16-byte loads per
 //     lane in flight), kept in fp32 registers across the <= 8-token chain,
-//     and written back once per distinct slot the chain stores into;
+//     and written back once per distinct slot the chain stores into; slab
+//     traffic uses non-temporal loads and stores (each byte is touched once);
 //   * both reductions over the key dim (S^T k and S^T q) come out of ONE
 //     pass over the decayed state: o = S_new^T q = (aS)^T q + delta (k.q),
 //     so each token needs one cross-lane reduction (xor shuffles inside a
@@ -75,7 +76,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     if (slot0 >= 0 && slot0 < a.num_slots) {
         const StT* base = pool + (size_t)slot0 * slot_stride + (size_t)h * slab + col;
 #pragma unroll
-        for (int m = 0; m < RPT; ++m) load8(base + (size_t)(rg + RP * m) * Dv, st[m]);
+        for (int m = 0; m < RPT; ++m) load8_nt(base + (size_t)(rg + RP * m) * Dv, st[m]);
     } else {
 #pragma unroll
         for (int m = 0; m < RPT; ++m)
@@ -171,7 +172,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         if (!later && slot >= 0 && slot < a.num_slots) {
             StT* base = pool + (size_t)slot * slot_stride + (size_t)h * slab + col;
 #pragma unroll
-            for (int m = 0; m < RPT; ++m) store8(base + (size_t)(rg + RP * m) * Dv, st[m]);
+            for (int m = 0; m < RPT; ++m) store8_nt(base + (size_t)(rg + RP * m) * Dv, st[m]);
         }
     }
     if (rg == 0) {
@@ -191,8 +192,11 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 
 template <int DK, typename ActT, typename StT>
 static hipError_t launch_dv(const DecodeArgs& a, hipStream_t stream) {
+    // column slices: all of Dv up to 128; 256-column slices for wider states,
+    // which keeps 32 KiB of bf16 slab in flight per workgroup when Dk = 64
     if (a.Dv == 64) return launch<DK, 64, ActT, StT>(a, stream);
-    return launch<DK, 128, ActT, StT>(a, stream);   // Dv in {128, 256, 512}: 128-column slices
+    if (a.Dv == 128) return launch<DK, 128, ActT, StT>(a, stream);
+    return launch<DK, 256, ActT, StT>(a, stream);
 }
 
 template <typename ActT, typename StT>

@@ -65,6 +65,34 @@ __device__ __forceinline__ void load4(const float* p, float (&x)[4]) {
     for (int i = 0; i < 4; ++i) x[i] = a[i];
 }
 
+// Non-temporal 8-element load / store, for data streamed through exactly once
+// (the decode state slabs): hints the caches not to keep the lines.
+__device__ __forceinline__ void load8_nt(const uint16_t* p, float (&x)[8]) {
+    const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void load8_nt(const float* p, float (&x)[8]) {
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { x[i] = a[i]; x[4 + i] = b[i]; }
+}
+__device__ __forceinline__ void store8_nt(uint16_t* p, const float (&x)[8]) {
+    u32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        r[i] = uint32_t(f32_to_bf16(x[2 * i])) | (uint32_t(f32_to_bf16(x[2 * i + 1])) << 16);
+    __builtin_nontemporal_store(r, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void store8_nt(float* p, const float (&x)[8]) {
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(p));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p + 4));
+}
+
 // Scalar load of one element of either dtype.
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
