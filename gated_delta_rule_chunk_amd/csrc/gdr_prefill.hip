@@ -469,8 +469,8 @@ __device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, i
 // S <- exp(g_last) S + k^T (v_new exp(g_last - g_cum)).
 template <int DS>
 __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[DS / 16], const PrefillDev& p,
-                                          int c, int h, _Float16* sST, _Float16* sVn, int tid, int wv, int lr,
-                                          int lq, int col0) {
+                                          int c, int h, _Float16* sST, _Float16* sVn, _Float16* sVr, int tid,
+                                          int wv, int lr, int lq, int col0) {
     constexpr int CT = DS / 16;
     const size_t ch = (size_t)c * p.Nv + h;
     // the state at the start of this chunk, for the output kernel
@@ -494,10 +494,17 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
             vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
         }
         const int col = 16 * ct + lr;
-        st_h4(p.vnT + ch * TILE + (size_t)(col0 + col) * 128 + tok, to_h4(vn));
+        st_h4(&sVr[col * LD16 + tok], to_h4(vn));
         st_h4(&sVn[col * LD16 + tok], to_h4(vs));
     }
     __syncthreads();
+    // v_new^T of this chunk and slice -> workspace, 16-byte coalesced pieces
+#pragma unroll
+    for (int n = 0; n < (DS * 16 + 511) / 512; ++n) {
+        const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
+        if (DS * 16 >= 512 || e_ < DS * 16)
+            st_h8(p.vnT + ch * TILE + (size_t)(col0 + row) * 128 + 8 * cc, ld_h8(&sVr[row * LD16 + 8 * cc]));
+    }
     const float dec = __expf(o.glast);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -515,6 +522,7 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     constexpr int NS = 128 / DS, CT = DS / 16;
     __shared__ __align__(16) _Float16 sST[DS * LD16];   // S^T [col][dk] (fp16), current chunk's start state
     __shared__ __align__(16) _Float16 sVn[DS * LD16];   // scaled v_new^T [col][tok]
+    __shared__ __align__(16) _Float16 sVr[DS * LD16];   // v_new^T [col][tok], staged for the workspace
 
     // XCD-aware placement: the NS slices of one (sequence, head) stream read
     // the same w / k^T tiles, so they are given workgroup ids that the
@@ -543,18 +551,36 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     const int c0 = p.meta[b], c1 = p.meta[b + 1];
     const ScanLane ln{(uint32_t)((16 * wv + lr) * 128 + 8 * lq), (uint32_t)((col0 + lr) * 128 + 16 * wv + 4 * lq),
                       (uint32_t)(16 * wv + 4 * lq)};
-    // Two register sets, A and B, alternate between the chunk being computed
-    // and the one being fetched (no copies between them, so each chunk's
-    // compute waits only for its own operands).
-    ScanOps<CT> A, B;
-    if (c0 < c1) scan_load(A, p, c0, h, hq, ln);
-    __syncthreads();
-    for (int c = c0; c < c1; c += 2) {
-        if (c + 1 < c1) scan_load(B, p, c + 1, h, hq, ln);
-        scan_step<DS>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0);
-        if (c + 1 >= c1) break;
-        if (c + 2 < c1) scan_load(A, p, c + 2, h, hq, ln);
-        scan_step<DS>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0);
+    // Register sets rotate between the chunk being computed and the ones being
+    // fetched (no copies between them, so each chunk's compute waits only for
+    // its own operands): three sets (two chunks of lookahead) up to 64 columns,
+    // two sets at 128 columns, where a third would not fit in registers.
+    if constexpr (DS <= 64) {
+        ScanOps<CT> A, B, C;
+        if (c0 < c1) scan_load(A, p, c0, h, hq, ln);
+        if (c0 + 1 < c1) scan_load(B, p, c0 + 1, h, hq, ln);
+        __syncthreads();
+        for (int c = c0; c < c1; c += 3) {
+            if (c + 2 < c1) scan_load(C, p, c + 2, h, hq, ln);
+            scan_step<DS>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
+            if (c + 1 >= c1) break;
+            if (c + 3 < c1) scan_load(A, p, c + 3, h, hq, ln);
+            scan_step<DS>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
+            if (c + 2 >= c1) break;
+            if (c + 4 < c1) scan_load(B, p, c + 4, h, hq, ln);
+            scan_step<DS>(C, S, p, c + 2, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
+        }
+    } else {
+        ScanOps<CT> A, B;
+        if (c0 < c1) scan_load(A, p, c0, h, hq, ln);
+        __syncthreads();
+        for (int c = c0; c < c1; c += 2) {
+            if (c + 1 < c1) scan_load(B, p, c + 1, h, hq, ln);
+            scan_step<DS>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
+            if (c + 1 >= c1) break;
+            if (c + 2 < c1) scan_load(A, p, c + 2, h, hq, ln);
+            scan_step<DS>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
+        }
     }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
