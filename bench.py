@@ -220,6 +220,30 @@ def bench_decode(args, gdr, torch, workloads):
                 roofline=roofline("gdr_decode", avg, nbytes=nb), alg_bytes_mb=nb / 1e6, copy_gbs=copy_gbs)
 
 
+def time_config(n, args, gdr, torch, workloads):
+    """Per-call time of one configured workload (inputs resident, one set)."""
+    inp = workloads.config_inputs(n)
+    dev = "cuda:0"
+    d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    if "cu_seqlens" in inp:
+        ws = torch.empty(gdr.chunk_prefill_workspace_size(inp["T"], inp["B"], inp["Nqk"], inp["Nv"]),
+                         dtype=torch.uint8, device=dev)
+
+        def f(i):
+            gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["scale"],
+                              state_in=d["state_in"], workspace=ws)
+        ntok = inp["T"]
+    else:
+        def f(i):
+            gdr.recurrent_decode(d["q"], d["k"], d["v"], d["g"], d["gk"], d["beta"], d["pool"], d["idx"],
+                                 d["lens"], d["scale"])
+        ntok = int(inp["lens"].sum())
+    steps = 5 if n == 5 else 20
+    dt, per = timed(f, steps, 2, gdr, torch)
+    return {"config": workloads.CONFIG_NAMES[n], "ms_per_call": dt / steps * 1e3, "tok_s": ntok / (dt / steps),
+            "kernels_us": {k: round(v[0] / max(v[1], 1) * 1e3, 1) for k, v in per.items() if v[1]}}
+
+
 def cpu_baseline_prefill(inp):
     import oracle
     t0 = time.perf_counter()
@@ -252,6 +276,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="time one path only (for counter runs)")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="also time every configured workload (one line per workload, after the main line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 launches), the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
@@ -312,6 +338,9 @@ def main():
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line))
+    if args.all_configs:
+        for n in (1, 2, 3, 4, 5):
+            print(json.dumps(time_config(n, args, gdr, torch, workloads)), flush=True)
 
 
 if __name__ == "__main__":

@@ -186,43 +186,133 @@ __device__ __forceinline__ int sw(int r, int c) {
 // accumulator layout equals its B-operand layout, so each solved block feeds
 // the next product straight from registers; no barrier is needed inside the
 // solve.  Operands are plain fp16 with fp32 accumulation.
-template <typename ActT>
-__global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
-    __shared__ __align__(16) _Float16 sA[128 * LD16];
-    __shared__ __align__(16) _Float16 sL[128 * LD16];
-    __shared__ float sD[8 * 16 * 17];
-    __shared__ float sGc[128], sBeta[128], sBE[128];
+// Raw (unconverted) loads, so that a prefetch does not wait for its data
+// until the data is used.
+template <typename ActT> struct Raw8;
+template <> struct Raw8<uint16_t> { u32x4 d; };
+template <> struct Raw8<float> { f32x4 a, b; };
+template <typename ActT> struct Raw4;
+template <> struct Raw4<uint16_t> { u32x2 d; };
+template <> struct Raw4<float> { f32x4 d; };
 
-    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
-    const int c = blockIdx.x / Nv, h = blockIdx.x % Nv, hq = h / G;
-    if (c >= p.meta[p.B]) return;
+__device__ __forceinline__ void raw_load(Raw8<uint16_t>& x, const uint16_t* p) { x.d = *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void raw_load(Raw8<float>& x, const float* p) {
+    x.a = *reinterpret_cast<const f32x4*>(p);
+    x.b = *reinterpret_cast<const f32x4*>(p + 4);
+}
+__device__ __forceinline__ void raw_load(Raw4<uint16_t>& x, const uint16_t* p) { x.d = *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void raw_load(Raw4<float>& x, const float* p) { x.d = *reinterpret_cast<const f32x4*>(p); }
+__device__ __forceinline__ void raw_zero(Raw8<uint16_t>& x) { x.d = u32x4{0u, 0u, 0u, 0u}; }
+__device__ __forceinline__ void raw_zero(Raw8<float>& x) { x.a = f32x4{0.f, 0.f, 0.f, 0.f}; x.b = x.a; }
+__device__ __forceinline__ void raw_zero(Raw4<uint16_t>& x) { x.d = u32x2{0u, 0u}; }
+__device__ __forceinline__ void raw_zero(Raw4<float>& x) { x.d = f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ void raw_cvt(const Raw8<uint16_t>& x, float (&y)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        y[2 * i] = __uint_as_float(x.d[i] << 16);
+        y[2 * i + 1] = __uint_as_float(x.d[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void raw_cvt(const Raw8<float>& x, float (&y)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { y[i] = x.a[i]; y[4 + i] = x.b[i]; }
+}
+__device__ __forceinline__ void raw_cvt(const Raw4<uint16_t>& x, float (&y)[4]) {
+    y[0] = __uint_as_float(x.d[0] << 16);
+    y[1] = __uint_as_float(x.d[0] & 0xffff0000u);
+    y[2] = __uint_as_float(x.d[1] << 16);
+    y[3] = __uint_as_float(x.d[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void raw_cvt(const Raw4<float>& x, float (&y)[4]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = x.d[i];
+}
+
+// Raw inputs of one (chunk, value head) item, held in registers so that the
+// next item's loads are in flight while the current item computes.
+//   k: row 16*wave + lr, key dims 32*ks + 8*lq .. +7 (A-fragment layout)
+//   g0/g1, b0/b1: gate and beta of rows 2*lane, 2*lane+1 (wave 0 only)
+// (v is first needed late in the item, so each item loads its own v rows at
+// its start.)
+template <typename ActT>
+struct IntraStage {
+    Raw8<ActT> k[4];
+    float g0, g1;
+    ActT b0, b1;
+    int c, h, t0, r;
+};
+
+template <typename ActT>
+__device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, int item, int wave, int lane,
+                                           int lr, int lq, int c4, int tg) {
+    const int Nv = p.Nv, Nqk = p.Nqk;
+    const int c = item / Nv, h = item % Nv, hq = h / (Nv / Nqk);
     const int t0 = p.cmap[4 * c + 1], r = p.cmap[4 * c + 2];
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    st.c = c; st.h = h; st.t0 = t0; st.r = r;
     const ActT* K = static_cast<const ActT*>(p.k);
-    const ActT* V = static_cast<const ActT*>(p.v);
     const ActT* BETA = static_cast<const ActT*>(p.beta);
+    const int row = 16 * wave + lr;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        if (row < r) raw_load(st.k[ks], K + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+        else raw_zero(st.k[ks]);
+    }
+    if (wave == 0) {
+        const int i0 = 2 * lane, i1 = i0 + 1;
+        st.g0 = i0 < r ? p.g[(size_t)(t0 + i0) * Nv + h] : 0.f;
+        st.g1 = i1 < r ? p.g[(size_t)(t0 + i1) * Nv + h] : 0.f;
+        st.b0 = i0 < r ? BETA[(size_t)(t0 + i0) * Nv + h] : ActT(0);
+        st.b1 = i1 < r ? BETA[(size_t)(t0 + i1) * Nv + h] : ActT(0);
+    }
+}
+
+struct IntraSmem {
+    _Float16* sA;
+    _Float16* sL;
+    float* sD;
+    float* sGc;
+    float* sBeta;
+    float* sBE;
+};
+
+template <typename ActT>
+__device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const PrefillDev& p, const IntraSmem& sm,
+                                           int tid_in) {
+    // The item loop would otherwise hoist every per-lane offset derived from
+    // the thread index out of the loop and keep them all live; an opaque copy
+    // of the index makes them per-item values instead.
+    int tid = tid_in;
+    asm volatile("" : "+v"(tid));
+    _Float16* sA = sm.sA;
+    _Float16* sL = sm.sL;
+    float* sD = sm.sD;
+    float* sGc = sm.sGc;
+    float* sBeta = sm.sBeta;
+    float* sBE = sm.sBE;
+    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
+    const int c = st.c, h = st.h, hq = h / G, r = st.r, t0 = st.t0;
+    const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const size_t ch = (size_t)c * Nv + h;
     const size_t cq = (size_t)c * Nqk + hq;
     const bool writes_keys = (h % G) == 0;   // one value head per group stores k^ and k^T
     const int c4 = tid & 31, tg = tid >> 5;   // transposing layout: tokens 8*tg.., columns 4*c4..
 
-    // ---- 1. loads: v rows, gate, beta, k rows (normalised -> sA, row-major)
-    float vv[8][4];
+    // v rows of this item (first used in step 7; the load overlaps steps 1-6)
+    Raw4<ActT> vr[8];
+    {
+        const ActT* V = static_cast<const ActT*>(p.v);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int row = 8 * tg + i;
-        if (row < r) load4(V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4, vv[i]);
-        else {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) vv[i][e] = 0.f;
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * tg + i;
+            if (row < r) raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4);
+            else raw_zero(vr[i]);
         }
     }
-    if (wave == 0) {   // gate cumulative sum and beta; lane owns rows 2l, 2l+1
+    __syncthreads();   // the previous item is done with the shared buffers
+    // ---- 1. gate cumulative sum and beta (wave 0); k rows normalised -> sA (row-major)
+    if (wave == 0) {   // lane owns rows 2l, 2l+1
         const int i0 = 2 * lane, i1 = i0 + 1;
-        const float g0 = i0 < r ? p.g[(size_t)(t0 + i0) * Nv + h] : 0.f;
-        const float g1 = i1 < r ? p.g[(size_t)(t0 + i1) * Nv + h] : 0.f;
-        const float b0 = i0 < r ? load1(BETA + (size_t)(t0 + i0) * Nv + h) : 0.f;
-        const float b1 = i1 < r ? load1(BETA + (size_t)(t0 + i1) * Nv + h) : 0.f;
+        const float g0 = st.g0, g1 = st.g1, b0 = load1(&st.b0), b1 = load1(&st.b1);
         const float s = g0 + g1;
         float incl = s;
 #pragma unroll
@@ -242,30 +332,25 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
         p.gc[ch * 128 + i0] = gc0;
         p.gc[ch * 128 + i1] = gc1;
     }
-    {   // k^ rows 16*wave + lr in A-fragment layout, L2-normalised
+    {
         const int row = 16 * wave + lr;
-        float kx[4][8];
+        float kf[4][8];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (row < r) load8(K + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq, kx[ks]);
-            else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) kx[ks][e] = 0.f;
-            }
-        }
+        for (int ks = 0; ks < 4; ++ks) raw_cvt(st.k[ks], kf[ks]);
         float ssq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ssq = fmaf(kx[ks][e], kx[ks][e], ssq);
+            for (int e = 0; e < 8; ++e) ssq = fmaf(kf[ks][e], kf[ks][e], ssq);
         ssq += __shfl_xor(ssq, 16);
         ssq += __shfl_xor(ssq, 32);
         const float rinv = 1.f / sqrtf(ssq + kNormEps);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
+            float kx[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) kx[ks][e] *= rinv;
-            const half8 kh = to_h8(kx[ks]);
+            for (int e = 0; e < 8; ++e) kx[e] = kf[ks][e] * rinv;
+            const half8 kh = to_h8(kx);
             st_h8(&sA[row * LD16 + 32 * ks + 8 * lq], kh);
             if (writes_keys) st_h8(p.khat + cq * TILE + (size_t)row * 128 + 32 * ks + 8 * lq, kh);
         }
@@ -401,12 +486,17 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __syncthreads();
 
     // ---- 7. (v beta)^T [col][tok] into sA
+    {
+        float vf[8][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        half8 col;
+        for (int i = 0; i < 8; ++i) raw_cvt(vr[i], vf[i]);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) col[i] = (_Float16)(vv[i][e] * sBeta[8 * tg + i]);
-        st_h8(&sA[sw(4 * c4 + e, 8 * tg)], col);
+        for (int e = 0; e < 4; ++e) {
+            half8 col;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) col[i] = (_Float16)(vf[i][e] * sBeta[8 * tg + i]);
+            st_h8(&sA[sw(4 * c4 + e, 8 * tg)], col);
+        }
     }
     __syncthreads();
 
@@ -422,6 +512,46 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
                 acc = mma(ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
                           ld_h8(&sA[sw(16 * J + lr, 32 * ks + 8 * lq)]), acc);
             st_h4(p.uT + ch * TILE + (size_t)(16 * J + lr) * 128 + 16 * I + 4 * lq, to_h4(acc));
+        }
+    }
+}
+
+// Persistent: each workgroup walks items blockIdx.x, blockIdx.x + gridDim.x, ...
+// (item = chunk * Nv + value head).  With bf16 activations two register
+// stages alternate, so the next item's inputs load while this one computes.
+template <typename ActT>
+__global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
+    __shared__ __align__(16) _Float16 sA[128 * LD16];
+    __shared__ __align__(16) _Float16 sL[128 * LD16];
+    __shared__ float sD[8 * 16 * 17];
+    __shared__ float sGc[128], sBeta[128], sBE[128];
+    const IntraSmem sm{sA, sL, sD, sGc, sBeta, sBE};
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int c4 = tid & 31, tg = tid >> 5;
+    const int n_items = p.meta[p.B] * p.Nv;
+    const int stride = gridDim.x;
+    int it = blockIdx.x;
+    if (it >= n_items) return;
+    if constexpr (sizeof(ActT) == 2) {
+        IntraStage<ActT> A, B;
+        intra_load(A, p, it, wave, lane, lr, lq, c4, tg);
+        while (true) {
+            const int nx = it + stride;
+            if (nx < n_items) intra_load(B, p, nx, wave, lane, lr, lq, c4, tg);
+            intra_item(A, p, sm, tid);
+            if (nx >= n_items) break;
+            it = nx;
+            const int nx2 = it + stride;
+            if (nx2 < n_items) intra_load(A, p, nx2, wave, lane, lr, lq, c4, tg);
+            intra_item(B, p, sm, tid);
+            if (nx2 >= n_items) break;
+            it = nx2;
+        }
+    } else {
+        for (; it < n_items; it += stride) {
+            IntraStage<ActT> A;
+            intra_load(A, p, it, wave, lane, lr, lq, c4, tg);
+            intra_item(A, p, sm, tid);
         }
     }
 }
@@ -724,7 +854,21 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
 
 }  // namespace
 
+// Compute units of the current device (queried once per device).
+static int compute_units() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (!cached[dev]) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool act_bf16, hipStream_t stream) {
+    const int ncu = compute_units();
     PrefillDev p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
     p.state_in = a.state_in; p.out = a.out; p.state_out = a.state_out;
@@ -746,9 +890,11 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
     if (e != hipSuccess) return e;
     const size_t nwg = (size_t)lay.nc * a.Nv;
     if (nwg > 0) {
+        // persistent: two workgroups per CU (LDS < 80 KiB each), each walking items
+        const size_t nint = nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu;
         timing_begin(kIntra, stream);
-        if (act_bf16) hipLaunchKernelGGL(intra_kernel<uint16_t>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
-        else hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
+        if (act_bf16) hipLaunchKernelGGL(intra_kernel<uint16_t>, dim3((unsigned)nint), dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nint), dim3(512), 0, stream, p);
         timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
