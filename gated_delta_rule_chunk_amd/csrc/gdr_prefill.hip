@@ -22,7 +22,7 @@
 //   intra     K1, one workgroup (8 waves) per (chunk, value head): every step
 //             that does not depend on S -- norms, cumsum, decay, L, the
 //             triangular inverse, u and w.  Fully parallel over chunks.
-//   scan      K2, one workgroup (4 waves) per (sequence, value head, slice of
+//   scan      K2, one workgroup (8 waves) per (sequence, value head, slice of
 //             DS state columns).  Columns of S are independent in every step,
 //             so the serial chunk loop is split over 128/DS workgroups.  S
 //             stays in fp32 MFMA accumulators for the whole sequence; per
@@ -35,10 +35,8 @@
 // operands, fp32 accumulation).  fp16 rather than bf16 operands: at the
 // tolerances these results are held to, bf16 rounding of the operands is too
 // coarse, fp16's 11-bit significand is not, and both run at the same rate.
-// The triangular inverse, the gates, the decays and the carried state stay
-// fp32; the merge products of the inverse use a hi/lo fp16 split (three
-// MFMAs per product) so that T itself is accurate to about fp32 before it is
-// rounded once for use.
+// The gates, the decays, the diagonal blocks of the triangular solve and the
+// carried state stay fp32.
 //
 // MFMA 16x16x32 lane layout (lane l, lr = l % 16, lq = l / 16):
 //   A[16 x 32]: lane holds A[lr][8 lq + e], e = 0..7
@@ -175,6 +173,15 @@ __device__ __forceinline__ int sw(int r, int c) {
     return r * LD16 + ((((c >> 3) ^ (r >> 3)) & 15) << 3) + (c & 7);
 }
 
+// The scan's A operands (w [tok][dk] and k^T [dk][tok]) are stored in the
+// workspace in MFMA A-fragment order, so that each fragment load of the scan
+// reads 1 KiB contiguous (whole cache lines): element (r, k) of such a tile
+// sits at 16x32 block (r / 16, k / 32), lane 16 ((k / 8) % 4) + r % 16 of that
+// block, element k % 8 of the lane's 8.
+__device__ __forceinline__ int frag_off(int r, int k) {
+    return (((r >> 4) * 4 + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+
 // ------------------------------------------------------------------ K1: intra-chunk
 // 8 waves; LDS < 80 KiB so that two workgroups share a CU.
 //   sA  fp16 [128][LD16]: k^ [tok][dk] (Gram) -> k^T [dk][tok] (swizzled, copied out)
@@ -186,6 +193,13 @@ __device__ __forceinline__ int sw(int r, int c) {
 // accumulator layout equals its B-operand layout, so each solved block feeds
 // the next product straight from registers; no barrier is needed inside the
 // solve.  Operands are plain fp16 with fp32 accumulation.
+// Load of a lane-uniform int that the running kernel never writes (the chunk
+// map), through the scalar unit: it waits on the scalar counter only, not on
+// the vector-memory counter that also tracks this workgroup's pending stores.
+__device__ __forceinline__ int32_t ld_uniform(const int32_t* ptr) {
+    return *(const __attribute__((address_space(4))) int32_t*)(ptr);
+}
+
 // Raw (unconverted) loads, so that a prefetch does not wait for its data
 // until the data is used.
 template <typename ActT> struct Raw8;
@@ -231,7 +245,10 @@ __device__ __forceinline__ void raw_cvt(const Raw4<float>& x, float (&y)[4]) {
 // Raw inputs of one (chunk, value head) item, held in registers so that the
 // next item's loads are in flight while the current item computes.
 //   k: row 16*wave + lr, key dims 32*ks + 8*lq .. +7 (A-fragment layout)
-//   g0/g1, b0/b1: gate and beta of rows 2*lane, 2*lane+1 (wave 0 only)
+//   g0/g1, b0/b1: gate and beta of rows 2*lane, 2*lane+1 (used by wave 0)
+// Rows past the chunk's end are loaded from its last row (every lane issues
+// the same loads on every path, which keeps the compiler's memory-counter
+// waits exact) and replaced by zeros when converted.
 // (v is first needed late in the item, so each item loads its own v rows at
 // its start.)
 template <typename ActT>
@@ -247,23 +264,21 @@ __device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDe
                                            int lr, int lq, int c4, int tg) {
     const int Nv = p.Nv, Nqk = p.Nqk;
     const int c = item / Nv, h = item % Nv, hq = h / (Nv / Nqk);
-    const int t0 = p.cmap[4 * c + 1], r = p.cmap[4 * c + 2];
+    const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
     st.c = c; st.h = h; st.t0 = t0; st.r = r;
     const ActT* K = static_cast<const ActT*>(p.k);
     const ActT* BETA = static_cast<const ActT*>(p.beta);
-    const int row = 16 * wave + lr;
+    const int last = max(r - 1, 0);   // every mapped chunk has r >= 1
+    const int row = min(16 * wave + lr, last);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        if (row < r) raw_load(st.k[ks], K + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
-        else raw_zero(st.k[ks]);
-    }
-    if (wave == 0) {
-        const int i0 = 2 * lane, i1 = i0 + 1;
-        st.g0 = i0 < r ? p.g[(size_t)(t0 + i0) * Nv + h] : 0.f;
-        st.g1 = i1 < r ? p.g[(size_t)(t0 + i1) * Nv + h] : 0.f;
-        st.b0 = i0 < r ? BETA[(size_t)(t0 + i0) * Nv + h] : ActT(0);
-        st.b1 = i1 < r ? BETA[(size_t)(t0 + i1) * Nv + h] : ActT(0);
-    }
+    for (int ks = 0; ks < 4; ++ks) raw_load(st.k[ks], K + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+    // only wave 0 uses the gates; the other waves issue the same loads at one
+    // lane-uniform address (a single cache line each)
+    const int i0 = wave == 0 ? min(2 * lane, last) : 0, i1 = wave == 0 ? min(2 * lane + 1, last) : 0;
+    st.g0 = p.g[(size_t)(t0 + i0) * Nv + h];
+    st.g1 = p.g[(size_t)(t0 + i1) * Nv + h];
+    st.b0 = BETA[(size_t)(t0 + i0) * Nv + h];
+    st.b1 = BETA[(size_t)(t0 + i1) * Nv + h];
 }
 
 struct IntraSmem {
@@ -297,22 +312,24 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     const bool writes_keys = (h % G) == 0;   // one value head per group stores k^ and k^T
     const int c4 = tid & 31, tg = tid >> 5;   // transposing layout: tokens 8*tg.., columns 4*c4..
 
-    // v rows of this item (first used in step 7; the load overlaps steps 1-6)
+    // v rows of this item (first used in step 7; the load overlaps steps 1-6).
+    // Rows past the chunk's end re-read its last row: they are multiplied by
+    // beta = 0 there.
     Raw4<ActT> vr[8];
     {
         const ActT* V = static_cast<const ActT*>(p.v);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int row = 8 * tg + i;
-            if (row < r) raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4);
-            else raw_zero(vr[i]);
+            const int row = min(8 * tg + i, max(r - 1, 0));
+            raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4);
         }
     }
     __syncthreads();   // the previous item is done with the shared buffers
     // ---- 1. gate cumulative sum and beta (wave 0); k rows normalised -> sA (row-major)
     if (wave == 0) {   // lane owns rows 2l, 2l+1
         const int i0 = 2 * lane, i1 = i0 + 1;
-        const float g0 = st.g0, g1 = st.g1, b0 = load1(&st.b0), b1 = load1(&st.b1);
+        const float g0 = i0 < r ? st.g0 : 0.f, g1 = i1 < r ? st.g1 : 0.f;
+        const float b0 = i0 < r ? load1(&st.b0) : 0.f, b1 = i1 < r ? load1(&st.b1) : 0.f;
         const float s = g0 + g1;
         float incl = s;
 #pragma unroll
@@ -336,7 +353,11 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
         const int row = 16 * wave + lr;
         float kf[4][8];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) raw_cvt(st.k[ks], kf[ks]);
+        for (int ks = 0; ks < 4; ++ks) {
+            raw_cvt(st.k[ks], kf[ks]);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) kf[ks][e] = row < r ? kf[ks][e] : 0.f;
+        }
         float ssq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -412,12 +433,12 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     }
     __syncthreads();
 
-    // ---- 4. unscaled k^T -> workspace; column block j = wave of T by forward substitution
+    // ---- 4. unscaled k^T -> workspace (fragment order); column block j = wave of T by forward substitution
     if (writes_keys) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
             const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
-            st_h8(p.khatT + cq * TILE + (size_t)row * 128 + 8 * gg, ld_h8(&sA[sw(row, 8 * gg)]));
+            st_h8(p.khatT + cq * TILE + frag_off(row, 8 * gg), ld_h8(&sA[sw(row, 8 * gg)]));
         }
     }
     half4 xh[8];
@@ -467,7 +488,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     }
     __syncthreads();
 
-    // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk]  (lower-triangular K
+    // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk], fragment order  (lower-triangular K
     //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
     const int pr = wave & 3, hsel = wave >> 2;
 #pragma unroll
@@ -480,7 +501,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
             for (int ks = 0; ks <= Jt / 2; ++ks)
                 acc = mma(ld_h8(&sA[sw(16 * It + lr, 32 * ks + 8 * lq)]),
                           ld_h8(&sL[(16 * Jt + lr) * LD16 + 32 * ks + 8 * lq]), acc);
-            st_h4(p.w + ch * TILE + (size_t)(16 * Jt + lr) * 128 + 16 * It + 4 * lq, to_h4(acc));
+            st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * It + 4 * lq), to_h4(acc));
         }
     }
     __syncthreads();
@@ -528,21 +549,24 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     const IntraSmem sm{sA, sL, sD, sGc, sBeta, sBE};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int c4 = tid & 31, tg = tid >> 5;
-    const int n_items = p.meta[p.B] * p.Nv;
+    const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
     const int stride = gridDim.x;
     int it = blockIdx.x;
     if (it >= n_items) return;
     if constexpr (sizeof(ActT) == 2) {
         IntraStage<ActT> A, B;
         intra_load(A, p, it, wave, lane, lr, lq, c4, tg);
+        // The next item's loads are issued on every pass (after the last
+        // item they re-read the current one, unused), so that the waits the
+        // compiler places for the current item's data never cover them.
         while (true) {
             const int nx = it + stride;
-            if (nx < n_items) intra_load(B, p, nx, wave, lane, lr, lq, c4, tg);
+            intra_load(B, p, nx < n_items ? nx : it, wave, lane, lr, lq, c4, tg);
             intra_item(A, p, sm, tid);
             if (nx >= n_items) break;
             it = nx;
             const int nx2 = it + stride;
-            if (nx2 < n_items) intra_load(A, p, nx2, wave, lane, lr, lq, c4, tg);
+            intra_load(A, p, nx2 < n_items ? nx2 : it, wave, lane, lr, lq, c4, tg);
             intra_item(B, p, sm, tid);
             if (nx2 >= n_items) break;
             it = nx2;
@@ -571,45 +595,78 @@ struct ScanOps {
 // Per-lane element offsets inside a chunk's tiles, fixed for the whole scan;
 // each chunk only moves the (uniform) tile base pointers.
 struct ScanLane {
-    uint32_t a;    // row 16*wv + lr of w / k^T, columns 8*lq
+    uint32_t a;    // fragment-order w / k^T: rows 16*wv + lr, columns 32*ks + 8*lq (+ 512 ks)
     uint32_t u;    // u^T: column col0 + lr, tokens 16*wv + 4*lq
     uint32_t g;    // g_cum: tokens 16*wv + 4*lq
 };
 
+// One chunk's operands, fetched in three parts: w (first needed by v_new),
+// then u and the gates, then k^T (first needed by the state update).
+template <int CT, int PART>
+__device__ __forceinline__ void scan_load_part(ScanOps<CT>& o, const PrefillDev& p, int c, int h, int hq,
+                                               const ScanLane& ln) {
+    const size_t ch = (size_t)c * p.Nv + h;
+    if constexpr (PART == 0) {
+        const _Float16* W = p.w + ch * TILE;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o.aw[ks] = ld_h8(W + ln.a + 512 * ks);
+    } else if constexpr (PART == 1) {
+        const _Float16* UT = p.uT + ch * TILE;
+        const float* GC = p.gc + ch * 128;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) o.u4[ct] = ld_h4(UT + ln.u + 16 * 128 * ct);
+        o.gcr = *reinterpret_cast<const f32x4*>(GC + ln.g);
+        o.glast = GC[127];
+    } else {
+        const _Float16* KT = p.khatT + ((size_t)c * p.Nqk + hq) * TILE;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o.ak[ks] = ld_h8(KT + ln.a + 512 * ks);
+    }
+}
 template <int CT>
 __device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, int c, int h, int hq,
                                           const ScanLane& ln) {
-    const size_t ch = (size_t)c * p.Nv + h;
-    const _Float16* W = p.w + ch * TILE;
-    const _Float16* KT = p.khatT + ((size_t)c * p.Nqk + hq) * TILE;
-    const _Float16* UT = p.uT + ch * TILE;
-    const float* GC = p.gc + ch * 128;
+    scan_load_part<CT, 0>(o, p, c, h, hq, ln);
+    scan_load_part<CT, 1>(o, p, c, h, hq, ln);
+    scan_load_part<CT, 2>(o, p, c, h, hq, ln);
+}
+
+// Copy DS rows of 128 halves from LDS (row pitch LD16) to a workspace tile
+// (row pitch 128). Every lane stores in every call (16-byte pieces, or 8-byte
+// pieces for a 16-row slice), so no wave skips a store.
+template <int DS>
+__device__ __forceinline__ void scan_copy_out(_Float16* dst, const _Float16* src, int tid) {
+    if constexpr (DS * 16 >= 512) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        o.aw[ks] = ld_h8(W + ln.a + 32 * ks);
-        o.ak[ks] = ld_h8(KT + ln.a + 32 * ks);
+        for (int n = 0; n < DS * 16 / 512; ++n) {
+            const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
+            st_h8(dst + (size_t)row * 128 + 8 * cc, ld_h8(&src[row * LD16 + 8 * cc]));
+        }
+    } else {
+        static_assert(DS * 32 == 512, "a 16-row slice takes one 8-byte piece per lane");
+        const int row = tid >> 5, cc = tid & 31;
+        st_h4(dst + (size_t)row * 128 + 4 * cc, ld_h4(&src[row * LD16 + 4 * cc]));
     }
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct) o.u4[ct] = ld_h4(UT + ln.u + 16 * 128 * ct);
-    o.gcr = *reinterpret_cast<const f32x4*>(GC + ln.g);
-    o.glast = GC[127];
 }
 
 // One chunk of the scan: record S_c and v_new for the output kernel, then
-// S <- exp(g_last) S + k^T (v_new exp(g_last - g_cum)).
-template <int DS>
+// S <- exp(g_last) S + k^T (v_new exp(g_last - g_cum)).  With LOAD, the
+// operands of chunk cn are fetched into nx in three parts spread over the
+// step (a burst of fetches would stall the waves' in-order issue behind the
+// memory pipeline); scheduling barriers keep the parts where they are.
+template <int DS, bool LOAD>
 __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[DS / 16], const PrefillDev& p,
                                           int c, int h, _Float16* sST, _Float16* sVn, _Float16* sVr, int tid,
-                                          int wv, int lr, int lq, int col0) {
+                                          int wv, int lr, int lq, int col0,
+                                          ScanOps<DS / 16>& nx, int cn, int hq, const ScanLane& ln) {
     constexpr int CT = DS / 16;
     const size_t ch = (size_t)c * p.Nv + h;
-    // the state at the start of this chunk, for the output kernel
-#pragma unroll
-    for (int n = 0; n < (DS * 16 + 511) / 512; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
-        if (DS * 16 >= 512 || e_ < DS * 16)
-            st_h8(p.ST + ch * TILE + (size_t)(col0 + row) * 128 + 8 * cc, ld_h8(&sST[row * LD16 + 8 * cc]));
+    if constexpr (LOAD) {
+        scan_load_part<CT, 0>(nx, p, cn, h, hq, ln);
+        __builtin_amdgcn_sched_barrier(0);
     }
+    // the state at the start of this chunk, for the output kernel
+    scan_copy_out<DS>(p.ST + ch * TILE + (size_t)col0 * 128, sST, tid);
     // v_new = u - w S for tokens 16*wv + 4*lq + e
     const int tok = 16 * wv + 4 * lq;
 #pragma unroll
@@ -627,13 +684,18 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
         st_h4(&sVr[col * LD16 + tok], to_h4(vn));
         st_h4(&sVn[col * LD16 + tok], to_h4(vs));
     }
+    if constexpr (LOAD) {
+        __builtin_amdgcn_sched_barrier(0);
+        scan_load_part<CT, 1>(nx, p, cn, h, hq, ln);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     __syncthreads();
     // v_new^T of this chunk and slice -> workspace, 16-byte coalesced pieces
-#pragma unroll
-    for (int n = 0; n < (DS * 16 + 511) / 512; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
-        if (DS * 16 >= 512 || e_ < DS * 16)
-            st_h8(p.vnT + ch * TILE + (size_t)(col0 + row) * 128 + 8 * cc, ld_h8(&sVr[row * LD16 + 8 * cc]));
+    scan_copy_out<DS>(p.vnT + ch * TILE + (size_t)col0 * 128, sVr, tid);
+    if constexpr (LOAD) {
+        __builtin_amdgcn_sched_barrier(0);
+        scan_load_part<CT, 2>(nx, p, cn, h, hq, ln);
+        __builtin_amdgcn_sched_barrier(0);
     }
     const float dec = __expf(o.glast);
 #pragma unroll
@@ -654,14 +716,16 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sVn[DS * LD16];   // scaled v_new^T [col][tok]
     __shared__ __align__(16) _Float16 sVr[DS * LD16];   // v_new^T [col][tok], staged for the workspace
 
-    // XCD-aware placement: the NS slices of one (sequence, head) stream read
-    // the same w / k^T tiles, so they are given workgroup ids that the
-    // hardware dispatches to the same XCD (id mod 8) and share its L2.
+    // XCD-aware placement: the NS slices of a (sequence, value head) stream
+    // read the same w tiles, and the G value heads of one qk head read the
+    // same k^T tiles, so all G*NS workgroups of a (sequence, qk head) group
+    // get ids the hardware dispatches to one XCD (id mod 8), sharing its L2.
+    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
     const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
-    const int slice = j % NS, stream = (j / NS) * 8 + xcd;
-    if (stream >= p.B * p.Nv) return;
-    const int Nv = p.Nv, Nqk = p.Nqk;
-    const int b = stream / Nv, h = stream % Nv, hq = h / (Nv / Nqk);
+    const int local = j % (G * NS), grp = (j / (G * NS)) * 8 + xcd;
+    if (grp >= p.B * Nqk) return;
+    const int slice = local % NS, stream = grp * G + local / NS;
+    const int b = stream / Nv, h = stream % Nv, hq = h / G;
     const int col0 = slice * DS;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
 
@@ -679,37 +743,47 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     for (int ct = 0; ct < CT; ++ct) st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(S[ct]));
 
     const int c0 = p.meta[b], c1 = p.meta[b + 1];
-    const ScanLane ln{(uint32_t)((16 * wv + lr) * 128 + 8 * lq), (uint32_t)((col0 + lr) * 128 + 16 * wv + 4 * lq),
+    const ScanLane ln{(uint32_t)(frag_off(16 * wv + lr, 8 * lq)), (uint32_t)((col0 + lr) * 128 + 16 * wv + 4 * lq),
                       (uint32_t)(16 * wv + 4 * lq)};
     // Register sets rotate between the chunk being computed and the ones being
     // fetched (no copies between them, so each chunk's compute waits only for
     // its own operands): three sets (two chunks of lookahead) up to 64 columns,
     // two sets at 128 columns, where a third would not fit in registers.
-    if constexpr (DS <= 64) {
-        ScanOps<CT> A, B, C;
-        if (c0 < c1) scan_load(A, p, c0, h, hq, ln);
-        if (c0 + 1 < c1) scan_load(B, p, c0 + 1, h, hq, ln);
-        __syncthreads();
-        for (int c = c0; c < c1; c += 3) {
-            if (c + 2 < c1) scan_load(C, p, c + 2, h, hq, ln);
-            scan_step<DS>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
-            if (c + 1 >= c1) break;
-            if (c + 3 < c1) scan_load(A, p, c + 3, h, hq, ln);
-            scan_step<DS>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
-            if (c + 2 >= c1) break;
-            if (c + 4 < c1) scan_load(B, p, c + 4, h, hq, ln);
-            scan_step<DS>(C, S, p, c + 2, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
-        }
-    } else {
-        ScanOps<CT> A, B;
-        if (c0 < c1) scan_load(A, p, c0, h, hq, ln);
-        __syncthreads();
-        for (int c = c0; c < c1; c += 2) {
-            if (c + 1 < c1) scan_load(B, p, c + 1, h, hq, ln);
-            scan_step<DS>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
-            if (c + 1 >= c1) break;
-            if (c + 2 < c1) scan_load(A, p, c + 2, h, hq, ln);
-            scan_step<DS>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0);
+    // The compiler's memory-counter waits are exact only when every path into
+    // a wait issued the same loads in the same order, so: every fetch is
+    // issued unconditionally (past the last chunk it re-reads the last chunk,
+    // unused), the prologue issues the sets whole and in loop order, and the
+    // main loop runs whole rounds with one back edge; the last chunks that do
+    // not fill a round are done after it, fetching nothing.
+    const int cl = c1 - 1;
+    __syncthreads();
+    if (c0 < c1) {
+        int c = c0;
+        if constexpr (DS <= 64) {
+            ScanOps<CT> A, B, C;
+            scan_load(A, p, c0, h, hq, ln);
+            __builtin_amdgcn_sched_barrier(0);
+            scan_load(B, p, min(c0 + 1, cl), h, hq, ln);
+            __builtin_amdgcn_sched_barrier(0);
+            for (; c + 3 <= c1; c += 3) {
+                scan_step<DS, true>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq, ln);
+                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0, A, min(c + 3, cl), hq,
+                                    ln);
+                scan_step<DS, true>(C, S, p, c + 2, h, sST, sVn, sVr, tid, wv, lr, lq, col0, B, min(c + 4, cl), hq,
+                                    ln);
+            }
+            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, C, 0, hq, ln);
+            if (c + 1 < c1) scan_step<DS, false>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0, C, 0, hq, ln);
+        } else {
+            ScanOps<CT> A, B;
+            scan_load(A, p, c0, h, hq, ln);
+            __builtin_amdgcn_sched_barrier(0);
+            for (; c + 2 <= c1; c += 2) {
+                scan_step<DS, true>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq, ln);
+                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0, A, min(c + 2, cl), hq,
+                                    ln);
+            }
+            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, B, 0, hq, ln);
         }
     }
 #pragma unroll
@@ -744,11 +818,12 @@ template <typename ActT>
 __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sBuf[128 * LD16];
     __shared__ __align__(16) _Float16 sP[128 * LD16];
+    __shared__ float sG[128];   // g_cum of the chunk
 
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
     const int c = blockIdx.x / Nv, h = blockIdx.x % Nv, hq = h / G;
-    if (c >= p.meta[p.B]) return;
-    const int t0 = p.cmap[4 * c + 1], r = p.cmap[4 * c + 2];
+    if (c >= ld_uniform(&p.meta[p.B])) return;
+    const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const ActT* Q = static_cast<const ActT*>(p.q);
     ActT* OUT = static_cast<ActT*>(p.out);
@@ -758,19 +833,16 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
 
     u32x4 stage[4];
     tile_fetch(stage, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
+    const float gmine = GC[tid & 127];
     // q^ (scaled) and q^ e^{g_cum} for rows 16 I + lr
     half8 qh[4], qe[4];
     {
-        const int row = 16 * I + lr;
+        // rows past the chunk's end re-read its last row (their outputs are
+        // never stored, and P is zero above the diagonal)
+        const int row = 16 * I + lr, lrow = min(row, max(r - 1, 0));
         float x[4][8];
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            if (row < r) load8(Q + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq, x[ks]);
-            else {
-#pragma unroll
-                for (int e = 0; e < 8; ++e) x[ks][e] = 0.f;
-            }
-        }
+        for (int ks = 0; ks < 4; ++ks) load8(Q + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq, x[ks]);
         float ssq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -790,6 +862,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         }
     }
     tile_store(stage, sBuf, tid);
+    if (tid < 128) sG[tid] = gmine;
     tile_fetch(stage, p.ST + ch * TILE, tid);
     __syncthreads();
 
@@ -802,7 +875,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * lq + e;
-            sP[i * LD16 + j] = (_Float16)(i >= j ? acc[e] * __expf(GC[i] - GC[j]) : 0.f);
+            sP[i * LD16 + j] = (_Float16)(i >= j ? acc[e] * __expf(sG[i] - sG[j]) : 0.f);
         }
     }
     if ((I & 1) == 0) {
@@ -899,10 +972,14 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // State columns are split over NS = 128 / DS workgroups per (sequence,
-    // head) stream, so that streams x NS fills the chip (about 256 groups).
+    // head) stream.  A narrower slice shortens each serial step (less MFMA
+    // and LDS work per workgroup) but every slice fetches the chunk's whole w
+    // and k^T tiles; on 256 CUs the best measured split keeps streams x NS
+    // between 256 and about 1024 workgroups.
     const size_t nstream = (size_t)a.B * a.Nv;
-    const int ns = nstream >= 256 ? 1 : nstream >= 128 ? 2 : nstream >= 64 ? 4 : 8;
-    const size_t nscan = (nstream + 7) / 8 * 8 * ns;
+    const int ns = nstream >= 512 ? 1 : nstream >= 256 ? 2 : nstream >= 64 ? 4 : 8;
+    const size_t ngroup = (size_t)a.B * a.Nqk;
+    const size_t nscan = (ngroup + 7) / 8 * 8 * (size_t)(a.Nv / a.Nqk) * ns;
     timing_begin(kScan, stream);
     switch (ns) {
         case 1: hipLaunchKernelGGL(scan_kernel<128>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
