@@ -46,7 +46,7 @@ PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
     L.off_khat = off;  off = align256(off + tile16 * nc * (size_t)Nqk);
     L.off_khatT = off; off = align256(off + tile16 * nc * (size_t)Nqk);
     L.off_w = off;     off = align256(off + tile16 * nc * (size_t)Nv);
-    L.off_uT = off;    off = align256(off + tile16 * nc * (size_t)Nv);
+    L.off_u = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_gc = off;    off = align256(off + sizeof(float) * kChunk * nc * (size_t)Nv);
     L.off_vnT = off;   off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_ST = off;    off = align256(off + tile16 * nc * (size_t)Nv);

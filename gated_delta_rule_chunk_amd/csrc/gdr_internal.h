@@ -40,15 +40,17 @@ hipError_t decode_launch(const DecodeArgs& a, bool act_bf16, bool state_bf16, hi
 // Workspace layout.  NC = upper bound on the number of 128-token chunks over
 // all sequences: sum_b ceil(len_b / 128) <= (T + B*127) / 128.  Every
 // per-(chunk, head) tile is 128 x 128 fp16 (32 KiB), zero-padded past the
-// chunk's valid rows.
+// chunk's valid rows.  Tiles marked "fragment order" hold their elements in
+// the order of the MFMA registers that write or read them (the prefill
+// source defines the two orders), not row-major.
 struct PrefillLayout {
     int64_t nc;             // chunk bound
     size_t off_meta;        // int32 [B+2]: first chunk of each sequence, then the total
     size_t off_cmap;        // int4  [NC]: (sequence, first token, valid rows, -)
-    size_t off_khat;        // fp16  [NC][Nqk][128 tok][128 dk]  normalised keys
-    size_t off_khatT;       // fp16  [NC][Nqk][128 dk][128 tok]  the same, transposed
-    size_t off_w;           // fp16  [NC][Nv][128 tok][128 dk]   w = T (k^ beta e^gcum)
-    size_t off_uT;          // fp16  [NC][Nv][128 col][128 tok]  u = T (v beta), transposed
+    size_t off_khat;        // fp16  [NC][Nqk] 128 tok x 128 dk, fragment order: normalised keys
+    size_t off_khatT;       // fp16  [NC][Nqk] 128 dk x 128 tok, fragment order: the same, transposed
+    size_t off_w;           // fp16  [NC][Nv]  128 tok x 128 dk, fragment order: w = T (k^ beta e^gcum)
+    size_t off_u;           // fp16  [NC][Nv]  128 tok x 128 col, fragment order: u = T (v beta)
     size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate
     size_t off_vnT;         // fp16  [NC][Nv][128 col][128 tok]  v_new = u - w S, transposed
     size_t off_ST;          // fp16  [NC][Nv][128 col][128 dk]   state at chunk start, transposed

@@ -67,7 +67,7 @@ struct PrefillDev {
     _Float16* khat;
     _Float16* khatT;
     _Float16* w;
-    _Float16* uT;
+    _Float16* u;
     float* gc;
     _Float16* vnT;
     _Float16* ST;
@@ -173,13 +173,26 @@ __device__ __forceinline__ int sw(int r, int c) {
     return r * LD16 + ((((c >> 3) ^ (r >> 3)) & 15) << 3) + (c & 7);
 }
 
-// The scan's A operands (w [tok][dk] and k^T [dk][tok]) are stored in the
-// workspace in MFMA A-fragment order, so that each fragment load of the scan
-// reads 1 KiB contiguous (whole cache lines): element (r, k) of such a tile
-// sits at 16x32 block (r / 16, k / 32), lane 16 ((k / 8) % 4) + r % 16 of that
-// block, element k % 8 of the lane's 8.
+// Workspace tiles that are written or read straight from MFMA registers are
+// stored in the order of those registers, so that every such access is
+// 512 B - 1 KiB contiguous (whole cache lines):
+//  * A-fragment order (k^ [tok][dk], k^T [dk][tok], w [tok][dk]): element
+//    (r, k) sits at 16x32 block (r / 16, k / 32), lane 16 ((k / 8) % 4) +
+//    r % 16 of that block, element k % 8 of the lane's 8.
+//  * C-fragment order (u [tok][col]): element (r, c) sits at 16x16 block
+//    (r / 16, c / 16), lane 16 ((r / 4) % 4) + c % 16, element r % 4.
 __device__ __forceinline__ int frag_off(int r, int k) {
     return (((r >> 4) * 4 + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) * 8 + (k & 7);
+}
+__device__ __forceinline__ int cfrag_off(int r, int c) {
+    return (((r >> 4) * 8 + (c >> 4)) * 64 + ((r >> 2) & 3) * 16 + (c & 15)) * 4 + (r & 3);
+}
+// Row and first column of the 8-element piece number e of an A-fragment tile
+// (pieces in storage order).
+__device__ __forceinline__ void frag_piece(int e, int& r, int& k) {
+    const int blk = e >> 6, l = e & 63;
+    r = 16 * (blk >> 2) + (l & 15);
+    k = 32 * (blk & 3) + 8 * (l >> 4);
 }
 
 // ------------------------------------------------------------------ K1: intra-chunk
@@ -373,7 +386,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
             for (int e = 0; e < 8; ++e) kx[e] = kf[ks][e] * rinv;
             const half8 kh = to_h8(kx);
             st_h8(&sA[row * LD16 + 32 * ks + 8 * lq], kh);
-            if (writes_keys) st_h8(p.khat + cq * TILE + (size_t)row * 128 + 32 * ks + 8 * lq, kh);
+            if (writes_keys) st_h8(p.khat + cq * TILE + frag_off(row, 32 * ks + 8 * lq), kh);
         }
     }
     __syncthreads();
@@ -437,8 +450,10 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     if (writes_keys) {
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-            const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
-            st_h8(p.khatT + cq * TILE + frag_off(row, 8 * gg), ld_h8(&sA[sw(row, 8 * gg)]));
+            const int e_ = tid + 512 * n;
+            int row, kc;
+            frag_piece(e_, row, kc);
+            st_h8(p.khatT + cq * TILE + (size_t)e_ * 8, ld_h8(&sA[sw(row, kc)]));
         }
     }
     half4 xh[8];
@@ -521,7 +536,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     }
     __syncthreads();
 
-    // ---- 8. u = T (v beta) -> uT [col][tok]
+    // ---- 8. u = T (v beta) -> u, fragment order
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const int I = which ? 7 - pr : pr;
@@ -532,7 +547,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
             for (int ks = 0; ks <= I / 2; ++ks)
                 acc = mma(ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
                           ld_h8(&sA[sw(16 * J + lr, 32 * ks + 8 * lq)]), acc);
-            st_h4(p.uT + ch * TILE + (size_t)(16 * J + lr) * 128 + 16 * I + 4 * lq, to_h4(acc));
+            st_h4(p.u + ch * TILE + cfrag_off(16 * I + 4 * lq, 16 * J + lr), to_h4(acc));
         }
     }
 }
@@ -596,7 +611,7 @@ struct ScanOps {
 // each chunk only moves the (uniform) tile base pointers.
 struct ScanLane {
     uint32_t a;    // fragment-order w / k^T: rows 16*wv + lr, columns 32*ks + 8*lq (+ 512 ks)
-    uint32_t u;    // u^T: column col0 + lr, tokens 16*wv + 4*lq
+    uint32_t u;    // C-fragment-order u: tokens 16*wv + 4*lq, column col0 + lr (+ 256 ct)
     uint32_t g;    // g_cum: tokens 16*wv + 4*lq
 };
 
@@ -611,10 +626,10 @@ __device__ __forceinline__ void scan_load_part(ScanOps<CT>& o, const PrefillDev&
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) o.aw[ks] = ld_h8(W + ln.a + 512 * ks);
     } else if constexpr (PART == 1) {
-        const _Float16* UT = p.uT + ch * TILE;
+        const _Float16* U = p.u + ch * TILE;
         const float* GC = p.gc + ch * 128;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct) o.u4[ct] = ld_h4(UT + ln.u + 16 * 128 * ct);
+        for (int ct = 0; ct < CT; ++ct) o.u4[ct] = ld_h4(U + ln.u + 256 * ct);
         o.gcr = *reinterpret_cast<const f32x4*>(GC + ln.g);
         o.glast = GC[127];
     } else {
@@ -743,7 +758,7 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     for (int ct = 0; ct < CT; ++ct) st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(S[ct]));
 
     const int c0 = p.meta[b], c1 = p.meta[b + 1];
-    const ScanLane ln{(uint32_t)(frag_off(16 * wv + lr, 8 * lq)), (uint32_t)((col0 + lr) * 128 + 16 * wv + 4 * lq),
+    const ScanLane ln{(uint32_t)(frag_off(16 * wv + lr, 8 * lq)), (uint32_t)(cfrag_off(16 * wv + 4 * lq, col0 + lr)),
                       (uint32_t)(16 * wv + 4 * lq)};
     // Register sets rotate between the chunk being computed and the ones being
     // fetched (no copies between them, so each chunk's compute waits only for
@@ -806,6 +821,20 @@ __device__ __forceinline__ void tile_fetch(u32x4 (&rg)[4], const _Float16* src, 
         rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)row * 128 + 8 * gg);
     }
 }
+// An A-fragment-order tile, fetched in storage order (16 B per lane, 1 KiB
+// contiguous per wave) and placed row-major in LDS.
+__device__ __forceinline__ void frag_tile_fetch(u32x4 (&rg)[4], const _Float16* src, int tid) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + 512 * n) * 8);
+}
+__device__ __forceinline__ void frag_tile_store(const u32x4 (&rg)[4], _Float16* dst, int tid) {
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        int row, k;
+        frag_piece(tid + 512 * n, row, k);
+        *reinterpret_cast<u32x4*>(dst + row * LD16 + k) = rg[n];
+    }
+}
 __device__ __forceinline__ void tile_store(const u32x4 (&rg)[4], _Float16* dst, int tid) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -832,7 +861,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     const int I = wv;
 
     u32x4 stage[4];
-    tile_fetch(stage, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
+    frag_tile_fetch(stage, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
     const float gmine = GC[tid & 127];
     // q^ (scaled) and q^ e^{g_cum} for rows 16 I + lr
     half8 qh[4], qe[4];
@@ -861,7 +890,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
             qe[ks] = to_h8(z);
         }
     }
-    tile_store(stage, sBuf, tid);
+    frag_tile_store(stage, sBuf, tid);   // k^ [tok][dk]
     if (tid < 128) sG[tid] = gmine;
     tile_fetch(stage, p.ST + ch * TILE, tid);
     __syncthreads();
@@ -950,7 +979,7 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
     p.khat = reinterpret_cast<_Float16*>(a.ws + lay.off_khat);
     p.khatT = reinterpret_cast<_Float16*>(a.ws + lay.off_khatT);
     p.w = reinterpret_cast<_Float16*>(a.ws + lay.off_w);
-    p.uT = reinterpret_cast<_Float16*>(a.ws + lay.off_uT);
+    p.u = reinterpret_cast<_Float16*>(a.ws + lay.off_u);
     p.gc = reinterpret_cast<float*>(a.ws + lay.off_gc);
     p.vnT = reinterpret_cast<_Float16*>(a.ws + lay.off_vnT);
     p.ST = reinterpret_cast<_Float16*>(a.ws + lay.off_ST);
