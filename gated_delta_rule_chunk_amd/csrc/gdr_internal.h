@@ -52,8 +52,8 @@ struct PrefillLayout {
     size_t off_w;           // fp16  [NC][Nv]  128 tok x 128 dk, fragment order: w = T (k^ beta e^gcum)
     size_t off_u;           // fp16  [NC][Nv]  128 tok x 128 col, fragment order: u = T (v beta)
     size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate
-    size_t off_vnT;         // fp16  [NC][Nv][128 col][128 tok]  v_new = u - w S, transposed
-    size_t off_ST;          // fp16  [NC][Nv][128 col][128 dk]   state at chunk start, transposed
+    size_t off_vn;          // fp16  [NC][Nv]  128 tok x 128 col, fragment order: v_new = u - w S
+    size_t off_Sc;          // fp16  [NC][Nv]  128 dk x 128 col, fragment order: state at chunk start
     size_t total;
 };
 

@@ -69,8 +69,8 @@ struct PrefillDev {
     _Float16* w;
     _Float16* u;
     float* gc;
-    _Float16* vnT;
-    _Float16* ST;
+    _Float16* vn;
+    _Float16* Sc;
     int64_t T;
     int64_t nc;
     int32_t B, Nqk, Nv;
@@ -646,24 +646,6 @@ __device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, i
     scan_load_part<CT, 2>(o, p, c, h, hq, ln);
 }
 
-// Copy DS rows of 128 halves from LDS (row pitch LD16) to a workspace tile
-// (row pitch 128). Every lane stores in every call (16-byte pieces, or 8-byte
-// pieces for a 16-row slice), so no wave skips a store.
-template <int DS>
-__device__ __forceinline__ void scan_copy_out(_Float16* dst, const _Float16* src, int tid) {
-    if constexpr (DS * 16 >= 512) {
-#pragma unroll
-        for (int n = 0; n < DS * 16 / 512; ++n) {
-            const int e_ = tid + 512 * n, row = e_ >> 4, cc = e_ & 15;
-            st_h8(dst + (size_t)row * 128 + 8 * cc, ld_h8(&src[row * LD16 + 8 * cc]));
-        }
-    } else {
-        static_assert(DS * 32 == 512, "a 16-row slice takes one 8-byte piece per lane");
-        const int row = tid >> 5, cc = tid & 31;
-        st_h4(dst + (size_t)row * 128 + 4 * cc, ld_h4(&src[row * LD16 + 4 * cc]));
-    }
-}
-
 // One chunk of the scan: record S_c and v_new for the output kernel, then
 // S <- exp(g_last) S + k^T (v_new exp(g_last - g_cum)).  With LOAD, the
 // operands of chunk cn are fetched into nx in three parts spread over the
@@ -671,7 +653,7 @@ __device__ __forceinline__ void scan_copy_out(_Float16* dst, const _Float16* src
 // memory pipeline); scheduling barriers keep the parts where they are.
 template <int DS, bool LOAD>
 __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[DS / 16], const PrefillDev& p,
-                                          int c, int h, _Float16* sST, _Float16* sVn, _Float16* sVr, int tid,
+                                          int c, int h, _Float16* sST, _Float16* sVn, int tid,
                                           int wv, int lr, int lq, int col0,
                                           ScanOps<DS / 16>& nx, int cn, int hq, const ScanLane& ln) {
     constexpr int CT = DS / 16;
@@ -680,10 +662,12 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
         scan_load_part<CT, 0>(nx, p, cn, h, hq, ln);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // the state at the start of this chunk, for the output kernel
-    scan_copy_out<DS>(p.ST + ch * TILE + (size_t)col0 * 128, sST, tid);
-    // v_new = u - w S for tokens 16*wv + 4*lq + e
+    // the state at the start of this chunk, for the output kernel (C-fragment
+    // order: straight from the accumulators, 512 B contiguous per store)
     const int tok = 16 * wv + 4 * lq;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) st_h4(p.Sc + ch * TILE + cfrag_off(tok, col0 + 16 * ct + lr), to_h4(S[ct]));
+    // v_new = u - w S for tokens 16*wv + 4*lq + e
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         f32x4 vp = {0.f, 0.f, 0.f, 0.f};
@@ -696,7 +680,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
             vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
         }
         const int col = 16 * ct + lr;
-        st_h4(&sVr[col * LD16 + tok], to_h4(vn));
+        st_h4(p.vn + ch * TILE + cfrag_off(tok, col0 + col), to_h4(vn));
         st_h4(&sVn[col * LD16 + tok], to_h4(vs));
     }
     if constexpr (LOAD) {
@@ -705,8 +689,6 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
-    // v_new^T of this chunk and slice -> workspace, 16-byte coalesced pieces
-    scan_copy_out<DS>(p.vnT + ch * TILE + (size_t)col0 * 128, sVr, tid);
     if constexpr (LOAD) {
         __builtin_amdgcn_sched_barrier(0);
         scan_load_part<CT, 2>(nx, p, cn, h, hq, ln);
@@ -729,7 +711,6 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     constexpr int NS = 128 / DS, CT = DS / 16;
     __shared__ __align__(16) _Float16 sST[DS * LD16];   // S^T [col][dk] (fp16), current chunk's start state
     __shared__ __align__(16) _Float16 sVn[DS * LD16];   // scaled v_new^T [col][tok]
-    __shared__ __align__(16) _Float16 sVr[DS * LD16];   // v_new^T [col][tok], staged for the workspace
 
     // XCD-aware placement: the NS slices of a (sequence, value head) stream
     // read the same w tiles, and the G value heads of one qk head read the
@@ -781,24 +762,24 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
             scan_load(B, p, min(c0 + 1, cl), h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
             for (; c + 3 <= c1; c += 3) {
-                scan_step<DS, true>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq, ln);
-                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0, A, min(c + 3, cl), hq,
+                scan_step<DS, true>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq, ln);
+                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 3, cl), hq,
                                     ln);
-                scan_step<DS, true>(C, S, p, c + 2, h, sST, sVn, sVr, tid, wv, lr, lq, col0, B, min(c + 4, cl), hq,
+                scan_step<DS, true>(C, S, p, c + 2, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 4, cl), hq,
                                     ln);
             }
-            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, C, 0, hq, ln);
-            if (c + 1 < c1) scan_step<DS, false>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0, C, 0, hq, ln);
+            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln);
+            if (c + 1 < c1) scan_step<DS, false>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln);
         } else {
             ScanOps<CT> A, B;
             scan_load(A, p, c0, h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
             for (; c + 2 <= c1; c += 2) {
-                scan_step<DS, true>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq, ln);
-                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, sVr, tid, wv, lr, lq, col0, A, min(c + 2, cl), hq,
+                scan_step<DS, true>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq, ln);
+                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 2, cl), hq,
                                     ln);
             }
-            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, sVr, tid, wv, lr, lq, col0, B, 0, hq, ln);
+            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, 0, hq, ln);
         }
     }
 #pragma unroll
@@ -814,13 +795,6 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
 // 8 waves; wave w owns output rows 16w .. 16w+15.  The three 32 KiB operand
 // tiles (k^, S_c^T, v_new^T) pass one after another through one LDS buffer,
 // each fetched into registers while the previous one is in use.
-__device__ __forceinline__ void tile_fetch(u32x4 (&rg)[4], const _Float16* src, int tid) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
-        rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)row * 128 + 8 * gg);
-    }
-}
 // An A-fragment-order tile, fetched in storage order (16 B per lane, 1 KiB
 // contiguous per wave) and placed row-major in LDS.
 __device__ __forceinline__ void frag_tile_fetch(u32x4 (&rg)[4], const _Float16* src, int tid) {
@@ -835,11 +809,16 @@ __device__ __forceinline__ void frag_tile_store(const u32x4 (&rg)[4], _Float16* 
         *reinterpret_cast<u32x4*>(dst + row * LD16 + k) = rg[n];
     }
 }
-__device__ __forceinline__ void tile_store(const u32x4 (&rg)[4], _Float16* dst, int tid) {
+// A C-fragment-order tile X [row][col] (fetched in storage order by
+// frag_tile_fetch) placed transposed in LDS, X^T [col][row]: each 16-byte
+// piece holds two lanes' runs of 4 rows.
+__device__ __forceinline__ void cfrag_tile_store_t(const u32x4 (&rg)[4], _Float16* dst, int tid) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
-        *reinterpret_cast<u32x4*>(dst + row * LD16 + 8 * gg) = rg[n];
+        const int e = tid + 512 * n, blk = e >> 5, l = 2 * (e & 31);
+        const int r = 16 * (blk >> 3) + 4 * (l >> 4), c = 16 * (blk & 7) + (l & 15);
+        *reinterpret_cast<u32x2*>(dst + c * LD16 + r) = u32x2{rg[n][0], rg[n][1]};
+        *reinterpret_cast<u32x2*>(dst + (c + 1) * LD16 + r) = u32x2{rg[n][2], rg[n][3]};
     }
 }
 
@@ -892,7 +871,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     }
     frag_tile_store(stage, sBuf, tid);   // k^ [tok][dk]
     if (tid < 128) sG[tid] = gmine;
-    tile_fetch(stage, p.ST + ch * TILE, tid);
+    frag_tile_fetch(stage, p.Sc + ch * TILE, tid);
     __syncthreads();
 
     // P = (q^ k^T) . D on the inclusive lower triangle -> sP rows of this wave
@@ -912,8 +891,8 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         for (int e = 0; e < 4; ++e) sP[(16 * I + 4 * lq + e) * LD16 + 16 * (I + 1) + lr] = (_Float16)0.f;
     }
     __syncthreads();
-    tile_store(stage, sBuf, tid);   // S_c^T [col][dk]
-    tile_fetch(stage, p.vnT + ch * TILE, tid);
+    cfrag_tile_store_t(stage, sBuf, tid);   // S_c^T [col][dk]
+    frag_tile_fetch(stage, p.vn + ch * TILE, tid);
     __syncthreads();
 
     f32x4 o[8];
@@ -925,7 +904,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         o[ct] = acc;
     }
     __syncthreads();
-    tile_store(stage, sBuf, tid);   // v_new^T [col][tok]
+    cfrag_tile_store_t(stage, sBuf, tid);   // v_new^T [col][tok]
     __syncthreads();
     for (int ks = 0; ks <= I / 2; ++ks) {
         const half8 a = ld_h8(&sP[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
@@ -981,8 +960,8 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
     p.w = reinterpret_cast<_Float16*>(a.ws + lay.off_w);
     p.u = reinterpret_cast<_Float16*>(a.ws + lay.off_u);
     p.gc = reinterpret_cast<float*>(a.ws + lay.off_gc);
-    p.vnT = reinterpret_cast<_Float16*>(a.ws + lay.off_vnT);
-    p.ST = reinterpret_cast<_Float16*>(a.ws + lay.off_ST);
+    p.vn = reinterpret_cast<_Float16*>(a.ws + lay.off_vn);
+    p.Sc = reinterpret_cast<_Float16*>(a.ws + lay.off_Sc);
     p.T = a.T; p.nc = lay.nc; p.B = a.B; p.Nqk = a.Nqk; p.Nv = a.Nv; p.scale = a.scale;
 
     timing_begin(kChunkmap, stream);
