@@ -839,9 +839,10 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     const float* GC = p.gc + ch * 128;
     const int I = wv;
 
-    u32x4 stage[4];
-    frag_tile_fetch(stage, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
-    const float gmine = GC[tid & 127];
+    // All of the item's tiles are fetched up front (one memory latency per
+    // item rather than one per phase); the q rows follow the first.
+    u32x4 stK[4], stS[4], stV[4];
+    frag_tile_fetch(stK, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
     // q^ (scaled) and q^ e^{g_cum} for rows 16 I + lr
     half8 qh[4], qe[4];
     {
@@ -851,6 +852,13 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         float x[4][8];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) load8(Q + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq, x[ks]);
+        const float eg = __expf(GC[row]);
+        const float gmine = GC[tid & 127];
+        __builtin_amdgcn_sched_barrier(0);
+        frag_tile_fetch(stS, p.Sc + ch * TILE, tid);
+        frag_tile_fetch(stV, p.vn + ch * TILE, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        if (tid < 128) sG[tid] = gmine;
         float ssq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -859,7 +867,6 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         ssq += __shfl_xor(ssq, 16);
         ssq += __shfl_xor(ssq, 32);
         const float rinv = p.scale / sqrtf(ssq + kNormEps);
-        const float eg = __expf(GC[row]);
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             float y[8], z[8];
@@ -869,9 +876,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
             qe[ks] = to_h8(z);
         }
     }
-    frag_tile_store(stage, sBuf, tid);   // k^ [tok][dk]
-    if (tid < 128) sG[tid] = gmine;
-    frag_tile_fetch(stage, p.Sc + ch * TILE, tid);
+    frag_tile_store(stK, sBuf, tid);   // k^ [tok][dk]
     __syncthreads();
 
     // P = (q^ k^T) . D on the inclusive lower triangle -> sP rows of this wave
@@ -891,8 +896,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         for (int e = 0; e < 4; ++e) sP[(16 * I + 4 * lq + e) * LD16 + 16 * (I + 1) + lr] = (_Float16)0.f;
     }
     __syncthreads();
-    cfrag_tile_store_t(stage, sBuf, tid);   // S_c^T [col][dk]
-    frag_tile_fetch(stage, p.vn + ch * TILE, tid);
+    cfrag_tile_store_t(stS, sBuf, tid);   // S_c^T [col][dk]
     __syncthreads();
 
     f32x4 o[8];
@@ -904,7 +908,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         o[ct] = acc;
     }
     __syncthreads();
-    cfrag_tile_store_t(stage, sBuf, tid);   // v_new^T [col][tok]
+    cfrag_tile_store_t(stV, sBuf, tid);   // v_new^T [col][tok]
     __syncthreads();
     for (int ks = 0; ks <= I / 2; ++ks) {
         const half8 a = ld_h8(&sP[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
