@@ -55,7 +55,7 @@ def _load():
         lib.gdr_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, ip, i, i, i, i, i, i,
                                            ctypes.c_double, dp, dp]
         lib.gdr_oracle_prefill.restype = i
-        lib.gdr_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, ip, ip,
+        lib.gdr_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, ip, ip, ip,
                                           i, i, i, i, i, i, ctypes.c_double, i, dp]
         lib.gdr_oracle_decode.restype = i
         lib.gdr_oracle_round_bf16.argtypes = [ctypes.c_double]
@@ -89,6 +89,8 @@ def _dp(a):
 
 
 def _ip(a):
+    if a is None:
+        return ctypes.POINTER(ctypes.c_int32)()
     return a.ctypes.data_as(ctypes.POINTER(ctypes.c_int32))
 
 
@@ -129,11 +131,12 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale):
     return out, state_out
 
 
-def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False):
+def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False, num_accepted=None):
     """Recurrent decode over a slot pool.
 
     q, k [B,Nk,S,Dk] (caller-normalised); v [B,Nv,S,Dv]; g, beta [B,Nv,S];
-    gk [B,Nv,S,Dk] or None; pool [slots,Nv,Dk,Dv]; idx [B*S]; lens [B].
+    gk [B,Nv,S,Dk] or None; pool [slots,Nv,Dk,Dv]; idx [B*S]; lens [B];
+    num_accepted [B] or None (row b starts from slot idx[b*S + n_b - 1]).
     Returns (out [B,Nv,S,Dv], pool_out [slots,Nv,Dk,Dv]) in float64; pool_out
     equals the input pool except for the slots the call writes.
     """
@@ -145,10 +148,12 @@ def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False)
     Nv, Dv = v.shape[1], v.shape[3]
     slots = pool.shape[0]
     assert pool.shape == (slots, Nv, Dk, Dv) and idx.shape[0] == B * S and lens.shape[0] == B
+    nacc = None if num_accepted is None else _i32(num_accepted).reshape(-1)
+    assert nacc is None or nacc.shape[0] == B
     out = np.zeros((B, Nv, S, Dv), np.float64)
     pool_out = pool.copy()
     rc = _load().gdr_oracle_decode(_dp(q), _dp(k), _dp(v), _dp(g), _dp(gk), _dp(beta),
-                                   _dp(pool), _dp(pool_out), slots, _ip(idx), _ip(lens),
+                                   _dp(pool), _dp(pool_out), slots, _ip(idx), _ip(lens), _ip(nacc),
                                    B, S, Nk, Nv, Dk, Dv, float(scale),
                                    1 if round_state_bf16 else 0, _dp(out))
     if rc != 0:

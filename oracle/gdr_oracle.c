@@ -155,22 +155,32 @@ int gdr_oracle_prefill(const double *q, const double *k, const double *v,
  *                                  receives the state after each token
  *   idx       [B*S]   slot per flattened token
  *   lens      [B]     valid tokens per row, 0..S
+ *   num_accepted [B] or NULL: accepted-token count per row ("num_accepted_tokens"
+ *               in the "lite_boost.ops.recurrent_gated_delta_rule" page's
+ *               parameter list: the tokens accepted, not rejected, in
+ *               speculative decoding; equal to the valid length in ordinary
+ *               inference).  NULL means 1 for every row.
  *   round_bf16: if nonzero, what is stored into pool_out is the bf16 rounding
  *               of the exact state (what a bf16 pool holds); the token chain
  *               itself stays exact.
  *   out       [B][Nv][S][Dv]
  *
  * Routing (the pages give one index per flattened token and say ordinary
- * inference uses one slot per row): the chain of row b starts from slot
- * idx[b*S + 0]; the state after token t is stored into slot idx[b*S + t];
- * tokens t >= lens[b] are neither read nor written and their out rows are 0.
+ * inference uses one slot per row): with n = num_accepted[b] clamped to
+ * 1..S, the chain of row b starts from slot idx[b*S + n - 1] -- the slot that
+ * holds the state after the last accepted token of the previous call, whose
+ * per-token states went to the same index positions; in ordinary inference
+ * all of a row's indices name one slot, so n does not matter.  An initial
+ * slot outside 0..slots-1 starts the chain from a zero state.  The state
+ * after token t is stored into slot idx[b*S + t]; tokens t >= lens[b] are
+ * neither read nor written and their out rows are 0.
  * Returns 0, -1 on invalid sizes / an index out of range, -2 on allocation
  * failure.
  */
 int gdr_oracle_decode(const double *q, const double *k, const double *v,
                       const double *g, const double *gk, const double *beta,
                       const double *pool_in, double *pool_out, int num_slots,
-                      const int32_t *idx, const int32_t *lens,
+                      const int32_t *idx, const int32_t *lens, const int32_t *num_accepted,
                       int B, int S, int Nk, int Nv, int Dk, int Dv,
                       double scale, int round_bf16, double *out)
 {
@@ -193,8 +203,13 @@ int gdr_oracle_decode(const double *q, const double *k, const double *v,
         for (int t = 0; t < S; ++t)
             memset(out + (((size_t)b * Nv + h) * S + t) * Dv, 0, sizeof(double) * (size_t)Dv);
         if (lens[b] > 0) {
-            const int s0 = idx[b * S + 0];
-            memcpy(Sm, pool_in + ((size_t)s0 * Nv + h) * slab, sizeof(double) * slab);
+            int n = num_accepted ? num_accepted[b] : 1;
+            n = n < 1 ? 1 : (n > S ? S : n);
+            const int s0 = idx[b * S + n - 1];
+            if (s0 >= 0 && s0 < num_slots)
+                memcpy(Sm, pool_in + ((size_t)s0 * Nv + h) * slab, sizeof(double) * slab);
+            else
+                memset(Sm, 0, sizeof(double) * slab);
             for (int t = 0; t < lens[b]; ++t) {
                 const size_t tq = (((size_t)b * Nk + hk) * S + t) * Dk;
                 const size_t tv = ((size_t)b * Nv + h) * S + t;

@@ -285,6 +285,82 @@ def test_multi_token_decode_equals_chained_single_tokens():
     assert not np.array_equal(pool_out[5], pool[5]) and not np.array_equal(pool_out[2], pool[2])
 
 
+def _spec_case(seed, B=3, S=4, Nk=1, Nv=2, Dk=4, Dv=3):
+    rng = np.random.default_rng(seed)
+    def toks():
+        q = rng.standard_normal((B, Nk, S, Dk))
+        k = rng.standard_normal((B, Nk, S, Dk))
+        k /= np.linalg.norm(k, axis=-1, keepdims=True)
+        return (q, k, rng.standard_normal((B, Nv, S, Dv)), -rng.uniform(0.01, 1, (B, Nv, S)),
+                -rng.uniform(0.01, 1, (B, Nv, S, Dk)), rng.uniform(0.05, 0.95, (B, Nv, S)))
+    return rng, toks(), toks()
+
+
+def test_speculative_continuation_starts_after_the_accepted_prefix():
+    """num_accepted_tokens (decode page, parameters): a call that drafted S
+    tokens stores the state after each token t in slot idx[b*S+t]; the next
+    call, told that n_b tokens were accepted, must continue from the state
+    after exactly n_b tokens of the first chain -- the same result as feeding
+    only the accepted tokens through one slot and then the new ones."""
+    B, S, Nv, Dk, Dv = 3, 4, 2, 4, 3
+    rng, r1, r2 = _spec_case(40, B, S, 1, Nv, Dk, Dv)
+    slots = B * S + B
+    pool = rng.standard_normal((slots, Nv, Dk, Dv))
+    # row b starts from its own slot b, which also receives the state after
+    # its token 0; each later drafted token has a slot of its own
+    idx = (np.arange(B * S, dtype=np.int32) + B).reshape(B, S)
+    start = np.arange(B, dtype=np.int32)
+    idx[:, 0] = start
+    idx = idx.reshape(-1)
+    lens = np.full(B, S, np.int32)
+    _, pool1 = oracle.decode(*r1[:4], r1[4], r1[5], pool, idx, lens, 0.7)
+    nacc = np.array([1, 3, 4], np.int32)
+    out2, _ = oracle.decode(*r2[:4], r2[4], r2[5], pool1, idx, lens, 0.7, num_accepted=nacc)
+    for b in range(B):
+        for h in range(Nv):
+            n = int(nacc[b])
+            cat = lambda a, c: np.concatenate([a[b, 0 if a.shape[1] == 1 else h, :n], c[b, 0 if c.shape[1] == 1 else h]])
+            q = cat(r1[0], r2[0]); k = cat(r1[1], r2[1]); v = cat(r1[2], r2[2])
+            g = cat(r1[3], r2[3]); gk = cat(r1[4], r2[4]); beta = cat(r1[5], r2[5])
+            o_ref, _ = _decode_one(q, k, v, g, beta, pool[start[b], h], scale=0.7, gk=gk)
+            np.testing.assert_allclose(out2[b, h], o_ref[n:], rtol=1e-12, atol=1e-13)
+
+
+def test_num_accepted_equal_to_length_is_ordinary_inference():
+    """With every index of a row naming one slot (ordinary inference),
+    num_accepted_tokens = actual_seq_lengths changes nothing."""
+    B, S = 3, 4
+    rng, r, _ = _spec_case(41, B, S)
+    pool = rng.standard_normal((5, 2, 4, 3))
+    idx = np.repeat(np.array([3, 0, 4], np.int32), S)
+    lens = np.array([4, 2, 3], np.int32)
+    a = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 0.9)
+    b = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 0.9, num_accepted=lens)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+
+
+def test_num_accepted_clamps_and_empty_initial_slot_is_zero():
+    """n is clamped to 1..S; an initial index outside the pool (a padded
+    position) starts the chain from a zero state."""
+    B, S = 2, 4
+    rng, r, _ = _spec_case(42, B, S)
+    pool = rng.standard_normal((6, 2, 4, 3))
+    idx = np.array([1, 2, -1, -1, 3, 4, 5, 0], np.int32)
+    lens = np.array([2, 4], np.int32)
+    o_hi, _ = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 1.0, num_accepted=np.array([9, 9], np.int32))
+    o_s, _ = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 1.0, num_accepted=np.array([4, 4], np.int32))
+    assert np.array_equal(o_hi, o_s)
+    o_lo, _ = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 1.0, num_accepted=np.array([0, -3], np.int32))
+    o_1, _ = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 1.0)
+    assert np.array_equal(o_lo, o_1)
+    # row 0 with n = 4 reads idx[3] = -1: same as a chain from a zero slot
+    zpool = pool.copy()
+    zpool[1] = 0.0
+    o_z, _ = oracle.decode(*r[:4], r[4], r[5], zpool, idx, lens, 1.0)
+    np.testing.assert_array_equal(o_s[0], o_z[0])
+
+
 def test_decode_equals_prefill_on_unit_inputs():
     """Cross-path: decode token by token == prefill of the same sequence when
     q, k are already unit (prefill then only adds the eps of its norm)."""
