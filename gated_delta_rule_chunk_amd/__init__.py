@@ -46,7 +46,7 @@ SIGNATURES = {
     "gdr_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                          _i32, ctypes.c_float, ctypes.c_int, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
-    "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _i32,
+    "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                             ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "gdr_timing_enable": (ctypes.c_int, [ctypes.c_int]),
@@ -191,14 +191,16 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
 
 
 def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths,
-                     scale=1.0, out=None):
+                     scale=1.0, out=None, num_accepted_tokens=None):
     """Recurrent Gated Delta Rule decode over a slot pool
     ("lite_boost.ops.recurrent_gated_delta_rule" page).
 
     q, k [B,Nk,S,Dk]; v [B,Nv,S,Dv]; beta [B,Nv,S] (act dtype); g [B,Nv,S]
     fp32; gk [B,Nv,S,Dk] fp32 or None; state_pool [slots,Nv,Dk,Dv] (bf16 or
     fp32, updated in place); ssm_state_indices [B*S] int32;
-    actual_seq_lengths [B] int32.  Returns (out [B,Nv,S,Dv], state_pool).
+    actual_seq_lengths [B] int32; num_accepted_tokens [B] int32 or None
+    (speculative decoding: row b resumes from slot
+    ssm_state_indices[b*S + n_b - 1]).  Returns (out [B,Nv,S,Dv], state_pool).
     """
     if q.dim() != 4 or k.shape != q.shape:
         raise ValueError(f"q and k must be [B,Nk,S,Dk] (got {tuple(q.shape)}, {tuple(k.shape)})")
@@ -217,6 +219,8 @@ def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual
                          f"(got {ssm_state_indices.numel()})")
     if actual_seq_lengths.numel() != B:
         raise ValueError(f"actual_seq_lengths must hold B = {B} entries")
+    if num_accepted_tokens is not None and num_accepted_tokens.numel() != B:
+        raise ValueError(f"num_accepted_tokens must hold B = {B} entries")
     act = _act(q, "q")
     for name, t in (("k", k), ("v", v), ("beta", beta)):
         if t.dtype != q.dtype:
@@ -224,19 +228,22 @@ def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual
     st = _act(state_pool, "state_pool")
     if g.dtype != torch.float32 or (gk is not None and gk.dtype != torch.float32):
         raise RuntimeError("g and gk must be float32")
-    if ssm_state_indices.dtype != torch.int32 or actual_seq_lengths.dtype != torch.int32:
-        raise RuntimeError("ssm_state_indices and actual_seq_lengths must be int32")
+    if ssm_state_indices.dtype != torch.int32 or actual_seq_lengths.dtype != torch.int32 or (
+            num_accepted_tokens is not None and num_accepted_tokens.dtype != torch.int32):
+        raise RuntimeError("ssm_state_indices, actual_seq_lengths and num_accepted_tokens must be int32")
     device = q.device
     if out is None:
         out = torch.empty((B, Nv, S, Dv), dtype=q.dtype, device=device)
     if out.shape != (B, Nv, S, Dv) or out.dtype != q.dtype:
         raise ValueError("out must be [B,Nv,S,Dv] of q's dtype")
     _dev(dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, state_pool=state_pool,
-              ssm_state_indices=ssm_state_indices, actual_seq_lengths=actual_seq_lengths, out=out),
+              ssm_state_indices=ssm_state_indices, actual_seq_lengths=actual_seq_lengths,
+              num_accepted_tokens=num_accepted_tokens, out=out),
          device)
     check(lib().gdr_recurrent_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
                                      _ptr(state_pool), state_pool.shape[0], _ptr(ssm_state_indices),
-                                     _ptr(actual_seq_lengths), B, S, Nk, Nv, Dk, Dv, float(scale),
+                                     _ptr(actual_seq_lengths), _ptr(num_accepted_tokens), B, S, Nk, Nv,
+                                     Dk, Dv, float(scale),
                                      act, st, _ptr(out), _stream(device)),
           "gdr_recurrent_decode")
     return out, state_pool

@@ -123,7 +123,7 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
 gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, const float* g,
                                 const float* gk, const void* beta, void* state_pool, int32_t num_slots,
                                 const int32_t* ssm_state_indices, const int32_t* actual_seq_lengths,
-                                int32_t B, int32_t S, int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv,
+                                const int32_t* num_accepted_tokens, int32_t B, int32_t S, int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv,
                                 float scale, gdr_dtype act, gdr_dtype state_dtype, void* out,
                                 void* hip_stream) {
     if (B < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "B must be >= 1 (got %d)", B);
@@ -142,11 +142,11 @@ gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, con
         return fail(GDR_ERR_DTYPE, "dtypes must be GDR_BF16 or GDR_FP32 (act=%d, state=%d)", (int)act,
                     (int)state_dtype);
     if (!q || !k || !v || !g || !beta || !state_pool || !ssm_state_indices || !actual_seq_lengths || !out)
-        return fail(GDR_ERR_INVALID_ARGUMENT, "only gk may be NULL");
+        return fail(GDR_ERR_INVALID_ARGUMENT, "only gk and num_accepted_tokens may be NULL");
     if ((int64_t)B * Nv * (Dv / (Dv == 64 ? 64 : 128)) > 0x7fffffffLL)
         return fail(GDR_ERR_INVALID_ARGUMENT, "B * Nv too large");
-    gdr::DecodeArgs a{q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths, out,
-                      num_slots, B, S, Nk, Nv, Dk, Dv, scale};
+    gdr::DecodeArgs a{q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths,
+                      num_accepted_tokens, out, num_slots, B, S, Nk, Nv, Dk, Dv, scale};
     return from_hip(gdr::decode_launch(a, act == GDR_BF16, state_dtype == GDR_BF16,
                                        static_cast<hipStream_t>(hip_stream)),
                     "decode launch");

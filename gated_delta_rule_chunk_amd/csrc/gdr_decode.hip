@@ -72,7 +72,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     // state slab (rows rg + RP*m, columns col..col+7) -> fp32 registers
     float st[RPT][8];
-    const int slot0 = len > 0 ? idx[0] : -1;
+    // the chain resumes from the state after the last accepted token of the
+    // previous call (index position n - 1; n = 1 in ordinary inference)
+    int nacc = a.nacc ? a.nacc[b] : 1;
+    nacc = nacc < 1 ? 1 : (nacc > S ? S : nacc);
+    const int slot0 = len > 0 ? idx[nacc - 1] : -1;
     if (slot0 >= 0 && slot0 < a.num_slots) {
         const StT* base = pool + (size_t)slot0 * slot_stride + (size_t)h * slab + col;
 #pragma unroll

@@ -28,6 +28,7 @@ struct DecodeArgs {
     void* pool;
     const int32_t* idx;
     const int32_t* lens;
+    const int32_t* nacc;   // accepted tokens per row, or null (= 1)
     void* out;
     int32_t num_slots, B, S, Nk, Nv, Dk, Dv;
     float scale;

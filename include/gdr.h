@@ -121,8 +121,9 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
  * ("lite_boost.ops.recurrent_gated_delta_rule" page).
  *
  * For batch row b, value head h (key head h / (Nv/Nk)), the token chain
- * starts from the slot state_pool[ssm_state_indices[b*S + 0], h]; for each
- * valid token t < actual_seq_lengths[b]:
+ * starts from the slot state_pool[ssm_state_indices[b*S + n - 1], h], where
+ * n is num_accepted_tokens[b] clamped to [1, S] (n = 1 if the pointer is
+ * NULL); for each valid token t < actual_seq_lengths[b]:
  *   S = S * exp(g) * exp(gk)     (gk per key row; omitted if gk is NULL)
  *   S = S + k ((v - S^T k) beta)^T
  *   out[b,h,t] = S^T (q * scale)
@@ -133,6 +134,14 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
  * pool, and their out rows are written as zeros.  Slots no token writes keep
  * their bits.  Rows must not write slots that other rows read or write.
  *
+ * num_accepted_tokens is the page's count of accepted (not rejected) tokens
+ * in speculative decoding, equal to actual_seq_lengths in ordinary
+ * inference: a call that drafted S tokens leaves the state after each draft
+ * token t in slot ssm_state_indices[b*S + t], and the next call, given the
+ * same index positions and n accepted tokens, resumes from the state after
+ * the n-th.  In ordinary inference a row's indices all name one slot and n
+ * does not matter.
+ *
  *   q, k                [B, Nk, S, Dk]  act dtype, caller-normalised (unit L2 norm)
  *   v                   [B, Nv, S, Dv]  act dtype
  *   g                   [B, Nv, S]      fp32 (expected < 0)
@@ -141,6 +150,7 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
  *   state_pool          [num_slots, Nv, Dk, Dv]  state dtype, updated in place
  *   ssm_state_indices   [B * S]         int32, device
  *   actual_seq_lengths  [B]             int32, device, each in [0, S]
+ *   num_accepted_tokens [B]             int32, device, or NULL
  *   B >= 1; 1 <= S <= 8 (decode only, as the page limits it);
  *   Nv a multiple of Nk; Dk in {64, 128}; Dv in {64, 128, 256, 512}
  *   scale               multiplies q before use (the page's scale_value)
@@ -155,7 +165,8 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
 gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, const float *g,
                                 const float *gk, const void *beta, void *state_pool,
                                 int32_t num_slots, const int32_t *ssm_state_indices,
-                                const int32_t *actual_seq_lengths, int32_t B, int32_t S,
+                                const int32_t *actual_seq_lengths,
+                                const int32_t *num_accepted_tokens, int32_t B, int32_t S,
                                 int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv, float scale,
                                 gdr_dtype act, gdr_dtype state_dtype, void *out,
                                 void *hip_stream);

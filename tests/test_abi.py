@@ -86,11 +86,12 @@ def test_prefill_host_validation():
 
 def decode_call(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, beta=FAKE, pool=FAKE, slots=8, idx=FAKE,
-             lens=FAKE, B=2, S=1, Nk=2, Nv=4, Dk=128, Dv=128, scale=0.1, act=gdr.GDR_BF16,
+             lens=FAKE, nacc=None, B=2, S=1, Nk=2, Nv=4, Dk=128, Dv=128, scale=0.1, act=gdr.GDR_BF16,
              st=gdr.GDR_BF16, out=FAKE, stream=None)
     a.update(over)
     return gdr.lib().gdr_recurrent_decode(a["q"], a["k"], a["v"], a["g"], a["gk"], a["beta"], a["pool"],
-                                          a["slots"], a["idx"], a["lens"], a["B"], a["S"], a["Nk"], a["Nv"],
+                                          a["slots"], a["idx"], a["lens"], a["nacc"], a["B"], a["S"], a["Nk"],
+                                          a["Nv"],
                                           a["Dk"], a["Dv"], a["scale"], a["act"], a["st"], a["out"],
                                           a["stream"])
 

@@ -16,15 +16,17 @@ def run_gpu(inp, pool=None):
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     pool_dev = (inp["pool"] if pool is None else pool).clone().to(DEV)
     out, _ = gdr.recurrent_decode(d["q"], d["k"], d["v"], d["g"], d["gk"], d["beta"], pool_dev,
-                                  d["idx"], d["lens"], d["scale"])
+                                  d["idx"], d["lens"], d["scale"], num_accepted_tokens=d.get("nacc"))
     torch.cuda.synchronize()
     return out.cpu(), pool_dev.cpu()
 
 
-def run_oracle(inp):
-    bf16_pool = inp["pool"].dtype == torch.bfloat16
-    return oracle.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["gk"], inp["beta"], inp["pool"],
-                         inp["idx"], inp["lens"], inp["scale"], round_state_bf16=bf16_pool)
+def run_oracle(inp, pool=None):
+    pool = inp["pool"] if pool is None else pool
+    bf16_pool = pool.dtype == torch.bfloat16
+    return oracle.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["gk"], inp["beta"], pool,
+                         inp["idx"], inp["lens"], inp["scale"], round_state_bf16=bf16_pool,
+                         num_accepted=inp.get("nacc"))
 
 
 def written_slots(inp):
@@ -135,3 +137,30 @@ def test_decode_is_deterministic():
     o2, p2 = run_gpu(inp)
     assert torch.equal(o1.view(torch.int16), o2.view(torch.int16))
     assert torch.equal(p1.view(torch.int16), p2.view(torch.int16))
+
+
+@pytest.mark.parametrize("Dk,Dv,with_gk", [(128, 128, False), (64, 512, True)])
+def test_decode_speculative_rounds_resume_after_accepted_tokens(Dk, Dv, with_gk):
+    """Speculative decoding: call 1 drafts S = 4 tokens per row, leaving the
+    state after each in a slot of its own; call 2 (same index positions,
+    num_accepted_tokens ~ U{1..4}) resumes each row from the state after its
+    last accepted draft.  Both calls run on the GPU and in the oracle."""
+    B, S, slots = 24, 4, 100
+    r1 = workloads.decode_inputs(70 + Dv, B=B, S=S, Nk=2, Nv=4, Dk=Dk, Dv=Dv, num_slots=slots,
+                                 with_gk=with_gk, routing="per_token")
+    r2 = workloads.decode_inputs(71 + Dv, B=B, S=S, Nk=2, Nv=4, Dk=Dk, Dv=Dv, num_slots=slots,
+                                 with_gk=with_gk, lens="random", routing="per_token", accepted=True)
+    r2["idx"] = r1["idx"].clone()
+    print(f"[decode parity] speculative rounds Dk={Dk} Dv={Dv} nacc={r2['nacc'].tolist()[:8]}...", flush=True)
+    _, pool1 = run_gpu(r1)
+    out2, pool2 = run_gpu(r2, pool=pool1)
+    _, pool1_ref = run_oracle(r1)
+    out2_ref, pool2_ref = run_oracle(r2, pool=torch.from_numpy(pool1_ref).to(torch.bfloat16))
+    lens = r2["lens"].numpy()
+    valid = np.zeros(out2.shape, bool)
+    for b in range(B):
+        valid[b, :, :lens[b]] = True
+    exc, lit = assert_out_close(to_f64(out2)[valid], out2_ref[valid], True, "speculative out")
+    ws = written_slots(r2)
+    es = assert_state_close(to_f64(pool2)[ws], pool2_ref[ws], "speculative state")
+    print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)

@@ -84,7 +84,8 @@ def _unit_rows(rng, shape):
 
 def decode_inputs(seed: int, B: int, S: int, Nk: int, Nv: int, Dk: int, Dv: int, num_slots: int,
                   with_gk: bool = False, lens: str = "full", routing: str = "one_slot",
-                  act: str = "bf16", state: str = "bf16", scale: float | None = None):
+                  act: str = "bf16", state: str = "bf16", scale: float | None = None,
+                  accepted: bool = False):
     """Recurrent-decode inputs over a slot pool.
 
     lens:    "full" (every row has S valid tokens) or "random" (U{1..S}).
@@ -92,8 +93,13 @@ def decode_inputs(seed: int, B: int, S: int, Nk: int, Nv: int, Dk: int, Dv: int,
                             B entries of a seeded permutation of the slots;
              "two_slots" -- row b owns slots {pi[2b], pi[2b+1]} of a seeded
                             permutation and each valid token picks one of the
-                            two at random (collision-free across rows).
-    Padded token positions (t >= len_b) get index -1 and zero-valued inputs.
+                            two at random (collision-free across rows);
+             "per_token" -- speculative decoding: row b owns S slots
+                            pi[S b .. S b + S - 1], one per token position,
+                            padded positions included.
+    accepted: also draw num_accepted_tokens nacc [B] ~ U{1..S}.
+    Padded token positions (t >= len_b) get zero-valued inputs and, except
+    under per_token routing, index -1.
     Returns a dict of CPU tensors: q, k [B,Nk,S,Dk]; v [B,Nv,S,Dv];
     beta [B,Nv,S]; g [B,Nv,S] fp32; gk [B,Nv,S,Dk] fp32 or None;
     pool [slots,Nv,Dk,Dv]; idx [B*S] int32; lens [B] int32; scale.
@@ -125,8 +131,13 @@ def decode_inputs(seed: int, B: int, S: int, Nk: int, Nv: int, Dk: int, Dv: int,
         pick = rng.integers(0, 2, (B, S))
         for b in range(B):
             idx[b, :ln[b]] = perm[2 * b + pick[b, :ln[b]]]
+    elif routing == "per_token":
+        if num_slots < S * B:
+            raise ValueError("per_token routing needs num_slots >= S*B")
+        idx[:] = perm[:S * B].reshape(B, S)
     else:
         raise ValueError(routing)
+    nacc = rng.integers(1, S + 1, B).astype(np.int32) if accepted else None
     # padded tokens carry zero-valued inputs (they are never read)
     for b in range(B):
         if ln[b] < S:
@@ -139,6 +150,7 @@ def decode_inputs(seed: int, B: int, S: int, Nk: int, Nv: int, Dk: int, Dv: int,
                 gk[b, :, ln[b]:] = 0
     return dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, pool=pool,
                 idx=torch.from_numpy(idx.reshape(-1).copy()), lens=torch.from_numpy(ln),
+                nacc=None if nacc is None else torch.from_numpy(nacc),
                 scale=SCALE_128 if scale is None else scale,
                 B=B, S=S, Nk=Nk, Nv=Nv, Dk=Dk, Dv=Dv, num_slots=num_slots, act=act, state=state)
 
