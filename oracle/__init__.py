@@ -53,10 +53,10 @@ def _load():
         ip = ctypes.POINTER(ctypes.c_int32)
         i = ctypes.c_int
         lib.gdr_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, ip, i, i, i, i, i, i,
-                                           ctypes.c_double, dp, dp]
+                                           ctypes.c_double, i, dp, dp]
         lib.gdr_oracle_prefill.restype = i
         lib.gdr_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, ip, ip, ip,
-                                          i, i, i, i, i, i, ctypes.c_double, i, dp]
+                                          i, i, i, i, i, i, ctypes.c_double, i, i, dp]
         lib.gdr_oracle_decode.restype = i
         lib.gdr_oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.gdr_oracle_round_bf16.restype = ctypes.c_double
@@ -105,12 +105,15 @@ def round_bf16(x):
     return np.vectorize(f, otypes=[np.float64])(x) if x.size else x.copy()
 
 
-def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale):
+RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
+
+
+def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, rule="gated_delta"):
     """Chunked-prefill semantics by the per-token recurrence.
 
     q, k [T,Nqk,Dk]; v [T,Nv,Dv]; g, beta [T,Nv]; state_in [B,Nv,Dk,Dv] or
-    None (zeros); cu_seqlens [B+1].  Returns (out [T,Nv,Dv], state_out
-    [B,Nv,Dk,Dv]) in float64.
+    None (zeros); cu_seqlens [B+1]; rule one of RULES.  Returns (out
+    [T,Nv,Dv], state_out [B,Nv,Dk,Dv]) in float64.
     """
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
     state_in = _f64(state_in)
@@ -124,14 +127,15 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale):
     out = np.zeros((T, Nv, Dv), np.float64)
     state_out = np.zeros((B, Nv, Dk, Dv), np.float64)
     rc = _load().gdr_oracle_prefill(_dp(q), _dp(k), _dp(v), _dp(g), _dp(beta), _dp(state_in),
-                                    _ip(cu), T, B, Nqk, Nv, Dk, Dv, float(scale),
+                                    _ip(cu), T, B, Nqk, Nv, Dk, Dv, float(scale), RULES[rule],
                                     _dp(out), _dp(state_out))
     if rc != 0:
         raise ValueError(f"oracle prefill rejected its arguments (rc={rc})")
     return out, state_out
 
 
-def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False, num_accepted=None):
+def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False, num_accepted=None,
+           rule="gated_delta"):
     """Recurrent decode over a slot pool.
 
     q, k [B,Nk,S,Dk] (caller-normalised); v [B,Nv,S,Dv]; g, beta [B,Nv,S];
@@ -155,7 +159,7 @@ def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False,
     rc = _load().gdr_oracle_decode(_dp(q), _dp(k), _dp(v), _dp(g), _dp(gk), _dp(beta),
                                    _dp(pool), _dp(pool_out), slots, _ip(idx), _ip(lens), _ip(nacc),
                                    B, S, Nk, Nv, Dk, Dv, float(scale),
-                                   1 if round_state_bf16 else 0, _dp(out))
+                                   1 if round_state_bf16 else 0, RULES[rule], _dp(out))
     if rc != 0:
         raise ValueError(f"oracle decode rejected its arguments (rc={rc})")
     return out, pool_out

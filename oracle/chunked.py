@@ -42,6 +42,11 @@ show the alternatives disagree):
     the boundary layout used everywhere else is S [Dk, Dv] = the page's S^T.
     This module takes and returns [Dk, Dv] and transposes internally.
   * A ragged last chunk is processed with its r < L valid rows only.
+
+Update rules ("LinearAttention" page, attribute update_rule): the rules
+without a gate (delta, linear) take g = 0; the rules without the delta term
+(gated, linear) have no pre-attention matrix, so its inverse is I, v_out = v
+and k_cumdecay = 0 (v_new = v).
 """
 from __future__ import annotations
 
@@ -79,7 +84,7 @@ def inverse_rows(A):
 
 
 def chunk_step(q, k, v, g, beta, S_dkdv, inverse=inverse_rows,
-               mask_sign=-1.0, strict_out_tril=False, raw_g_last=False, raw_g_in_kgexp=False):
+               mask_sign=-1.0, strict_out_tril=False, raw_g_last=False, raw_g_in_kgexp=False, delta=True):
     """One chunk of r rows (already L2-normalised q, k; q already scaled).
 
     q, k [r, Dk]; v [r, Dv]; g, beta [r]; S_dkdv [Dk, Dv].
@@ -94,9 +99,13 @@ def chunk_step(q, k, v, g, beta, S_dkdv, inverse=inverse_rows,
     k_beta = k * beta[:, None]                               # Pre-Attention Matrix
     M_mask = mask_sign * np.tril(np.ones((r, r)), -1)
     A = (k_beta @ k.T) * D * M_mask
-    Ainv = inverse(A)                                        # Matrix Inversion
-    v_out = Ainv @ (v * beta[:, None])                       # Value and Key Cumulative Decay
-    k_cumdecay = Ainv @ (k_beta * np.exp(g_cum)[:, None])
+    if delta:
+        Ainv = inverse(A)                                    # Matrix Inversion
+        v_out = Ainv @ (v * beta[:, None])                   # Value and Key Cumulative Decay
+        k_cumdecay = Ainv @ (k_beta * np.exp(g_cum)[:, None])
+    else:                                                    # no delta term: v_new = v
+        v_out = v
+        k_cumdecay = np.zeros_like(k)
     S = S_dkdv.T                                             # the page's S is [Dv, Dk]
     v_prime = k_cumdecay @ S.T                               # Recurrent State Attention
     o_inter = (q * np.exp(g_cum)[:, None]) @ S.T
@@ -110,7 +119,7 @@ def chunk_step(q, k, v, g, beta, S_dkdv, inverse=inverse_rows,
     return o, S_new.T
 
 
-def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, **readings):
+def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, rule="gated_delta", **readings):
     """Chunked prefill over packed varlen sequences, fp64.
 
     q, k [T,Nqk,Dk]; v [T,Nv,Dv]; g, beta [T,Nv]; state_in [B,Nv,Dk,Dv] or
@@ -120,8 +129,11 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, **readings):
     k = np.asarray(k, np.float64)
     v = np.asarray(v, np.float64)
     g = np.asarray(g, np.float64)
+    if rule in ("delta", "linear"):
+        g = np.zeros_like(g)
     beta = np.asarray(beta, np.float64)
     cu = np.asarray(cu_seqlens, np.int64)
+    readings = dict(readings, delta=rule in ("gated_delta", "delta"))
     T, Nqk, Dk = q.shape
     Nv, Dv = v.shape[1], v.shape[2]
     B = len(cu) - 1

@@ -27,6 +27,17 @@
  * `scale` (the decode page states that q is multiplied by the scale before
  * computation; the same convention is used for prefill).
  *
+ * Update rules ("LinearAttention" contrib-operator page, attribute
+ * update_rule: linear, gated, delta, gated_delta; the page names them
+ * without formulas).  The plain readings, each dropping parts of the
+ * recurrence above:
+ *   rule 0  gated_delta   the recurrence above (default)
+ *   rule 1  delta         no decay: g and gk are ignored (exp(.) = 1)
+ *   rule 2  gated         no delta term: S <- S * exp(g) * exp(gk) + k v^T
+ *                         (beta and kv_mem are not used)
+ *   rule 3  linear        neither: S <- S + k v^T
+ * The codes are part of the C ABI of the GPU library as well.
+ *
  * Value head h reads query/key head h / (Nv / Nqk) (contiguous GQA groups).
  * The pages only require Nv to be a multiple of Nqk; the contiguous grouping
  * is a convention both sides of the parity tests fix.
@@ -61,28 +72,37 @@ double gdr_oracle_round_bf16(double x)
 }
 
 /* One token of the recurrence on an fp64 state S [Dk][Dv] (row-major).
- *   decay_row[i] = exp(g) * exp(gk[i]) (precomputed by the caller)
+ *   decay_row[i] = exp(g) * exp(gk[i]) (precomputed by the caller; 1 for
+ *   rules without a gate)
+ *   delta: nonzero for the delta rules; otherwise S += k v^T (beta unused)
  *   q_scaled = q * scale
  * Writes o [Dv].  kv is caller scratch of length Dv. */
 static void token_step(double *S, int Dk, int Dv,
                        const double *decay_row,
-                       const double *k, const double *v, double beta,
+                       const double *k, const double *v, double beta, int delta,
                        const double *q_scaled, double *o, double *kv)
 {
     /* state decay: row i scaled by exp(g) * exp(gk_i) */
     for (int i = 0; i < Dk; ++i)
         for (int j = 0; j < Dv; ++j)
             S[(size_t)i * Dv + j] *= decay_row[i];
-    /* memory retrieval: kv_mem = S^T k */
-    for (int j = 0; j < Dv; ++j) {
-        double acc = 0.0;
-        for (int i = 0; i < Dk; ++i) acc += S[(size_t)i * Dv + j] * k[i];
-        kv[j] = acc;
+    if (delta) {
+        /* memory retrieval: kv_mem = S^T k */
+        for (int j = 0; j < Dv; ++j) {
+            double acc = 0.0;
+            for (int i = 0; i < Dk; ++i) acc += S[(size_t)i * Dv + j] * k[i];
+            kv[j] = acc;
+        }
+        /* delta update: S += k ((v - kv_mem) * beta)^T */
+        for (int i = 0; i < Dk; ++i)
+            for (int j = 0; j < Dv; ++j)
+                S[(size_t)i * Dv + j] += k[i] * ((v[j] - kv[j]) * beta);
+    } else {
+        /* additive update: S += k v^T */
+        for (int i = 0; i < Dk; ++i)
+            for (int j = 0; j < Dv; ++j)
+                S[(size_t)i * Dv + j] += k[i] * v[j];
     }
-    /* delta update: S += k ((v - kv_mem) * beta)^T */
-    for (int i = 0; i < Dk; ++i)
-        for (int j = 0; j < Dv; ++j)
-            S[(size_t)i * Dv + j] += k[i] * ((v[j] - kv[j]) * beta);
     /* output: o = S^T (q * scale) */
     for (int j = 0; j < Dv; ++j) {
         double acc = 0.0;
@@ -109,16 +129,18 @@ static void l2norm(const double *x, int n, double mul, double *y)
  *   cu_seqlens[B+1], cu[0] = 0, non-decreasing, cu[B] = T
  *   out       [T][Nv][Dv]
  *   state_out [B][Nv][Dk][Dv]
+ *   rule      update rule 0..3 (see above)
  * Returns 0 on success, -1 on invalid sizes, -2 on allocation failure.
  */
 int gdr_oracle_prefill(const double *q, const double *k, const double *v,
                        const double *g, const double *beta,
                        const double *state_in, const int32_t *cu_seqlens,
                        int T, int B, int Nqk, int Nv, int Dk, int Dv,
-                       double scale, double *out, double *state_out)
+                       double scale, int rule, double *out, double *state_out)
 {
-    if (T < 0 || B < 1 || Nqk < 1 || Nv < 1 || Dk < 1 || Dv < 1 || Nv % Nqk)
+    if (T < 0 || B < 1 || Nqk < 1 || Nv < 1 || Dk < 1 || Dv < 1 || Nv % Nqk || rule < 0 || rule > 3)
         return -1;
+    const int gated = rule == 0 || rule == 2, delta = rule == 0 || rule == 1;
     const int G = Nv / Nqk;
     int failed = 0;
 #pragma omp parallel for schedule(dynamic, 1) reduction(| : failed)
@@ -133,10 +155,11 @@ int gdr_oracle_prefill(const double *q, const double *k, const double *v,
         for (int t = cu_seqlens[b]; t < cu_seqlens[b + 1]; ++t) {
             l2norm(q + ((size_t)t * Nqk + hq) * Dk, Dk, scale, qs);
             l2norm(k + ((size_t)t * Nqk + hq) * Dk, Dk, 1.0, ks);
-            const double a = exp(g[(size_t)t * Nv + h]);
+            const double a = gated ? exp(g[(size_t)t * Nv + h]) : 1.0;
             for (int i = 0; i < Dk; ++i) decay[i] = a;   /* no per-key gate in prefill */
             token_step(S, Dk, Dv, decay, ks, v + ((size_t)t * Nv + h) * Dv,
-                       beta[(size_t)t * Nv + h], qs, out + ((size_t)t * Nv + h) * Dv, kv);
+                       delta ? beta[(size_t)t * Nv + h] : 0.0, delta, qs,
+                       out + ((size_t)t * Nv + h) * Dv, kv);
         }
         free(scratch);
     }
@@ -164,6 +187,7 @@ int gdr_oracle_prefill(const double *q, const double *k, const double *v,
  *               of the exact state (what a bf16 pool holds); the token chain
  *               itself stays exact.
  *   out       [B][Nv][S][Dv]
+ *   rule      update rule 0..3 (see above)
  *
  * Routing (the pages give one index per flattened token and say ordinary
  * inference uses one slot per row): with n = num_accepted[b] clamped to
@@ -182,10 +206,12 @@ int gdr_oracle_decode(const double *q, const double *k, const double *v,
                       const double *pool_in, double *pool_out, int num_slots,
                       const int32_t *idx, const int32_t *lens, const int32_t *num_accepted,
                       int B, int S, int Nk, int Nv, int Dk, int Dv,
-                      double scale, int round_bf16, double *out)
+                      double scale, int round_bf16, int rule, double *out)
 {
-    if (B < 1 || S < 1 || Nk < 1 || Nv < 1 || Dk < 1 || Dv < 1 || Nv % Nk || num_slots < 1)
+    if (B < 1 || S < 1 || Nk < 1 || Nv < 1 || Dk < 1 || Dv < 1 || Nv % Nk || num_slots < 1 ||
+        rule < 0 || rule > 3)
         return -1;
+    const int gated = rule == 0 || rule == 2, delta = rule == 0 || rule == 1;
     for (int b = 0; b < B; ++b) {
         if (lens[b] < 0 || lens[b] > S) return -1;
         for (int t = 0; t < lens[b]; ++t)
@@ -214,10 +240,10 @@ int gdr_oracle_decode(const double *q, const double *k, const double *v,
                 const size_t tq = (((size_t)b * Nk + hk) * S + t) * Dk;
                 const size_t tv = ((size_t)b * Nv + h) * S + t;
                 for (int i = 0; i < Dk; ++i) qs[i] = q[tq + i] * scale;
-                const double a = exp(g[tv]);
+                const double a = gated ? exp(g[tv]) : 1.0;
                 for (int i = 0; i < Dk; ++i)
-                    decay[i] = gk ? a * exp(gk[tv * Dk + i]) : a;
-                token_step(Sm, Dk, Dv, decay, k + tq, v + tv * Dv, beta[tv], qs,
+                    decay[i] = (gated && gk) ? a * exp(gk[tv * Dk + i]) : a;
+                token_step(Sm, Dk, Dv, decay, k + tq, v + tv * Dv, delta ? beta[tv] : 0.0, delta, qs,
                            out + tv * Dv, kv);
                 double *dst = pool_out + ((size_t)idx[b * S + t] * Nv + h) * slab;
                 for (size_t e = 0; e < slab; ++e)

@@ -285,6 +285,68 @@ def test_multi_token_decode_equals_chained_single_tokens():
     assert not np.array_equal(pool_out[5], pool[5]) and not np.array_equal(pool_out[2], pool[2])
 
 
+# ---------------------------------------------------------------- update rules
+
+@pytest.mark.parametrize("rule", ["gated_delta", "delta", "gated", "linear"])
+@pytest.mark.parametrize("L", [1, 3, 8])
+def test_update_rules_chunked_equal_recurrence(rule, L):
+    """Each update rule ("LinearAttention" page, update_rule): the chunked
+    statement (no pre-attention matrix without the delta term, g = 0
+    without the gate) equals the per-token recurrence."""
+    rng = np.random.default_rng(60 + L)
+    q, k, v, g, beta, s0, cu = rand_prefill(rng, [11, 5], 1, 2, 4, 3)
+    o_r, s_r = oracle.prefill(q, k, v, g, beta, s0, cu, 0.8, rule=rule)
+    o_c, s_c = chunked.prefill(q, k, v, g, beta, s0, cu, 0.8, L=L, rule=rule)
+    np.testing.assert_allclose(o_c, o_r, rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(s_c, s_r, rtol=1e-11, atol=1e-12)
+
+
+def test_linear_and_gated_rules_closed_form():
+    """Without the delta term the state is a (decayed) sum of outer products:
+    o_t = e^{G_t} S0^T q_t + sum_{s<=t} e^{G_t - G_s} (q_t . k_s) v_s with
+    G_t = sum_{r<=t} g_r (G = 0 for the linear rule); beta plays no part."""
+    rng = np.random.default_rng(64)
+    T, Dk, Dv = 9, 5, 4
+    q, k, v, g, beta, s0, cu = rand_prefill(rng, [T], 1, 1, Dk, Dv)
+    qn = q[:, 0] / np.sqrt(np.sum(q[:, 0] ** 2, -1, keepdims=True) + 1e-6) * 0.7
+    kn = k[:, 0] / np.sqrt(np.sum(k[:, 0] ** 2, -1, keepdims=True) + 1e-6)
+    for rule, G in (("linear", np.zeros(T)), ("gated", np.cumsum(g[:, 0]))):
+        o, st = oracle.prefill(q, k, v, g, beta, s0, cu, 0.7, rule=rule)
+        o2, _ = oracle.prefill(q, k, v, g, np.ones_like(beta), s0, cu, 0.7, rule=rule)
+        assert np.array_equal(o, o2)
+        for t in range(T):
+            ref = np.exp(G[t]) * s0[0, 0].T @ qn[t]
+            for s_ in range(t + 1):
+                ref += np.exp(G[t] - G[s_]) * (qn[t] @ kn[s_]) * v[s_, 0]
+            np.testing.assert_allclose(o[t, 0], ref, rtol=1e-12, atol=1e-13)
+        Sref = np.exp(G[-1]) * s0[0, 0] + sum(np.exp(G[-1] - G[s_]) * np.outer(kn[s_], v[s_, 0]) for s_ in range(T))
+        np.testing.assert_allclose(st[0, 0], Sref, rtol=1e-12, atol=1e-13)
+
+
+def test_delta_rule_is_gated_delta_without_gates():
+    rng = np.random.default_rng(65)
+    q, k, v, g, beta, s0, cu = rand_prefill(rng, [7, 4], 1, 2, 4, 3)
+    a = oracle.prefill(q, k, v, g, beta, s0, cu, 0.5, rule="delta")
+    b = oracle.prefill(q, k, v, np.zeros_like(g), beta, s0, cu, 0.5)
+    for x, y in zip(a, b):
+        assert np.array_equal(x, y)
+    # decode: g and gk are ignored by the delta and linear rules
+    _, r, _ = _spec_case(66)
+    pool = rng.standard_normal((4, 2, 4, 3))
+    idx = np.repeat(np.array([0, 1, 2], np.int32), 4)
+    lens = np.array([4, 3, 1], np.int32)
+    d1 = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 0.9, rule="delta")
+    d2 = oracle.decode(r[0], r[1], r[2], np.zeros_like(r[3]), None, r[5], pool, idx, lens, 0.9)
+    for x, y in zip(d1, d2):
+        assert np.array_equal(x, y)
+    l1 = oracle.decode(*r[:4], r[4], r[5], pool, idx, lens, 0.9, rule="linear")
+    l2 = oracle.decode(*r[:4], None, np.ones_like(r[5]), pool, idx, lens, 0.9, rule="gated")
+    l3 = oracle.decode(r[0], r[1], r[2], np.zeros_like(r[3]), None, r[5], pool, idx, lens, 0.9, rule="gated")
+    for x, y in zip(l1, l3):
+        assert np.array_equal(x, y)
+    assert not np.array_equal(l1[0], l2[0])
+
+
 def _spec_case(seed, B=3, S=4, Nk=1, Nv=2, Dk=4, Dv=3):
     rng = np.random.default_rng(seed)
     def toks():
