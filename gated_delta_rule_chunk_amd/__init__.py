@@ -44,11 +44,11 @@ SIGNATURES = {
     "gdr_chunk_prefill_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32,
                                                         ctypes.POINTER(ctypes.c_size_t)]),
     "gdr_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
-                                         _i32, ctypes.c_float, ctypes.c_int, _vp, _vp, _vp,
+                                         _i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
     "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
-                                            ctypes.c_int, ctypes.c_int, _vp, _vp]),
+                                            ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
     "gdr_timing_enable": (ctypes.c_int, [ctypes.c_int]),
     "gdr_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
                                        _i32]),
@@ -105,6 +105,19 @@ def _dev(tensors, device):
             raise ValueError(f"{name} must be contiguous")
 
 
+RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
+
+
+def _rule(rule, g, beta) -> int:
+    if rule not in RULES:
+        raise ValueError(f"rule must be one of {sorted(RULES)} (got {rule!r})")
+    if rule in ("gated_delta", "gated") and g is None:
+        raise ValueError(f"rule {rule} needs g")
+    if rule in ("gated_delta", "delta") and beta is None:
+        raise ValueError(f"rule {rule} needs beta")
+    return RULES[rule]
+
+
 def _ptr(t):
     return None if t is None else t.data_ptr()
 
@@ -134,11 +147,13 @@ def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, state_out=None,
-                  workspace=None):
+                  workspace=None, rule="gated_delta"):
     """Chunked Gated Delta Rule prefill ("Qwen3Next Samples" page).
 
     q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv] (act dtype: bf16 or fp32);
-    g [T,Nv] fp32; cu_seqlens [B+1] int32; state_in [B,Nv,D,D] fp32 or None.
+    g [T,Nv] fp32; cu_seqlens [B+1] int32; state_in [B,Nv,D,D] fp32 or None;
+    rule one of RULES (g may be None without a gate, beta without the delta
+    term).
     Returns (out [T,Nv,D] act dtype, state_out [B,Nv,D,D] fp32).  `out`,
     `state_out` and `workspace` (uint8, >= chunk_prefill_workspace_size
     bytes) may be passed in to avoid allocations.
@@ -150,16 +165,17 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
     Nv = v.shape[1]
     if v.shape[2] != D:
         raise ValueError("v must have the head dimension of q")
-    if g.shape != (T, Nv) or beta.shape != (T, Nv):
+    code = _rule(rule, g, beta)
+    if (g is not None and g.shape != (T, Nv)) or (beta is not None and beta.shape != (T, Nv)):
         raise ValueError(f"g and beta must be [T, Nv] = [{T}, {Nv}]")
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 2:
         raise ValueError("cu_seqlens must be [B+1] with B >= 1")
     B = cu_seqlens.numel() - 1
     act = _act(q, "q")
     for name, t in (("k", k), ("v", v), ("beta", beta)):
-        if t.dtype != q.dtype:
+        if t is not None and t.dtype != q.dtype:
             raise RuntimeError(f"{name} must have the dtype of q ({q.dtype}), got {t.dtype}")
-    if g.dtype != torch.float32:
+    if g is not None and g.dtype != torch.float32:
         raise RuntimeError("g must be float32")
     if cu_seqlens.dtype != torch.int32:
         raise RuntimeError("cu_seqlens must be int32")
@@ -183,7 +199,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
     _dev(dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, out=out,
               state_out=state_out, workspace=workspace), device)
     check(lib().gdr_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
-                                  _ptr(cu_seqlens), T, B, Nqk, Nv, D, float(scale), act, _ptr(out),
+                                  _ptr(cu_seqlens), T, B, Nqk, Nv, D, float(scale), code, act, _ptr(out),
                                   _ptr(state_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(device)),
           "gdr_chunk_prefill")
@@ -191,7 +207,7 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
 
 
 def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths,
-                     scale=1.0, out=None, num_accepted_tokens=None):
+                     scale=1.0, out=None, num_accepted_tokens=None, rule="gated_delta"):
     """Recurrent Gated Delta Rule decode over a slot pool
     ("lite_boost.ops.recurrent_gated_delta_rule" page).
 
@@ -200,7 +216,9 @@ def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual
     fp32, updated in place); ssm_state_indices [B*S] int32;
     actual_seq_lengths [B] int32; num_accepted_tokens [B] int32 or None
     (speculative decoding: row b resumes from slot
-    ssm_state_indices[b*S + n_b - 1]).  Returns (out [B,Nv,S,Dv], state_pool).
+    ssm_state_indices[b*S + n_b - 1]); rule one of RULES (g and gk may be
+    None without a gate, beta without the delta term).  Returns
+    (out [B,Nv,S,Dv], state_pool).
     """
     if q.dim() != 4 or k.shape != q.shape:
         raise ValueError(f"q and k must be [B,Nk,S,Dk] (got {tuple(q.shape)}, {tuple(k.shape)})")
@@ -208,7 +226,8 @@ def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual
     if v.dim() != 4 or v.shape[0] != B or v.shape[2] != S:
         raise ValueError(f"v must be [B,Nv,S,Dv] (got {tuple(v.shape)})")
     Nv, Dv = v.shape[1], v.shape[3]
-    if g.shape != (B, Nv, S) or beta.shape != (B, Nv, S):
+    code = _rule(rule, g, beta)
+    if (g is not None and g.shape != (B, Nv, S)) or (beta is not None and beta.shape != (B, Nv, S)):
         raise ValueError("g and beta must be [B, Nv, S]")
     if gk is not None and gk.shape != (B, Nv, S, Dk):
         raise ValueError("gk must be [B, Nv, S, Dk]")
@@ -223,10 +242,10 @@ def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual
         raise ValueError(f"num_accepted_tokens must hold B = {B} entries")
     act = _act(q, "q")
     for name, t in (("k", k), ("v", v), ("beta", beta)):
-        if t.dtype != q.dtype:
+        if t is not None and t.dtype != q.dtype:
             raise RuntimeError(f"{name} must have the dtype of q ({q.dtype}), got {t.dtype}")
     st = _act(state_pool, "state_pool")
-    if g.dtype != torch.float32 or (gk is not None and gk.dtype != torch.float32):
+    if (g is not None and g.dtype != torch.float32) or (gk is not None and gk.dtype != torch.float32):
         raise RuntimeError("g and gk must be float32")
     if ssm_state_indices.dtype != torch.int32 or actual_seq_lengths.dtype != torch.int32 or (
             num_accepted_tokens is not None and num_accepted_tokens.dtype != torch.int32):
@@ -243,7 +262,7 @@ def recurrent_decode(q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual
     check(lib().gdr_recurrent_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
                                      _ptr(state_pool), state_pool.shape[0], _ptr(ssm_state_indices),
                                      _ptr(actual_seq_lengths), _ptr(num_accepted_tokens), B, S, Nk, Nv,
-                                     Dk, Dv, float(scale),
+                                     Dk, Dv, float(scale), code,
                                      act, st, _ptr(out), _stream(device)),
           "gdr_recurrent_decode")
     return out, state_pool

@@ -97,25 +97,34 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
     return ok();
 }
 
+static bool rule_ok(gdr_update_rule r) {
+    return r == GDR_RULE_GATED_DELTA || r == GDR_RULE_DELTA || r == GDR_RULE_GATED || r == GDR_RULE_LINEAR;
+}
+static bool rule_gated(gdr_update_rule r) { return r == GDR_RULE_GATED_DELTA || r == GDR_RULE_GATED; }
+static bool rule_delta(gdr_update_rule r) { return r == GDR_RULE_GATED_DELTA || r == GDR_RULE_DELTA; }
+
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
                              const void* beta, const float* state_in, const int32_t* cu_seqlens,
                              int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D, float scale,
-                             gdr_dtype act, void* out, float* state_out, void* workspace,
-                             size_t workspace_bytes, void* hip_stream) {
+                             gdr_update_rule rule, gdr_dtype act, void* out, float* state_out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream) {
     gdr_status s = check_prefill_sizes(T, B, Nqk, Nv, D);
     if (s != GDR_OK) return s;
     if (act != GDR_BF16 && act != GDR_FP32)
         return fail(GDR_ERR_DTYPE, "activation dtype must be GDR_BF16 or GDR_FP32 (got %d)", (int)act);
+    if (!rule_ok(rule)) return fail(GDR_ERR_INVALID_ARGUMENT, "unknown update rule %d", (int)rule);
     if (!cu_seqlens || !state_out)
         return fail(GDR_ERR_INVALID_ARGUMENT, "cu_seqlens and state_out must not be NULL");
-    if (T > 0 && (!q || !k || !v || !g || !beta || !out))
-        return fail(GDR_ERR_INVALID_ARGUMENT, "q, k, v, g, beta and out must not be NULL when T > 0");
+    if (T > 0 && (!q || !k || !v || !out || (rule_gated(rule) && !g) || (rule_delta(rule) && !beta)))
+        return fail(GDR_ERR_INVALID_ARGUMENT,
+                    "q, k, v, out (and g for the gated rules, beta for the delta rules) must not be NULL "
+                    "when T > 0");
     const gdr::PrefillLayout lay = gdr::prefill_layout(T, B, Nqk, Nv);
     if (!workspace || workspace_bytes < lay.total)
         return fail(GDR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu, ptr %p)", lay.total,
                     workspace_bytes, workspace);
     gdr::PrefillArgs a{q, k, v, g, beta, state_in, cu_seqlens, out, state_out,
-                       static_cast<char*>(workspace), T, B, Nqk, Nv, scale};
+                       static_cast<char*>(workspace), T, B, Nqk, Nv, scale, (int32_t)rule};
     return from_hip(gdr::prefill_launch(a, lay, act == GDR_BF16, static_cast<hipStream_t>(hip_stream)),
                     "prefill launch");
 }
@@ -123,9 +132,9 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
 gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, const float* g,
                                 const float* gk, const void* beta, void* state_pool, int32_t num_slots,
                                 const int32_t* ssm_state_indices, const int32_t* actual_seq_lengths,
-                                const int32_t* num_accepted_tokens, int32_t B, int32_t S, int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv,
-                                float scale, gdr_dtype act, gdr_dtype state_dtype, void* out,
-                                void* hip_stream) {
+                                const int32_t* num_accepted_tokens, int32_t B, int32_t S, int32_t Nk,
+                                int32_t Nv, int32_t Dk, int32_t Dv, float scale, gdr_update_rule rule,
+                                gdr_dtype act, gdr_dtype state_dtype, void* out, void* hip_stream) {
     if (B < 1) return fail(GDR_ERR_INVALID_ARGUMENT, "B must be >= 1 (got %d)", B);
     if (S < 1 || S > gdr::kMaxDecodeTokens)
         return fail(GDR_ERR_INVALID_ARGUMENT, "S must be in [1, %d] (got %d)", gdr::kMaxDecodeTokens, S);
@@ -141,12 +150,16 @@ gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, con
     if ((act != GDR_BF16 && act != GDR_FP32) || (state_dtype != GDR_BF16 && state_dtype != GDR_FP32))
         return fail(GDR_ERR_DTYPE, "dtypes must be GDR_BF16 or GDR_FP32 (act=%d, state=%d)", (int)act,
                     (int)state_dtype);
-    if (!q || !k || !v || !g || !beta || !state_pool || !ssm_state_indices || !actual_seq_lengths || !out)
-        return fail(GDR_ERR_INVALID_ARGUMENT, "only gk and num_accepted_tokens may be NULL");
+    if (!rule_ok(rule)) return fail(GDR_ERR_INVALID_ARGUMENT, "unknown update rule %d", (int)rule);
+    if (!q || !k || !v || !state_pool || !ssm_state_indices || !actual_seq_lengths || !out ||
+        (rule_gated(rule) && !g) || (rule_delta(rule) && !beta))
+        return fail(GDR_ERR_INVALID_ARGUMENT,
+                    "only gk, num_accepted_tokens, g (rules without a gate) and beta (rules without the "
+                    "delta term) may be NULL");
     if ((int64_t)B * Nv * (Dv / (Dv == 64 ? 64 : 128)) > 0x7fffffffLL)
         return fail(GDR_ERR_INVALID_ARGUMENT, "B * Nv too large");
     gdr::DecodeArgs a{q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths,
-                      num_accepted_tokens, out, num_slots, B, S, Nk, Nv, Dk, Dv, scale};
+                      num_accepted_tokens, out, num_slots, B, S, Nk, Nv, Dk, Dv, scale, (int32_t)rule};
     return from_hip(gdr::decode_launch(a, act == GDR_BF16, state_dtype == GDR_BF16,
                                        static_cast<hipStream_t>(hip_stream)),
                     "decode launch");

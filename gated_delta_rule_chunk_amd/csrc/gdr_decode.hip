@@ -88,21 +88,25 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
             for (int c = 0; c < 8; ++c) st[m][c] = 0.f;
     }
 
+    // update rule ("LinearAttention" page, update_rule): the delta and linear
+    // rules have no decay, the gated and linear rules no delta term
+    const bool gated = a.rule == 0 || a.rule == 2, delta = a.rule == 0 || a.rule == 1;
+
     // per-token key rows, scaled query rows and row decays -> LDS
     for (int e = tid; e < len * DK; e += NT) {
         const int t = e / DK, i = e % DK;
         const size_t qi = (((size_t)b * a.Nk + hk) * S + t) * DK + i;
         s_k[t][i] = load1(k + qi);
         s_q[t][i] = load1(q + qi) * a.scale;
-        const float eg = expf(a.g[tok0 + t]);
-        s_a[t][i] = a.gk ? eg * expf(a.gk[(tok0 + t) * DK + i]) : eg;
+        const float eg = gated ? expf(a.g[tok0 + t]) : 1.f;
+        s_a[t][i] = (gated && a.gk) ? eg * expf(a.gk[(tok0 + t) * DK + i]) : eg;
     }
     __syncthreads();
 
     for (int t = 0; t < len; ++t) {
         float vv[8];
         load8(v + (tok0 + t) * Dv + col, vv);
-        const float bt = load1(beta + tok0 + t);
+        const float bt = delta ? load1(beta + tok0 + t) : 1.f;
 
         // decay + partial reductions over this thread's rows
         float pk[8], pq[8], pkq = 0.f;
@@ -157,7 +161,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float d[8], o[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            d[c] = bt * (vv[c] - kv[c]);
+            d[c] = delta ? bt * (vv[c] - kv[c]) : vv[c];
             o[c] = fmaf(d[c], kq, qs[c]);
         }
 #pragma unroll

@@ -32,6 +32,7 @@ struct DecodeArgs {
     void* out;
     int32_t num_slots, B, S, Nk, Nv, Dk, Dv;
     float scale;
+    int32_t rule;          // update rule code (0 gated_delta, 1 delta, 2 gated, 3 linear)
 };
 
 hipError_t decode_launch(const DecodeArgs& a, bool act_bf16, bool state_bf16, hipStream_t stream);
@@ -74,6 +75,7 @@ struct PrefillArgs {
     int64_t T;
     int32_t B, Nqk, Nv;
     float scale;
+    int32_t rule;          // update rule code (0 gated_delta, 1 delta, 2 gated, 3 linear)
 };
 
 hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool act_bf16,

@@ -53,6 +53,16 @@ constexpr int LD16 = 136;   // fp16 LDS row stride (elements): 272 B, 16-byte al
 constexpr int TILE = 128 * 128;
 constexpr float kNormEps = 1e-6f;
 
+// Update rules ("LinearAttention" page, update_rule; codes as in the C ABI):
+// 0 gated_delta, 1 delta (no decay), 2 gated (no delta term), 3 linear
+// (neither).  Only the intra kernel depends on the rule: without a gate the
+// gates are zero; without the delta term L = 0 (so T = I), u = v and w = 0,
+// which turns the scan's v_new = u - w S into v.
+template <int RULE> struct Rule {
+    static constexpr bool gated = RULE == 0 || RULE == 2;
+    static constexpr bool delta = RULE == 0 || RULE == 1;
+};
+
 struct PrefillDev {
     const void* q;
     const void* k;
@@ -272,7 +282,7 @@ struct IntraStage {
     int c, h, t0, r;
 };
 
-template <typename ActT>
+template <typename ActT, int RULE>
 __device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, int item, int wave, int lane,
                                            int lr, int lq, int c4, int tg) {
     const int Nv = p.Nv, Nqk = p.Nqk;
@@ -288,10 +298,19 @@ __device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDe
     // only wave 0 uses the gates; the other waves issue the same loads at one
     // lane-uniform address (a single cache line each)
     const int i0 = wave == 0 ? min(2 * lane, last) : 0, i1 = wave == 0 ? min(2 * lane + 1, last) : 0;
-    st.g0 = p.g[(size_t)(t0 + i0) * Nv + h];
-    st.g1 = p.g[(size_t)(t0 + i1) * Nv + h];
-    st.b0 = BETA[(size_t)(t0 + i0) * Nv + h];
-    st.b1 = BETA[(size_t)(t0 + i1) * Nv + h];
+    if constexpr (Rule<RULE>::gated) {
+        st.g0 = p.g[(size_t)(t0 + i0) * Nv + h];
+        st.g1 = p.g[(size_t)(t0 + i1) * Nv + h];
+    } else {
+        st.g0 = st.g1 = 0.f;
+    }
+    if constexpr (Rule<RULE>::delta) {
+        st.b0 = BETA[(size_t)(t0 + i0) * Nv + h];
+        st.b1 = BETA[(size_t)(t0 + i1) * Nv + h];
+    } else {
+        (void)BETA;
+        st.b0 = st.b1 = ActT(0);
+    }
 }
 
 struct IntraSmem {
@@ -303,7 +322,7 @@ struct IntraSmem {
     float* sBE;
 };
 
-template <typename ActT>
+template <typename ActT, int RULE>
 __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const PrefillDev& p, const IntraSmem& sm,
                                            int tid_in) {
     // The item loop would otherwise hoist every per-lane offset derived from
@@ -342,7 +361,9 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     if (wave == 0) {   // lane owns rows 2l, 2l+1
         const int i0 = 2 * lane, i1 = i0 + 1;
         const float g0 = i0 < r ? st.g0 : 0.f, g1 = i1 < r ? st.g1 : 0.f;
-        const float b0 = i0 < r ? load1(&st.b0) : 0.f, b1 = i1 < r ? load1(&st.b1) : 0.f;
+        // without the delta term beta is 1 for u = T v and 0 for w (below)
+        const float b0 = i0 < r ? (Rule<RULE>::delta ? load1(&st.b0) : 1.f) : 0.f;
+        const float b1 = i1 < r ? (Rule<RULE>::delta ? load1(&st.b1) : 1.f) : 0.f;
         const float s = g0 + g1;
         float incl = s;
 #pragma unroll
@@ -358,7 +379,8 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
         if (i1 >= r) gc1 = glast;
         sGc[i0] = gc0; sGc[i1] = gc1;
         sBeta[i0] = b0; sBeta[i1] = b1;
-        sBE[i0] = b0 * __expf(gc0); sBE[i1] = b1 * __expf(gc1);
+        sBE[i0] = Rule<RULE>::delta ? b0 * __expf(gc0) : 0.f;
+        sBE[i1] = Rule<RULE>::delta ? b1 * __expf(gc1) : 0.f;
         p.gc[ch * 128 + i0] = gc0;
         p.gc[ch * 128 + i1] = gc1;
     }
@@ -398,15 +420,17 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
         int I, J;
         tri_tile(n, I, J);
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (Rule<RULE>::delta) {
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            acc = mma(ld_h8(&sA[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
-                      ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mma(ld_h8(&sA[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
+                          ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+        }
         const int j = 16 * J + lr;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int i = 16 * I + 4 * lq + e;
-            const float Lij = i > j ? sBeta[i] * acc[e] * __expf(sGc[i] - sGc[j]) : 0.f;
+            const float Lij = (Rule<RULE>::delta && i > j) ? sBeta[i] * acc[e] * __expf(sGc[i] - sGc[j]) : 0.f;
             sL[i * LD16 + j] = (_Float16)Lij;
             if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
         }
@@ -555,7 +579,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
 // Persistent: each workgroup walks items blockIdx.x, blockIdx.x + gridDim.x, ...
 // (item = chunk * Nv + value head).  With bf16 activations two register
 // stages alternate, so the next item's inputs load while this one computes.
-template <typename ActT>
+template <typename ActT, int RULE>
 __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sA[128 * LD16];
     __shared__ __align__(16) _Float16 sL[128 * LD16];
@@ -570,27 +594,27 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     if (it >= n_items) return;
     if constexpr (sizeof(ActT) == 2) {
         IntraStage<ActT> A, B;
-        intra_load(A, p, it, wave, lane, lr, lq, c4, tg);
+        intra_load<ActT, RULE>(A, p, it, wave, lane, lr, lq, c4, tg);
         // The next item's loads are issued on every pass (after the last
         // item they re-read the current one, unused), so that the waits the
         // compiler places for the current item's data never cover them.
         while (true) {
             const int nx = it + stride;
-            intra_load(B, p, nx < n_items ? nx : it, wave, lane, lr, lq, c4, tg);
-            intra_item(A, p, sm, tid);
+            intra_load<ActT, RULE>(B, p, nx < n_items ? nx : it, wave, lane, lr, lq, c4, tg);
+            intra_item<ActT, RULE>(A, p, sm, tid);
             if (nx >= n_items) break;
             it = nx;
             const int nx2 = it + stride;
-            intra_load(A, p, nx2 < n_items ? nx2 : it, wave, lane, lr, lq, c4, tg);
-            intra_item(B, p, sm, tid);
+            intra_load<ActT, RULE>(A, p, nx2 < n_items ? nx2 : it, wave, lane, lr, lq, c4, tg);
+            intra_item<ActT, RULE>(B, p, sm, tid);
             if (nx2 >= n_items) break;
             it = nx2;
         }
     } else {
         for (; it < n_items; it += stride) {
             IntraStage<ActT> A;
-            intra_load(A, p, it, wave, lane, lr, lq, c4, tg);
-            intra_item(A, p, sm, tid);
+            intra_load<ActT, RULE>(A, p, it, wave, lane, lr, lq, c4, tg);
+            intra_item<ActT, RULE>(A, p, sm, tid);
         }
     }
 }
@@ -952,6 +976,20 @@ static int compute_units() {
     return cached[dev];
 }
 
+template <int RULE>
+static void launch_intra_rule(bool act_bf16, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+    if (act_bf16) hipLaunchKernelGGL((intra_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((intra_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
+}
+static void launch_intra(int rule, bool act_bf16, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+    switch (rule) {
+        case 1: launch_intra_rule<1>(act_bf16, grid, stream, p); break;
+        case 2: launch_intra_rule<2>(act_bf16, grid, stream, p); break;
+        case 3: launch_intra_rule<3>(act_bf16, grid, stream, p); break;
+        default: launch_intra_rule<0>(act_bf16, grid, stream, p); break;
+    }
+}
+
 hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool act_bf16, hipStream_t stream) {
     const int ncu = compute_units();
     PrefillDev p;
@@ -978,8 +1016,7 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
         // persistent: two workgroups per CU (LDS < 80 KiB each), each walking items
         const size_t nint = nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu;
         timing_begin(kIntra, stream);
-        if (act_bf16) hipLaunchKernelGGL(intra_kernel<uint16_t>, dim3((unsigned)nint), dim3(512), 0, stream, p);
-        else hipLaunchKernelGGL(intra_kernel<float>, dim3((unsigned)nint), dim3(512), 0, stream, p);
+        launch_intra(a.rule, act_bf16, dim3((unsigned)nint), stream, p);
         timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }

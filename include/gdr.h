@@ -61,6 +61,22 @@ typedef enum gdr_dtype {
     GDR_BF16 = 1
 } gdr_dtype;
 
+/* State update rule ("LinearAttention" contrib-operator page, attribute
+ * update_rule, which names linear, gated, delta and gated_delta without
+ * formulas).  Readings: each rule drops parts of the gated delta rule
+ *   S = S exp(g) exp(gk);  S = S + k ((v - S^T k) beta)^T;  o = S^T q:
+ *   GDR_RULE_GATED_DELTA  all of it (the default of both pages)
+ *   GDR_RULE_DELTA        no decay (g and gk are ignored and may be NULL)
+ *   GDR_RULE_GATED        no delta term: S = S exp(g) exp(gk) + k v^T
+ *                         (beta is ignored and may be NULL)
+ *   GDR_RULE_LINEAR       neither: S = S + k v^T */
+typedef enum gdr_update_rule {
+    GDR_RULE_GATED_DELTA = 0,
+    GDR_RULE_DELTA = 1,
+    GDR_RULE_GATED = 2,
+    GDR_RULE_LINEAR = 3
+} gdr_update_rule;
+
 /* Static text for a status code ("unknown status" for other values). */
 const char *gdr_status_string(int status);
 
@@ -93,7 +109,8 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  *   q^ = q / sqrt(sum q^2 + 1e-6) * scale,  k^ = k / sqrt(sum k^2 + 1e-6)
  *   S = exp(g) S;  S = S + k^ ((v - S^T k^) beta)^T;  out = S^T q^
  * and writes the final S to state_out[b,h].  A sequence of length 0 passes
- * its state through unchanged.
+ * its state through unchanged.  `rule` selects a reduced update (see
+ * gdr_update_rule); q and k are L2-normalised inside for every rule.
  *
  *   q, k        [T, Nqk, D]   act dtype   (raw; normalised inside)
  *   v           [T, Nv, D]    act dtype
@@ -103,6 +120,8 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  *   cu_seqlens  [B + 1]       int32, device; cu[0] = 0, non-decreasing, cu[B] = T
  *   T, B, Nqk, Nv, D          sizes; D must be 128 (the page fixes D = L = 128)
  *   scale                     multiplies the normalised q (e.g. 1/sqrt(D))
+ *   rule                      update rule; g may be NULL without a gate,
+ *                             beta without the delta term
  *   act                       GDR_BF16 or GDR_FP32 (q, k, v, beta, out)
  *   out         [T, Nv, D]    act dtype
  *   state_out   [B, Nv, D, D] fp32; may be the same pointer as state_in
@@ -112,8 +131,9 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
 gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
                              const void *beta, const float *state_in, const int32_t *cu_seqlens,
                              int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D,
-                             float scale, gdr_dtype act, void *out, float *state_out,
-                             void *workspace, size_t workspace_bytes, void *hip_stream);
+                             float scale, gdr_update_rule rule, gdr_dtype act, void *out,
+                             float *state_out, void *workspace, size_t workspace_bytes,
+                             void *hip_stream);
 
 /* ------------------------------------------------------------------ decode
  *
@@ -154,6 +174,8 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
  *   B >= 1; 1 <= S <= 8 (decode only, as the page limits it);
  *   Nv a multiple of Nk; Dk in {64, 128}; Dv in {64, 128, 256, 512}
  *   scale               multiplies q before use (the page's scale_value)
+ *   rule                update rule (see gdr_update_rule); g may be NULL
+ *                       without a gate, beta without the delta term
  *   act                 GDR_BF16 or GDR_FP32 (q, k, v, beta, out)
  *   state_dtype         GDR_BF16 (the page's pool) or GDR_FP32
  *   out                 [B, Nv, S, Dv]  act dtype
@@ -168,8 +190,8 @@ gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, con
                                 const int32_t *actual_seq_lengths,
                                 const int32_t *num_accepted_tokens, int32_t B, int32_t S,
                                 int32_t Nk, int32_t Nv, int32_t Dk, int32_t Dv, float scale,
-                                gdr_dtype act, gdr_dtype state_dtype, void *out,
-                                void *hip_stream);
+                                gdr_update_rule rule, gdr_dtype act, gdr_dtype state_dtype,
+                                void *out, void *hip_stream);
 
 /* ------------------------------------------------------------------ timing
  *

@@ -61,12 +61,13 @@ def test_workspace_size_validation_and_monotonicity():
 
 def prefill_call(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state_in=None, cu=FAKE, T=256, B=1, Nqk=2,
-             Nv=4, D=128, scale=0.1, act=gdr.GDR_BF16, out=FAKE, state_out=FAKE, ws=FAKE,
+             Nv=4, D=128, scale=0.1, rule=0, act=gdr.GDR_BF16, out=FAKE, state_out=FAKE, ws=FAKE,
              ws_bytes=1 << 40, stream=None)
     a.update(over)
     return gdr.lib().gdr_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["cu"],
-                                       a["T"], a["B"], a["Nqk"], a["Nv"], a["D"], a["scale"], a["act"],
-                                       a["out"], a["state_out"], a["ws"], a["ws_bytes"], a["stream"])
+                                       a["T"], a["B"], a["Nqk"], a["Nv"], a["D"], a["scale"], a["rule"],
+                                       a["act"], a["out"], a["state_out"], a["ws"], a["ws_bytes"],
+                                       a["stream"])
 
 
 def test_prefill_host_validation():
@@ -82,17 +83,25 @@ def test_prefill_host_validation():
     assert prefill_call(ws=None) == E.GDR_ERR_WORKSPACE
     assert prefill_call(ws_bytes=100) == E.GDR_ERR_WORKSPACE
     assert b"workspace" in gdr.lib().gdr_last_error()
+    # update rules: unknown codes fail; g / beta may be NULL only where the rule ignores them
+    assert prefill_call(rule=7) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(g=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(g=None, rule=1, ws=None) == E.GDR_ERR_WORKSPACE      # passes the pointer checks
+    assert prefill_call(beta=None, rule=2, ws=None) == E.GDR_ERR_WORKSPACE
+    assert prefill_call(g=None, beta=None, rule=3, ws=None) == E.GDR_ERR_WORKSPACE
+    assert prefill_call(beta=None, rule=1) == E.GDR_ERR_INVALID_ARGUMENT
+    assert prefill_call(g=None, rule=2) == E.GDR_ERR_INVALID_ARGUMENT
 
 
 def decode_call(**over):
     a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, beta=FAKE, pool=FAKE, slots=8, idx=FAKE,
-             lens=FAKE, nacc=None, B=2, S=1, Nk=2, Nv=4, Dk=128, Dv=128, scale=0.1, act=gdr.GDR_BF16,
+             lens=FAKE, nacc=None, B=2, S=1, Nk=2, Nv=4, Dk=128, Dv=128, scale=0.1, rule=0, act=gdr.GDR_BF16,
              st=gdr.GDR_BF16, out=FAKE, stream=None)
     a.update(over)
     return gdr.lib().gdr_recurrent_decode(a["q"], a["k"], a["v"], a["g"], a["gk"], a["beta"], a["pool"],
                                           a["slots"], a["idx"], a["lens"], a["nacc"], a["B"], a["S"], a["Nk"],
                                           a["Nv"],
-                                          a["Dk"], a["Dv"], a["scale"], a["act"], a["st"], a["out"],
+                                          a["Dk"], a["Dv"], a["scale"], a["rule"], a["act"], a["st"], a["out"],
                                           a["stream"])
 
 
@@ -109,6 +118,10 @@ def test_decode_host_validation():
     assert decode_call(st=5) == E.GDR_ERR_DTYPE
     assert decode_call(idx=None) == E.GDR_ERR_INVALID_ARGUMENT
     assert decode_call(pool=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(rule=9) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(g=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(beta=None, rule=1) == E.GDR_ERR_INVALID_ARGUMENT
+    assert decode_call(g=None, rule=2) == E.GDR_ERR_INVALID_ARGUMENT
     assert b"Nv" in gdr.lib().gdr_last_error() or True
 
 

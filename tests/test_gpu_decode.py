@@ -12,21 +12,26 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_gpu(inp, pool=None):
+def run_gpu(inp, pool=None, rule="gated_delta"):
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     pool_dev = (inp["pool"] if pool is None else pool).clone().to(DEV)
-    out, _ = gdr.recurrent_decode(d["q"], d["k"], d["v"], d["g"], d["gk"], d["beta"], pool_dev,
-                                  d["idx"], d["lens"], d["scale"], num_accepted_tokens=d.get("nacc"))
+    g, gk, beta = d["g"], d["gk"], d["beta"]
+    if rule in ("delta", "linear"):   # NULL where the rule ignores the input
+        g = gk = None
+    if rule in ("gated", "linear"):
+        beta = None
+    out, _ = gdr.recurrent_decode(d["q"], d["k"], d["v"], g, gk, beta, pool_dev,
+                                  d["idx"], d["lens"], d["scale"], num_accepted_tokens=d.get("nacc"), rule=rule)
     torch.cuda.synchronize()
     return out.cpu(), pool_dev.cpu()
 
 
-def run_oracle(inp, pool=None):
+def run_oracle(inp, pool=None, rule="gated_delta"):
     pool = inp["pool"] if pool is None else pool
     bf16_pool = pool.dtype == torch.bfloat16
     return oracle.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["gk"], inp["beta"], pool,
                          inp["idx"], inp["lens"], inp["scale"], round_state_bf16=bf16_pool,
-                         num_accepted=inp.get("nacc"))
+                         num_accepted=inp.get("nacc"), rule=rule)
 
 
 def written_slots(inp):
@@ -35,10 +40,10 @@ def written_slots(inp):
     return sorted({int(idx[b, t]) for b in range(inp["B"]) for t in range(lens[b])})
 
 
-def check_parity(inp, tag):
+def check_parity(inp, tag, rule="gated_delta"):
     print(f"[decode parity] {tag}", flush=True)
-    out, pool = run_gpu(inp)
-    out_ref, pool_ref = run_oracle(inp)
+    out, pool = run_gpu(inp, rule=rule)
+    out_ref, pool_ref = run_oracle(inp, rule=rule)
     bf16_out = out.dtype == torch.bfloat16
     lens = inp["lens"].numpy()
     valid = np.zeros(out.shape, bool)
@@ -164,3 +169,12 @@ def test_decode_speculative_rounds_resume_after_accepted_tokens(Dk, Dv, with_gk)
     ws = written_slots(r2)
     es = assert_state_close(to_f64(pool2)[ws], pool2_ref[ws], "speculative state")
     print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("rule", ["delta", "gated", "linear"])
+def test_decode_update_rules(rule):
+    """Update rules ("LinearAttention" page, update_rule) with NULL g, gk or
+    beta where the rule ignores them."""
+    inp = workloads.decode_inputs(90, B=12, S=3, Nk=2, Nv=4, Dk=128, Dv=128, num_slots=30, with_gk=True,
+                                  lens="random", routing="two_slots")
+    check_parity(inp, f"rule {rule}", rule=rule)

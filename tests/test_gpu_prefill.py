@@ -12,18 +12,22 @@ pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
 
 
-def run_gpu(inp, state_in="from_inputs"):
+def run_gpu(inp, state_in="from_inputs", rule="gated_delta", drop_unused=True):
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     s_in = d["state_in"] if isinstance(state_in, str) else (None if state_in is None else state_in.to(DEV))
-    out, st = gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["scale"],
-                                state_in=s_in)
+    g, beta = d["g"], d["beta"]
+    if drop_unused:   # the rules without a gate / delta term take NULL there
+        g = None if rule in ("delta", "linear") else g
+        beta = None if rule in ("gated", "linear") else beta
+    out, st = gdr.chunk_prefill(d["q"], d["k"], d["v"], g, beta, d["cu_seqlens"], d["scale"],
+                                state_in=s_in, rule=rule)
     torch.cuda.synchronize()
     return out.cpu(), st.cpu()
 
 
-def run_oracle(inp):
+def run_oracle(inp, rule="gated_delta"):
     return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["state_in"],
-                          inp["cu_seqlens"], inp["scale"])
+                          inp["cu_seqlens"], inp["scale"], rule=rule)
 
 
 def check_parity(inp, tag):
@@ -143,3 +147,19 @@ def test_prefill_every_scan_slice_width(B, Nqk, Nv):
     lens = [150 + 37 * i for i in range(B)]
     inp = workloads.prefill_inputs(60 + B, lens, Nqk=Nqk, Nv=Nv, act="bf16")
     check_parity(inp, f"B={B} Nv={Nv} ({B * Nv} streams)")
+
+
+@pytest.mark.parametrize("rule", ["delta", "gated", "linear"])
+def test_prefill_update_rules(rule):
+    """Update rules ("LinearAttention" page, update_rule) against the oracle,
+    with NULL gates / beta where the rule ignores them; passing them instead
+    must not change a bit."""
+    inp = workloads.prefill_inputs(80, [300, 129, 5, 0, 260], Nqk=2, Nv=4, act="bf16")
+    print(f"[prefill parity] rule {rule}", flush=True)
+    out, st = run_gpu(inp, rule=rule)
+    out_ref, st_ref = run_oracle(inp, rule=rule)
+    exc, lit = assert_out_close(out, out_ref, True, f"{rule} out")
+    es = assert_state_close(st, st_ref, f"{rule} state")
+    print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
+    out2, st2 = run_gpu(inp, rule=rule, drop_unused=False)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(st, st2)
