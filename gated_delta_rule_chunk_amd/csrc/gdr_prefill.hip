@@ -168,13 +168,6 @@ __global__ __launch_bounds__(256) void chunkmap_kernel(const int32_t* cu, Prefil
     }
 }
 
-// lower-triangular tile index n (0..35) -> (I, J) with J <= I
-__device__ __forceinline__ void tri_tile(int n, int& I, int& J) {
-    I = 0;
-    while ((I + 1) * (I + 2) / 2 <= n) ++I;
-    J = n - I * (I + 1) / 2;
-}
-
 // Transposed fp16 tiles ([col][tok] or [dk][tok]) are stored with the 16-byte
 // group index XOR-swizzled by the row's 8-row block, so that both the
 // transposing 16-byte writes and the MFMA fragment reads are free of LDS bank
@@ -415,24 +408,41 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
 
     // ---- 2. Gram k^ k^T on the lower 16-tiles -> L (fp16 in sL, diagonal
     //         blocks also fp32 in sD); zeros above the block diagonal of sL;
-    //         k^ read back transposed (8 tokens x 4 dk per thread)
-    for (int n = wave; n < 36; n += 8) {
-        int I, J;
-        tri_tile(n, I, J);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        if constexpr (Rule<RULE>::delta) {
+    //         k^ read back transposed (8 tokens x 4 dk per thread).
+    //         Waves take whole tile rows so that a row's A fragments load
+    //         once: rows pair up as (pp, 7 - pp); wave 2 pp takes row pp and
+    //         the first 4 - pp tiles of row 7 - pp, wave 2 pp + 1 the other
+    //         four tiles of row 7 - pp (4 or 5 tiles per wave).  Row-major k^
+    //         is already in the B-fragment layout of k^T.
+    {
+        auto gram_row = [&](int I, int J0, int J1) {
+            half8 a[4];
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                acc = mma(ld_h8(&sA[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
-                          ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
-        }
-        const int j = 16 * J + lr;
+            for (int ks = 0; ks < 4; ++ks) a[ks] = ld_h8(&sA[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
+            for (int J = J0; J < J1; ++J) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if constexpr (Rule<RULE>::delta) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * lq + e;
-            const float Lij = (Rule<RULE>::delta && i > j) ? sBeta[i] * acc[e] * __expf(sGc[i] - sGc[j]) : 0.f;
-            sL[i * LD16 + j] = (_Float16)Lij;
-            if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
+                    for (int ks = 0; ks < 4; ++ks)
+                        acc = mma(a[ks], ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+                }
+                const int j = 16 * J + lr;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int i = 16 * I + 4 * lq + e;
+                    const float Lij =
+                        (Rule<RULE>::delta && i > j) ? sBeta[i] * acc[e] * __expf(sGc[i] - sGc[j]) : 0.f;
+                    sL[i * LD16 + j] = (_Float16)Lij;
+                    if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
+                }
+            }
+        };
+        const int pp = wave >> 1;
+        if (wave & 1) {
+            gram_row(7 - pp, 4 - pp, 8 - pp);
+        } else {
+            gram_row(pp, 0, pp + 1);
+            gram_row(7 - pp, 0, 4 - pp);
         }
     }
     {
@@ -529,19 +539,23 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
 
     // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk], fragment order  (lower-triangular K
     //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
+    //         The wave's four output tiles share each B fragment (row Jt of T).
     const int pr = wave & 3, hsel = wave >> 2;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const int Jt = which ? 7 - pr : pr;
+        f32x4 acc[4];
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) {
-            const int It = 4 * hsel + ii;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= Jt / 2; ++ks)
-                acc = mma(ld_h8(&sA[sw(16 * It + lr, 32 * ks + 8 * lq)]),
-                          ld_h8(&sL[(16 * Jt + lr) * LD16 + 32 * ks + 8 * lq]), acc);
-            st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * It + 4 * lq), to_h4(acc));
+        for (int ii = 0; ii < 4; ++ii) acc[ii] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks <= Jt / 2; ++ks) {
+            const half8 b = ld_h8(&sL[(16 * Jt + lr) * LD16 + 32 * ks + 8 * lq]);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                acc[ii] = mma(ld_h8(&sA[sw(16 * (4 * hsel + ii) + lr, 32 * ks + 8 * lq)]), b, acc[ii]);
         }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * (4 * hsel + ii) + 4 * lq), to_h4(acc[ii]));
     }
     __syncthreads();
 
@@ -561,18 +575,22 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     __syncthreads();
 
     // ---- 8. u = T (v beta) -> u, fragment order
+    //         The wave's four output tiles share each A fragment (row I of T).
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const int I = which ? 7 - pr : pr;
+        f32x4 acc[4];
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            const int J = 4 * hsel + jj;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int ks = 0; ks <= I / 2; ++ks)
-                acc = mma(ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]),
-                          ld_h8(&sA[sw(16 * J + lr, 32 * ks + 8 * lq)]), acc);
-            st_h4(p.u + ch * TILE + cfrag_off(16 * I + 4 * lq, 16 * J + lr), to_h4(acc));
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks <= I / 2; ++ks) {
+            const half8 a = ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                acc[jj] = mma(a, ld_h8(&sA[sw(16 * (4 * hsel + jj) + lr, 32 * ks + 8 * lq)]), acc[jj]);
         }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            st_h4(p.u + ch * TILE + cfrag_off(16 * I + 4 * lq, 16 * (4 * hsel + jj) + lr), to_h4(acc[jj]));
     }
 }
 
