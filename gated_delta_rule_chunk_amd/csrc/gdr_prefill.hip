@@ -176,6 +176,18 @@ __device__ __forceinline__ int sw(int r, int c) {
     return r * LD16 + ((((c >> 3) ^ (r >> 3)) & 15) << 3) + (c & 7);
 }
 
+// Workgroup ids are dispatched round-robin over the 8 XCDs (id mod 8), each
+// with its own L2.  group_slot(id, G) renumbers them so that the G
+// consecutive slots of one qk-head group -- items (chunk, value head) that
+// read the same k and q rows -- run on one XCD, one after the other, and the
+// second read hits that L2:
+//   slot = ((id / 8) / G * 8 + id % 8) * G + (id / 8) % G,
+// a bijection on [0, n) for n a multiple of 8 G (launches round up to one).
+__device__ __forceinline__ int group_slot(int id, int G) {
+    const int x = id & 7, j = id >> 3;
+    return ((j / G) * 8 + x) * G + j % G;
+}
+
 // Workspace tiles that are written or read straight from MFMA registers are
 // stored in the order of those registers, so that every such access is
 // 512 B - 1 KiB contiguous (whole cache lines):
@@ -607,8 +619,8 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int c4 = tid & 31, tg = tid >> 5;
     const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
-    const int stride = gridDim.x;
-    int it = blockIdx.x;
+    const int stride = gridDim.x;   // a multiple of 8 G
+    int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
     if (it >= n_items) return;
     if constexpr (sizeof(ActT) == 2) {
         IntraStage<ActT> A, B;
@@ -871,7 +883,8 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     __shared__ float sG[128];   // g_cum of the chunk
 
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
-    const int c = blockIdx.x / Nv, h = blockIdx.x % Nv, hq = h / G;
+    const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
+    const int c = item / Nv, h = item % Nv, hq = h / G;
     if (c >= ld_uniform(&p.meta[p.B])) return;
     const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
@@ -1032,7 +1045,8 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
     const size_t nwg = (size_t)lay.nc * a.Nv;
     if (nwg > 0) {
         // persistent: two workgroups per CU (LDS < 80 KiB each), each walking items
-        const size_t nint = nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu;
+        const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
+        const size_t nint = ((nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu) + g8 - 1) / g8 * g8;
         timing_begin(kIntra, stream);
         launch_intra(a.rule, act_bf16, dim3((unsigned)nint), stream, p);
         timing_end(kIntra, stream);
@@ -1058,8 +1072,10 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nwg > 0) {
         timing_begin(kOutput, stream);
-        if (act_bf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
-        else hipLaunchKernelGGL(output_kernel<float>, dim3((unsigned)nwg), dim3(512), 0, stream, p);
+        const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
+        const unsigned nout = (unsigned)((nwg + g8 - 1) / g8 * g8);
+        if (act_bf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+        else hipLaunchKernelGGL(output_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
         timing_end(kOutput, stream);
         e = hipGetLastError();
     }
