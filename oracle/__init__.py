@@ -60,6 +60,8 @@ def _load():
         lib.gdr_oracle_decode.restype = i
         lib.gdr_oracle_round_bf16.argtypes = [ctypes.c_double]
         lib.gdr_oracle_round_bf16.restype = ctypes.c_double
+        lib.gdr_oracle_round_fp16.argtypes = [ctypes.c_double]
+        lib.gdr_oracle_round_fp16.restype = ctypes.c_double
         lib.gdr_oracle_num_threads.argtypes = []
         lib.gdr_oracle_num_threads.restype = i
         _lib = lib
@@ -105,6 +107,13 @@ def round_bf16(x):
     return np.vectorize(f, otypes=[np.float64])(x) if x.size else x.copy()
 
 
+def round_fp16(x):
+    """Round float64 values to the nearest IEEE half (ties to even), as float64."""
+    f = _load().gdr_oracle_round_fp16
+    x = np.asarray(x, dtype=np.float64)
+    return np.vectorize(f, otypes=[np.float64])(x) if x.size else x.copy()
+
+
 RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
 
 
@@ -135,7 +144,7 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, rule="gated_delta"):
 
 
 def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False, num_accepted=None,
-           rule="gated_delta"):
+           rule="gated_delta", round_state=None):
     """Recurrent decode over a slot pool.
 
     q, k [B,Nk,S,Dk] (caller-normalised); v [B,Nv,S,Dv]; g, beta [B,Nv,S];
@@ -159,7 +168,8 @@ def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False,
     rc = _load().gdr_oracle_decode(_dp(q), _dp(k), _dp(v), _dp(g), _dp(gk), _dp(beta),
                                    _dp(pool), _dp(pool_out), slots, _ip(idx), _ip(lens), _ip(nacc),
                                    B, S, Nk, Nv, Dk, Dv, float(scale),
-                                   1 if round_state_bf16 else 0, RULES[rule], _dp(out))
+                                   {None: 0, "bf16": 1, "fp16": 2}["bf16" if round_state_bf16 else round_state],
+                                   RULES[rule], _dp(out))
     if rc != 0:
         raise ValueError(f"oracle decode rejected its arguments (rc={rc})")
     return out, pool_out

@@ -71,6 +71,26 @@ double gdr_oracle_round_bf16(double x)
     return ldexp(m, e);
 }
 
+/* Round a double to the nearest IEEE binary16 value (11 significant bits,
+ * ties to even; subnormals below 2^-14 in steps of 2^-24; magnitudes that
+ * round past 65504 become infinite), returned as a double.  Used only to
+ * state what an fp16 state pool stores after an exact update. */
+double gdr_oracle_round_fp16(double x)
+{
+    if (x == 0.0 || !isfinite(x)) return x;
+    const double ax = fabs(x);
+    double r;
+    if (ax < ldexp(1.0, -14)) {
+        r = nearbyint(ax * ldexp(1.0, 24)) * ldexp(1.0, -24);
+    } else {
+        int e;
+        const double m = frexp(ax, &e);          /* ax = m * 2^e, 0.5 <= m < 1 */
+        r = ldexp(nearbyint(m * 2048.0) / 2048.0, e);
+        if (r > 65504.0) r = INFINITY;
+    }
+    return x < 0 ? -r : r;
+}
+
 /* One token of the recurrence on an fp64 state S [Dk][Dv] (row-major).
  *   decay_row[i] = exp(g) * exp(gk[i]) (precomputed by the caller; 1 for
  *   rules without a gate)
@@ -183,9 +203,9 @@ int gdr_oracle_prefill(const double *q, const double *k, const double *v,
  *               parameter list: the tokens accepted, not rejected, in
  *               speculative decoding; equal to the valid length in ordinary
  *               inference).  NULL means 1 for every row.
- *   round_bf16: if nonzero, what is stored into pool_out is the bf16 rounding
- *               of the exact state (what a bf16 pool holds); the token chain
- *               itself stays exact.
+ *   round_mode: 1 (2): what is stored into pool_out is the bf16 (fp16)
+ *               rounding of the exact state (what such a pool holds); 0
+ *               stores it exactly.  The token chain itself stays exact.
  *   out       [B][Nv][S][Dv]
  *   rule      update rule 0..3 (see above)
  *
@@ -206,7 +226,7 @@ int gdr_oracle_decode(const double *q, const double *k, const double *v,
                       const double *pool_in, double *pool_out, int num_slots,
                       const int32_t *idx, const int32_t *lens, const int32_t *num_accepted,
                       int B, int S, int Nk, int Nv, int Dk, int Dv,
-                      double scale, int round_bf16, int rule, double *out)
+                      double scale, int round_mode, int rule, double *out)
 {
     if (B < 1 || S < 1 || Nk < 1 || Nv < 1 || Dk < 1 || Dv < 1 || Nv % Nk || num_slots < 1 ||
         rule < 0 || rule > 3)
@@ -247,7 +267,8 @@ int gdr_oracle_decode(const double *q, const double *k, const double *v,
                            out + tv * Dv, kv);
                 double *dst = pool_out + ((size_t)idx[b * S + t] * Nv + h) * slab;
                 for (size_t e = 0; e < slab; ++e)
-                    dst[e] = round_bf16 ? gdr_oracle_round_bf16(Sm[e]) : Sm[e];
+                    dst[e] = round_mode == 1 ? gdr_oracle_round_bf16(Sm[e])
+                           : round_mode == 2 ? gdr_oracle_round_fp16(Sm[e]) : Sm[e];
             }
         }
         free(Sm);

@@ -205,6 +205,19 @@ def test_round_bf16_matches_torch_on_fp32_values():
     assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
 
 
+def test_round_fp16_matches_numpy_half():
+    """numpy's float64 -> float16 cast is a single RNE rounding (normals,
+    subnormals, overflow to infinity)."""
+    rng = np.random.default_rng(18)
+    x = np.concatenate([rng.standard_normal(20000), rng.standard_normal(2000) * 1e-5,
+                        rng.standard_normal(2000) * 3e4, [65504.0, 65519.0, 65520.0, 1e-8, 2.0 ** -25,
+                                                          3 * 2.0 ** -25, 1 + 2.0 ** -11, 1 + 3 * 2.0 ** -11]])
+    x = np.concatenate([x, -x])
+    with np.errstate(over="ignore"):   # the overflow to infinity is part of the check
+        ref = x.astype(np.float16).astype(np.float64)
+    assert np.isinf(ref).any() and np.array_equal(oracle.round_fp16(x), ref)
+
+
 # ---------------------------------------------------------------- invariants
 
 def test_gqa_equals_replicated_heads():
