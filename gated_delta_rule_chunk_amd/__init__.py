@@ -32,6 +32,7 @@ GDR_ERR_WORKSPACE = 4
 GDR_ERR_HIP = 5
 GDR_FP32 = 0
 GDR_BF16 = 1
+GDR_FP16 = 2
 
 # Every symbol include/gdr.h declares, with its ctypes signature.
 _vp = ctypes.c_void_p
@@ -86,12 +87,12 @@ def check(status: int, what: str) -> None:
     raise RuntimeError(msg)
 
 
-_DT = {torch.bfloat16: GDR_BF16, torch.float32: GDR_FP32}
+_DT = {torch.bfloat16: GDR_BF16, torch.float32: GDR_FP32, torch.float16: GDR_FP16}
 
 
 def _act(t: torch.Tensor, name: str) -> int:
     if t.dtype not in _DT:
-        raise RuntimeError(f"{name}: dtype {t.dtype} not supported (bfloat16 or float32)")
+        raise RuntimeError(f"{name}: dtype {t.dtype} not supported (bfloat16, float16 or float32)")
     return _DT[t.dtype]
 
 

@@ -110,8 +110,8 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
                              void* workspace, size_t workspace_bytes, void* hip_stream) {
     gdr_status s = check_prefill_sizes(T, B, Nqk, Nv, D);
     if (s != GDR_OK) return s;
-    if (act != GDR_BF16 && act != GDR_FP32)
-        return fail(GDR_ERR_DTYPE, "activation dtype must be GDR_BF16 or GDR_FP32 (got %d)", (int)act);
+    if (act != GDR_BF16 && act != GDR_FP32 && act != GDR_FP16)
+        return fail(GDR_ERR_DTYPE, "activation dtype must be GDR_BF16, GDR_FP16 or GDR_FP32 (got %d)", (int)act);
     if (!rule_ok(rule)) return fail(GDR_ERR_INVALID_ARGUMENT, "unknown update rule %d", (int)rule);
     if (!cu_seqlens || !state_out)
         return fail(GDR_ERR_INVALID_ARGUMENT, "cu_seqlens and state_out must not be NULL");
@@ -125,7 +125,7 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
                     workspace_bytes, workspace);
     gdr::PrefillArgs a{q, k, v, g, beta, state_in, cu_seqlens, out, state_out,
                        static_cast<char*>(workspace), T, B, Nqk, Nv, scale, (int32_t)rule};
-    return from_hip(gdr::prefill_launch(a, lay, act == GDR_BF16, static_cast<hipStream_t>(hip_stream)),
+    return from_hip(gdr::prefill_launch(a, lay, (int)act, static_cast<hipStream_t>(hip_stream)),
                     "prefill launch");
 }
 
@@ -147,8 +147,9 @@ gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, con
     if (Dk != 64 && Dk != 128) return fail(GDR_ERR_UNSUPPORTED, "decode supports Dk in {64, 128} (got %d)", Dk);
     if (Dv != 64 && Dv != 128 && Dv != 256 && Dv != 512)
         return fail(GDR_ERR_UNSUPPORTED, "decode supports Dv in {64, 128, 256, 512} (got %d)", Dv);
-    if ((act != GDR_BF16 && act != GDR_FP32) || (state_dtype != GDR_BF16 && state_dtype != GDR_FP32))
-        return fail(GDR_ERR_DTYPE, "dtypes must be GDR_BF16 or GDR_FP32 (act=%d, state=%d)", (int)act,
+    auto dt_ok = [](gdr_dtype d) { return d == GDR_BF16 || d == GDR_FP32 || d == GDR_FP16; };
+    if (!dt_ok(act) || !dt_ok(state_dtype))
+        return fail(GDR_ERR_DTYPE, "dtypes must be GDR_BF16, GDR_FP16 or GDR_FP32 (act=%d, state=%d)", (int)act,
                     (int)state_dtype);
     if (!rule_ok(rule)) return fail(GDR_ERR_INVALID_ARGUMENT, "unknown update rule %d", (int)rule);
     if (!q || !k || !v || !state_pool || !ssm_state_indices || !actual_seq_lengths || !out ||
@@ -160,7 +161,7 @@ gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, con
         return fail(GDR_ERR_INVALID_ARGUMENT, "B * Nv too large");
     gdr::DecodeArgs a{q, k, v, g, gk, beta, state_pool, ssm_state_indices, actual_seq_lengths,
                       num_accepted_tokens, out, num_slots, B, S, Nk, Nv, Dk, Dv, scale, (int32_t)rule};
-    return from_hip(gdr::decode_launch(a, act == GDR_BF16, state_dtype == GDR_BF16,
+    return from_hip(gdr::decode_launch(a, (int)act, (int)state_dtype,
                                        static_cast<hipStream_t>(hip_stream)),
                     "decode launch");
 }

@@ -213,11 +213,17 @@ static hipError_t launch_dk(const DecodeArgs& a, hipStream_t stream) {
     return launch_dv<128, ActT, StT>(a, stream);
 }
 
-hipError_t decode_launch(const DecodeArgs& a, bool act_bf16, bool state_bf16, hipStream_t stream) {
-    if (act_bf16) {
-        return state_bf16 ? launch_dk<uint16_t, uint16_t>(a, stream) : launch_dk<uint16_t, float>(a, stream);
-    }
-    return state_bf16 ? launch_dk<float, uint16_t>(a, stream) : launch_dk<float, float>(a, stream);
+template <typename ActT>
+static hipError_t launch_st(const DecodeArgs& a, int st, hipStream_t stream) {
+    if (st == kActBf16) return launch_dk<ActT, uint16_t>(a, stream);
+    if (st == kActFp16) return launch_dk<ActT, _Float16>(a, stream);
+    return launch_dk<ActT, float>(a, stream);
+}
+
+hipError_t decode_launch(const DecodeArgs& a, int act, int st, hipStream_t stream) {
+    if (act == kActBf16) return launch_st<uint16_t>(a, st, stream);
+    if (act == kActFp16) return launch_st<_Float16>(a, st, stream);
+    return launch_st<float>(a, st, stream);
 }
 
 }  // namespace gdr

@@ -93,8 +93,39 @@ __device__ __forceinline__ void store8_nt(float* p, const float (&x)[8]) {
     __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(p + 4));
 }
 
-// Scalar load of one element of either dtype.
+// Scalar load of one element of any activation dtype.
 __device__ __forceinline__ float load1(const uint16_t* p) { return bf16_to_f32(*p); }
 __device__ __forceinline__ float load1(const float* p) { return *p; }
+__device__ __forceinline__ float load1(const _Float16* p) { return (float)*p; }
+
+// ---- IEEE half (fp16) activations and state: one 16-byte access per 8 ----
+__device__ __forceinline__ void load8(const _Float16* p, float (&x)[8]) {
+    const half8 r = *reinterpret_cast<const half8*>(p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)r[i];
+}
+__device__ __forceinline__ void store8(_Float16* p, const float (&x)[8]) {
+    half8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = (_Float16)x[i];   // round to nearest even
+    *reinterpret_cast<half8*>(p) = r;
+}
+__device__ __forceinline__ void load4(const _Float16* p, float (&x)[4]) {
+    const half4 r = *reinterpret_cast<const half4*>(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = (float)r[i];
+}
+__device__ __forceinline__ void load8_nt(const _Float16* p, float (&x)[8]) {
+    const u32x4 r = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    const half8 h = __builtin_bit_cast(half8, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+}
+__device__ __forceinline__ void store8_nt(_Float16* p, const float (&x)[8]) {
+    half8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (_Float16)x[i];
+    __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h), reinterpret_cast<u32x4*>(p));
+}
 
 }  // namespace gdr

@@ -35,7 +35,11 @@ struct DecodeArgs {
     int32_t rule;          // update rule code (0 gated_delta, 1 delta, 2 gated, 3 linear)
 };
 
-hipError_t decode_launch(const DecodeArgs& a, bool act_bf16, bool state_bf16, hipStream_t stream);
+// Element dtype codes (the values of gdr_dtype): fp32, bf16 (stored as
+// uint16_t bit patterns), IEEE half (_Float16).
+constexpr int kActFp32 = 0, kActBf16 = 1, kActFp16 = 2;
+
+hipError_t decode_launch(const DecodeArgs& a, int act, int state, hipStream_t stream);
 
 // ---------------------------------------------------------------- prefill
 //
@@ -78,7 +82,7 @@ struct PrefillArgs {
     int32_t rule;          // update rule code (0 gated_delta, 1 delta, 2 gated, 3 linear)
 };
 
-hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool act_bf16,
+hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int act,
                           hipStream_t stream);
 
 }  // namespace gdr

@@ -232,9 +232,11 @@ __device__ __forceinline__ int32_t ld_uniform(const int32_t* ptr) {
 // until the data is used.
 template <typename ActT> struct Raw8;
 template <> struct Raw8<uint16_t> { u32x4 d; };
+template <> struct Raw8<_Float16> { u32x4 d; };
 template <> struct Raw8<float> { f32x4 a, b; };
 template <typename ActT> struct Raw4;
 template <> struct Raw4<uint16_t> { u32x2 d; };
+template <> struct Raw4<_Float16> { u32x2 d; };
 template <> struct Raw4<float> { f32x4 d; };
 
 __device__ __forceinline__ void raw_load(Raw8<uint16_t>& x, const uint16_t* p) { x.d = *reinterpret_cast<const u32x4*>(p); }
@@ -243,6 +245,18 @@ __device__ __forceinline__ void raw_load(Raw8<float>& x, const float* p) {
     x.b = *reinterpret_cast<const f32x4*>(p + 4);
 }
 __device__ __forceinline__ void raw_load(Raw4<uint16_t>& x, const uint16_t* p) { x.d = *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void raw_load(Raw8<_Float16>& x, const _Float16* p) { x.d = *reinterpret_cast<const u32x4*>(p); }
+__device__ __forceinline__ void raw_load(Raw4<_Float16>& x, const _Float16* p) { x.d = *reinterpret_cast<const u32x2*>(p); }
+__device__ __forceinline__ void raw_cvt(const Raw8<_Float16>& x, float (&y)[8]) {
+    const half8 h = __builtin_bit_cast(half8, x.d);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = (float)h[i];
+}
+__device__ __forceinline__ void raw_cvt(const Raw4<_Float16>& x, float (&y)[4]) {
+    const half4 h = __builtin_bit_cast(half4, x.d);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) y[i] = (float)h[i];
+}
 __device__ __forceinline__ void raw_load(Raw4<float>& x, const float* p) { x.d = *reinterpret_cast<const f32x4*>(p); }
 __device__ __forceinline__ void raw_zero(Raw8<uint16_t>& x) { x.d = u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ void raw_zero(Raw8<float>& x) { x.a = f32x4{0.f, 0.f, 0.f, 0.f}; x.b = x.a; }
@@ -1008,20 +1022,21 @@ static int compute_units() {
 }
 
 template <int RULE>
-static void launch_intra_rule(bool act_bf16, dim3 grid, hipStream_t stream, const PrefillDev& p) {
-    if (act_bf16) hipLaunchKernelGGL((intra_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
+static void launch_intra_rule(int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+    if (act == kActBf16) hipLaunchKernelGGL((intra_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
+    else if (act == kActFp16) hipLaunchKernelGGL((intra_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
     else hipLaunchKernelGGL((intra_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
 }
-static void launch_intra(int rule, bool act_bf16, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+static void launch_intra(int rule, int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
     switch (rule) {
-        case 1: launch_intra_rule<1>(act_bf16, grid, stream, p); break;
-        case 2: launch_intra_rule<2>(act_bf16, grid, stream, p); break;
-        case 3: launch_intra_rule<3>(act_bf16, grid, stream, p); break;
-        default: launch_intra_rule<0>(act_bf16, grid, stream, p); break;
+        case 1: launch_intra_rule<1>(act, grid, stream, p); break;
+        case 2: launch_intra_rule<2>(act, grid, stream, p); break;
+        case 3: launch_intra_rule<3>(act, grid, stream, p); break;
+        default: launch_intra_rule<0>(act, grid, stream, p); break;
     }
 }
 
-hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool act_bf16, hipStream_t stream) {
+hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int act, hipStream_t stream) {
     const int ncu = compute_units();
     PrefillDev p;
     p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
@@ -1048,7 +1063,7 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         const size_t nint = ((nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu) + g8 - 1) / g8 * g8;
         timing_begin(kIntra, stream);
-        launch_intra(a.rule, act_bf16, dim3((unsigned)nint), stream, p);
+        launch_intra(a.rule, act, dim3((unsigned)nint), stream, p);
         timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1074,7 +1089,8 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, bool a
         timing_begin(kOutput, stream);
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         const unsigned nout = (unsigned)((nwg + g8 - 1) / g8 * g8);
-        if (act_bf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+        if (act == kActBf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+        else if (act == kActFp16) hipLaunchKernelGGL(output_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
         else hipLaunchKernelGGL(output_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
         timing_end(kOutput, stream);
         e = hipGetLastError();

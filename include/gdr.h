@@ -56,9 +56,13 @@ typedef enum gdr_status {
 } gdr_status;
 
 /* Element types of activation and state tensors. */
+/* Element dtypes.  GDR_FP16 is IEEE binary16 (the LinearAttention page
+ * allows float16 or float32 activations and state); GDR_BF16 is the
+ * recurrent_gated_delta_rule page's dtype. */
 typedef enum gdr_dtype {
     GDR_FP32 = 0,
-    GDR_BF16 = 1
+    GDR_BF16 = 1,
+    GDR_FP16 = 2
 } gdr_dtype;
 
 /* State update rule ("LinearAttention" contrib-operator page, attribute
@@ -122,7 +126,7 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  *   scale                     multiplies the normalised q (e.g. 1/sqrt(D))
  *   rule                      update rule; g may be NULL without a gate,
  *                             beta without the delta term
- *   act                       GDR_BF16 or GDR_FP32 (q, k, v, beta, out)
+ *   act                       GDR_BF16, GDR_FP16 or GDR_FP32 (q, k, v, beta, out)
  *   out         [T, Nv, D]    act dtype
  *   state_out   [B, Nv, D, D] fp32; may be the same pointer as state_in
  *   workspace   device memory of at least the size the query returns
@@ -176,8 +180,8 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
  *   scale               multiplies q before use (the page's scale_value)
  *   rule                update rule (see gdr_update_rule); g may be NULL
  *                       without a gate, beta without the delta term
- *   act                 GDR_BF16 or GDR_FP32 (q, k, v, beta, out)
- *   state_dtype         GDR_BF16 (the page's pool) or GDR_FP32
+ *   act                 GDR_BF16, GDR_FP16 or GDR_FP32 (q, k, v, beta, out)
+ *   state_dtype         GDR_BF16 (the page's pool), GDR_FP16 or GDR_FP32
  *   out                 [B, Nv, S, Dv]  act dtype
  * Out-of-range slot indices are not checked on the host (they live on the
  * device); a token whose slot is out of range stores nothing, and a chain

@@ -114,7 +114,7 @@ def test_decode_host_validation():
     assert decode_call(slots=0) == E.GDR_ERR_INVALID_ARGUMENT
     assert decode_call(Dk=96) == E.GDR_ERR_UNSUPPORTED
     assert decode_call(Dv=100) == E.GDR_ERR_UNSUPPORTED
-    assert decode_call(act=2) == E.GDR_ERR_DTYPE
+    assert decode_call(act=3) == E.GDR_ERR_DTYPE
     assert decode_call(st=5) == E.GDR_ERR_DTYPE
     assert decode_call(idx=None) == E.GDR_ERR_INVALID_ARGUMENT
     assert decode_call(pool=None) == E.GDR_ERR_INVALID_ARGUMENT

@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_chunk_amd as gdr
 import oracle
 import workloads
-from parity import assert_out_close, assert_state_close, to_f64
+from parity import assert_out_close, assert_state_close, out_kind, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -28,9 +28,9 @@ def run_gpu(inp, pool=None, rule="gated_delta"):
 
 def run_oracle(inp, pool=None, rule="gated_delta"):
     pool = inp["pool"] if pool is None else pool
-    bf16_pool = pool.dtype == torch.bfloat16
+    rnd = {torch.bfloat16: "bf16", torch.float16: "fp16"}.get(pool.dtype)
     return oracle.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["gk"], inp["beta"], pool,
-                         inp["idx"], inp["lens"], inp["scale"], round_state_bf16=bf16_pool,
+                         inp["idx"], inp["lens"], inp["scale"], round_state=rnd,
                          num_accepted=inp.get("nacc"), rule=rule)
 
 
@@ -44,21 +44,20 @@ def check_parity(inp, tag, rule="gated_delta"):
     print(f"[decode parity] {tag}", flush=True)
     out, pool = run_gpu(inp, rule=rule)
     out_ref, pool_ref = run_oracle(inp, rule=rule)
-    bf16_out = out.dtype == torch.bfloat16
     lens = inp["lens"].numpy()
     valid = np.zeros(out.shape, bool)
     for b in range(inp["B"]):
         valid[b, :, :lens[b]] = True
-    exc, lit = assert_out_close(to_f64(out)[valid], out_ref[valid], bf16_out, f"{tag} out")
+    exc, lit = assert_out_close(to_f64(out)[valid], out_ref[valid], out_kind(out), f"{tag} out")
     # padded token rows are zeros
     assert not torch.any(out[torch.from_numpy(~valid)] != 0)
     ws = written_slots(inp)
     es = assert_state_close(to_f64(pool)[ws], pool_ref[ws], f"{tag} state")
     # every slot no token writes keeps its exact bits
     untouched = sorted(set(range(inp["num_slots"])) - set(ws))
-    assert torch.equal(pool[untouched].view(torch.int16) if pool.dtype == torch.bfloat16 else pool[untouched],
-                       inp["pool"][untouched].view(torch.int16) if pool.dtype == torch.bfloat16
-                       else inp["pool"][untouched])
+    two_byte = pool.element_size() == 2
+    assert torch.equal(pool[untouched].view(torch.int16) if two_byte else pool[untouched],
+                       inp["pool"][untouched].view(torch.int16) if two_byte else inp["pool"][untouched])
     print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
 
 
@@ -178,3 +177,12 @@ def test_decode_update_rules(rule):
     inp = workloads.decode_inputs(90, B=12, S=3, Nk=2, Nv=4, Dk=128, Dv=128, num_slots=30, with_gk=True,
                                   lens="random", routing="two_slots")
     check_parity(inp, f"rule {rule}", rule=rule)
+
+
+@pytest.mark.parametrize("act,state", [("fp16", "fp16"), ("fp16", "fp32"), ("bf16", "fp16")])
+def test_decode_fp16_activations_and_state(act, state):
+    """IEEE half activations and/or state pool (the LinearAttention page
+    allows float16 for both)."""
+    inp = workloads.decode_inputs(95, B=10, S=3, Nk=2, Nv=4, Dk=128, Dv=128, num_slots=25, with_gk=True,
+                                  lens="random", routing="two_slots", act=act, state=state)
+    check_parity(inp, f"act {act} state {state}")

@@ -6,7 +6,7 @@ import torch
 import gated_delta_rule_chunk_amd as gdr
 import oracle
 import workloads
-from parity import assert_out_close, assert_state_close, to_f64
+from parity import assert_out_close, assert_state_close, out_kind, to_f64
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -34,7 +34,7 @@ def check_parity(inp, tag):
     print(f"[prefill parity] {tag}", flush=True)
     out, st = run_gpu(inp)
     out_ref, st_ref = run_oracle(inp)
-    exc, lit = assert_out_close(out, out_ref, out.dtype == torch.bfloat16, f"{tag} out")
+    exc, lit = assert_out_close(out, out_ref, out_kind(out), f"{tag} out")
     es = assert_state_close(st, st_ref, f"{tag} state")
     print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
     return out, st
@@ -163,3 +163,9 @@ def test_prefill_update_rules(rule):
     print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
     out2, st2 = run_gpu(inp, rule=rule, drop_unused=False)
     assert torch.equal(out.view(torch.int16), out2.view(torch.int16)) and torch.equal(st, st2)
+
+
+def test_prefill_fp16_activations():
+    """IEEE half activations (the LinearAttention page allows float16)."""
+    inp = workloads.prefill_inputs(85, [300, 129, 77], Nqk=2, Nv=4, act="fp16")
+    check_parity(inp, "fp16 activations")

@@ -26,7 +26,7 @@ import torch
 
 SCALE_128 = 1.0 / math.sqrt(128.0)
 
-_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+_TORCH_DTYPE = {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}
 
 
 def _cast(x: np.ndarray, dtype: str) -> torch.Tensor:
