@@ -91,8 +91,8 @@ def bytes_decode(inp):
     distinct written slab once, plus the valid tokens' activations."""
     import numpy as np
     B, S, Nk, Nv, Dk, Dv = (inp[k] for k in ("B", "S", "Nk", "Nv", "Dk", "Dv"))
-    sb = 2 if inp["state"] == "bf16" else 4
-    ab = 2 if inp["act"] == "bf16" else 4
+    sb = 4 if inp["state"] == "fp32" else 2
+    ab = 4 if inp["act"] == "fp32" else 2
     idx = inp["idx"].numpy().reshape(B, S)
     lens = inp["lens"].numpy()
     slab = Nv * Dk * Dv * sb

@@ -26,7 +26,7 @@
 
 namespace gdr {
 
-template <int DK, int CW, typename ActT, typename StT>
+template <int DK, int CW, typename ActT, typename StT, bool ANY_RULE>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     constexpr int NT = 256;
     constexpr int WAVES = NT / 64;
@@ -89,8 +89,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 
     // update rule ("LinearAttention" page, update_rule): the delta and linear
-    // rules have no decay, the gated and linear rules no delta term
-    const bool gated = a.rule == 0 || a.rule == 2, delta = a.rule == 0 || a.rule == 1;
+    // rules have no decay, the gated and linear rules no delta term.  The
+    // gated delta rule is compiled without the run-time choice (ANY_RULE
+    // false): the choice costs registers and about a tenth of the bandwidth.
+    const bool gated = !ANY_RULE || a.rule == 0 || a.rule == 2;
+    const bool delta = !ANY_RULE || a.rule == 0 || a.rule == 1;
+    // without the delta term, d = v: kv enters with weight 0 and beta is 1
+    // (branch-free, so the token loop is not duplicated per rule)
+    const float kvw = delta ? 1.f : 0.f;
 
     // per-token key rows, scaled query rows and row decays -> LDS
     for (int e = tid; e < len * DK; e += NT) {
@@ -161,7 +167,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
         float d[8], o[8];
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
-            d[c] = delta ? bt * (vv[c] - kv[c]) : vv[c];
+            d[c] = bt * (vv[c] - kvw * kv[c]);
             o[c] = fmaf(d[c], kq, qs[c]);
         }
 #pragma unroll
@@ -193,7 +199,8 @@ template <int DK, int CW, typename ActT, typename StT>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const size_t nwg = (size_t)a.B * a.Nv * (a.Dv / CW);
     timing_begin(kDecode, stream);
-    hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    if (a.rule == 0) hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    else hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
     timing_end(kDecode, stream);
     return hipGetLastError();
 }
