@@ -169,3 +169,22 @@ def test_prefill_fp16_activations():
     """IEEE half activations (the LinearAttention page allows float16)."""
     inp = workloads.prefill_inputs(85, [300, 129, 77], Nqk=2, Nv=4, act="fp16")
     check_parity(inp, "fp16 activations")
+
+
+@pytest.mark.parametrize("Nqk,Nv", [(2, 16), (4, 4), (1, 8)])
+def test_prefill_gqa_group_sizes(Nqk, Nv):
+    """Group sizes G = Nv / Nqk of 8, 1 and 8 with one qk head: the
+    XCD-grouped launch grids round up to multiples of 8 G."""
+    inp = workloads.prefill_inputs(90 + Nv, [333, 129, 64, 1], Nqk=Nqk, Nv=Nv, act="bf16")
+    check_parity(inp, f"Nqk={Nqk} Nv={Nv}")
+
+
+def test_prefill_many_short_sequences():
+    """300 sequences (more than one 256-wide pass of the chunk-map prefix),
+    lengths 0..200 including empty ones."""
+    rng = np.random.default_rng(99)
+    lens = rng.integers(0, 201, 300).tolist()
+    lens[5] = 0
+    lens[299] = 0
+    inp = workloads.prefill_inputs(98, lens, Nqk=1, Nv=2, act="bf16")
+    check_parity(inp, f"B=300 T={sum(lens)}")
