@@ -13,9 +13,12 @@ Timing: W untimed warm-up steps, then K steps bracketed by
 torch.cuda.synchronize() on both sides, wall clock.  Inputs rotate over
 --sets device copies (default 4, about 0.9 GB for prefill and 2 GiB of
 pools for decode) so that the 256 MB Infinity Cache cannot hold one step's
-inputs until the next.  Per-kernel durations come from hipEvents that the
-library records around each kernel on the launch stream over the timed
-region (gdr_timing_*).
+inputs until the next.  Kernel durations come from hipEvents that the
+library records around its kernels on the launch stream (gdr_timing_*).
+Each event pair delays the stream by a few microseconds, so the timed
+region records them around the dominant kernel only (its average is the
+roofline's duration); the per-kernel breakdown comes from a short untimed
+pass with every kernel's events, run before the timed region.
 
 Roofline: algorithmic flops per kernel (MFMA-bound kernels, fp16 dense peak
 2.5 PFLOP/s) or algorithmic bytes (HBM-bound decode, 8 TB/s); the formulas
@@ -121,20 +124,32 @@ def counter_traffic(kernel):
 
 
 def timed(fn, steps, warmup, gdr, torch):
+    """Warm up; take the per-kernel breakdown in an untimed pass with every
+    kernel's events; then time `steps` steps with events around the dominant
+    kernel only.  Returns (seconds, breakdown {name: (ms, launches)},
+    dominant name, its (ms, launches) over the timed region)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
     gdr.timing_read()            # discard warm-up records
+    probe = max(3, min(steps, 10))
     gdr.timing_enable(True)
+    for i in range(probe):
+        fn(warmup + i)
+    torch.cuda.synchronize()
+    gdr.timing_enable(False)
+    breakdown = {k: v for k, v in gdr.timing_read().items() if v[1]}
+    dominant = max(breakdown, key=lambda k: breakdown[k][0] / breakdown[k][1])
+    gdr.timing_enable(True, kernels=[dominant])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        fn(warmup + i)
+        fn(warmup + probe + i)
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     gdr.timing_enable(False)
-    per_kernel = gdr.timing_read()
-    return dt, per_kernel
+    live = gdr.timing_read()[dominant]
+    return dt, breakdown, dominant, live
 
 
 def roofline(name, avg_s, flops=None, nbytes=None):
@@ -163,17 +178,18 @@ def bench_prefill(args, gdr, torch, workloads):
         gdr.chunk_prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu_seqlens"], s["scale"],
                           state_in=s["state_in"], out=out, state_out=st, workspace=ws)
 
-    dt, per = timed(step, args.steps, args.warmup, gdr, torch)
+    dt, per, dominant, live = timed(step, args.steps, args.warmup, gdr, torch)
     seq_lens = [1000, 4096, 300, 2796]
     fl = flops_prefill(seq_lens, Nqk, Nv)
     kernels = {}
     for name in fl:
-        ms, n = per[name]
+        ms, n = per.get(name, (0.0, 0))
         avg = ms / 1e3 / max(n, 1)
         kernels[name] = {"avg_us": avg * 1e6, "launches": n, "alg_gflop": fl[name] / 1e9,
                          "mfma_frac": (fl[name] / avg / MFMA_PEAK_FP16) if avg > 0 and fl[name] else None}
-    dominant = max(kernels, key=lambda k: kernels[k]["avg_us"])
-    dom_avg = kernels[dominant]["avg_us"] / 1e6
+    # the dominant kernel's average over the timed region itself
+    dom_avg = live[0] / 1e3 / max(live[1], 1)
+    kernels[dominant]["avg_us_timed_region"] = dom_avg * 1e6
     step_s = dt / args.steps
     f_total = sum(fl.values())
     b_total = bytes_prefill(T, B, Nqk, Nv)
@@ -197,7 +213,7 @@ def bench_decode(args, gdr, torch, workloads):
                              s["lens"], s["scale"], out=out)
 
     steps = max(args.steps * 4, 20)
-    dt, per = timed(step, steps, args.warmup, gdr, torch)
+    dt, per, _, live = timed(step, steps, args.warmup, gdr, torch)
     # reference: a plain device copy moving the same number of bytes (half read, half written)
     nb_copy = (bytes_decode(inp) // 2 + 255) // 256 * 256
     src = torch.empty(nb_copy, dtype=torch.uint8, device=dev).fill_(1)
@@ -212,7 +228,7 @@ def bench_decode(args, gdr, torch, workloads):
     torch.cuda.synchronize()
     copy_gbs = 2 * nb_copy * 20 / (e0.elapsed_time(e1) / 1e3) / 1e9
     del src, dst
-    ms, n = per["gdr_decode"]
+    ms, n = live
     avg = ms / 1e3 / max(n, 1)
     nb = bytes_decode(inp)
     ntok = int(inp["lens"].sum())
@@ -239,7 +255,7 @@ def time_config(n, args, gdr, torch, workloads):
                                  d["lens"], d["scale"])
         ntok = int(inp["lens"].sum())
     steps = 5 if n == 5 else 20
-    dt, per = timed(f, steps, 2, gdr, torch)
+    dt, per, _, _ = timed(f, steps, 2, gdr, torch)
     return {"config": workloads.CONFIG_NAMES[n], "ms_per_call": dt / steps * 1e3, "tok_s": ntok / (dt / steps),
             "kernels_us": {k: round(v[0] / max(v[1], 1) * 1e3, 1) for k, v in per.items() if v[1]}}
 

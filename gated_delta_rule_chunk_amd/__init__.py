@@ -127,9 +127,18 @@ def _stream(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def timing_enable(on: bool = True) -> None:
-    """Record hipEvents around every kernel the library enqueues (see gdr.h)."""
-    check(lib().gdr_timing_enable(1 if on else 0), "gdr_timing_enable")
+def timing_enable(on: bool = True, kernels=None) -> None:
+    """Record hipEvents around the named kernels (every kernel if None; see gdr.h)."""
+    if not on:
+        mask = 0
+    elif kernels is None:
+        mask = -1
+    else:
+        names = [lib().gdr_timing_kernel_name(i).decode() for i in range(TIMING_KERNELS)]
+        mask = 0
+        for k in kernels:
+            mask |= 1 << names.index(k)
+    check(lib().gdr_timing_enable(mask), "gdr_timing_enable")
 
 
 def timing_read() -> dict:

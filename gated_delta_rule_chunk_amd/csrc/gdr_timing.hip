@@ -1,6 +1,6 @@
 // gdr_timing.hip -- opt-in per-kernel timing with HIP events.
 //
-// When enabled (gdr_timing_enable), every kernel the library enqueues is
+// For the kernels selected by gdr_timing_enable's mask, every launch is
 // bracketed by two hipEvents recorded on the same stream, so the durations
 // measured are those of the kernels as they run in the caller's sequence.
 // gdr_timing_read waits for the recorded events, returns the summed
@@ -21,7 +21,7 @@ struct Rec {
     hipEvent_t begin, end;
 };
 
-std::atomic<bool> g_enabled{false};
+std::atomic<int> g_mask{0};
 std::mutex g_mu;
 std::vector<Rec> g_recs;            // launches recorded since the last read
 std::vector<hipEvent_t> g_free;     // events ready for reuse
@@ -49,7 +49,7 @@ const char* kernel_name(int id) {
 }
 
 void timing_begin(int id, hipStream_t s) {
-    if (!g_enabled.load(std::memory_order_relaxed)) return;
+    if (!((g_mask.load(std::memory_order_relaxed) >> id) & 1)) return;
     hipEvent_t e = take_event();
     if (e && hipEventRecord(e, s) == hipSuccess) t_open[id] = e;
 }
@@ -68,8 +68,8 @@ void timing_end(int id, hipStream_t s) {
 
 extern "C" {
 
-gdr_status gdr_timing_enable(int enable) {
-    gdr::g_enabled.store(enable != 0);
+gdr_status gdr_timing_enable(int kernel_mask) {
+    gdr::g_mask.store(kernel_mask);
     return GDR_OK;
 }
 

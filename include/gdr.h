@@ -199,17 +199,21 @@ gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, con
 
 /* ------------------------------------------------------------------ timing
  *
- * Opt-in per-kernel timing, for benchmarks and profiling.  While enabled,
- * every kernel the library enqueues is bracketed by two hipEvents recorded
- * on the caller's stream.  gdr_timing_read waits for those events, writes
- * for each kernel id i < n the summed duration total_ms[i] and the number of
- * launches launches[i] recorded since the previous read, and forgets them.
- * Kernel ids: 0 gdr_chunkmap, 1 gdr_intra, 2 gdr_scan, 3 gdr_output (the
- * prefill kernels, in launch order) and 4 gdr_decode.  Disabled is the
- * default; the hooks then cost nothing measurable.
+ * Opt-in per-kernel timing, for benchmarks and profiling.  gdr_timing_enable
+ * takes a bit mask of kernel ids (bit i for kernel i; GDR_TIMING_ALL for
+ * every kernel, 0 to switch timing off).  Every launch of a selected kernel
+ * is bracketed by two hipEvents recorded on the caller's stream (each pair
+ * adds a few microseconds to the stream, so time only the kernels needed).
+ * gdr_timing_read waits for those events, writes for each kernel id i < n the
+ * summed duration total_ms[i] and the number of launches launches[i]
+ * recorded since the previous read, and forgets them.  Kernel ids:
+ * 0 gdr_chunkmap, 1 gdr_intra, 2 gdr_scan, 3 gdr_output (the prefill
+ * kernels, in launch order) and 4 gdr_decode.  Off is the default; the hooks
+ * then cost nothing measurable.
  */
 #define GDR_TIMING_KERNELS 5
-gdr_status gdr_timing_enable(int enable);
+#define GDR_TIMING_ALL (-1)
+gdr_status gdr_timing_enable(int kernel_mask);
 gdr_status gdr_timing_read(double *total_ms, int32_t *launches, int32_t n);
 const char *gdr_timing_kernel_name(int32_t id);
 
