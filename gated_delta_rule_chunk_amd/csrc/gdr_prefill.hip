@@ -97,6 +97,11 @@ __device__ __forceinline__ half8 ld_h8(const _Float16* p) { return *reinterpret_
 __device__ __forceinline__ void st_h8(_Float16* p, half8 v) { *reinterpret_cast<half8*>(p) = v; }
 __device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_cast<const half4*>(p); }
 __device__ __forceinline__ void st_h4(_Float16* p, half4 v) { *reinterpret_cast<half4*>(p) = v; }
+// streaming store (evict-first in the caches): for results that no workgroup of
+// the same kernel reads back, so they do not push shared operand tiles out of L2
+__device__ __forceinline__ void st_h4_nt(_Float16* p, half4 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<half4*>(p));
+}
 
 __device__ __forceinline__ half8 to_h8(const float (&x)[8]) {
     half8 h;
@@ -734,7 +739,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
     // order: straight from the accumulators, 512 B contiguous per store)
     const int tok = 16 * wv + 4 * lq;
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) st_h4(p.Sc + ch * TILE + cfrag_off(tok, col0 + 16 * ct + lr), to_h4(S[ct]));
+    for (int ct = 0; ct < CT; ++ct) st_h4_nt(p.Sc + ch * TILE + cfrag_off(tok, col0 + 16 * ct + lr), to_h4(S[ct]));
     // v_new = u - w S for tokens 16*wv + 4*lq + e
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -748,7 +753,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
             vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
         }
         const int col = 16 * ct + lr;
-        st_h4(p.vn + ch * TILE + cfrag_off(tok, col0 + col), to_h4(vn));
+        st_h4_nt(p.vn + ch * TILE + cfrag_off(tok, col0 + col), to_h4(vn));
         st_h4(&sVn[col * LD16 + tok], to_h4(vs));
     }
     if constexpr (LOAD) {
