@@ -43,7 +43,6 @@ PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
     size_t off = 0;
     L.off_meta = off;  off = align256(off + sizeof(int32_t) * ((size_t)B + 2));
     L.off_cmap = off;  off = align256(off + sizeof(int32_t) * 4 * nc);
-    L.off_khat = off;  off = align256(off + tile16 * nc * (size_t)Nqk);
     L.off_khatT = off; off = align256(off + tile16 * nc * (size_t)Nqk);
     L.off_w = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_u = off;     off = align256(off + tile16 * nc * (size_t)Nv);

@@ -53,8 +53,7 @@ struct PrefillLayout {
     int64_t nc;             // chunk bound
     size_t off_meta;        // int32 [B+2]: first chunk of each sequence, then the total
     size_t off_cmap;        // int4  [NC]: (sequence, first token, valid rows, -)
-    size_t off_khat;        // fp16  [NC][Nqk] 128 tok x 128 dk, fragment order: normalised keys
-    size_t off_khatT;       // fp16  [NC][Nqk] 128 dk x 128 tok, fragment order: the same, transposed
+    size_t off_khatT;       // fp16  [NC][Nqk] 128 dk x 128 tok, fragment order: normalised keys, transposed
     size_t off_w;           // fp16  [NC][Nv]  128 tok x 128 dk, fragment order: w = T (k^ beta e^gcum)
     size_t off_u;           // fp16  [NC][Nv]  128 tok x 128 col, fragment order: u = T (v beta)
     size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate

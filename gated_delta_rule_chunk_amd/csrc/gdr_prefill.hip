@@ -74,7 +74,6 @@ struct PrefillDev {
     float* state_out;
     int32_t* meta;
     int32_t* cmap;
-    _Float16* khat;
     _Float16* khatT;
     _Float16* w;
     _Float16* u;
@@ -365,7 +364,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     const int wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const size_t ch = (size_t)c * Nv + h;
     const size_t cq = (size_t)c * Nqk + hq;
-    const bool writes_keys = (h % G) == 0;   // one value head per group stores k^ and k^T
+    const bool writes_keys = (h % G) == 0;   // one value head per group stores k^T
     const int c4 = tid & 31, tg = tid >> 5;   // transposing layout: tokens 8*tg.., columns 4*c4..
 
     // v rows of this item (first used in step 7; the load overlaps steps 1-6).
@@ -432,7 +431,6 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
             for (int e = 0; e < 8; ++e) kx[e] = kf[ks][e] * rinv;
             const half8 kh = to_h8(kx);
             st_h8(&sA[row * LD16 + 32 * ks + 8 * lq], kh);
-            if (writes_keys) st_h8(p.khat + cq * TILE + frag_off(row, 32 * ks + 8 * lq), kh);
         }
     }
     __syncthreads();
@@ -865,22 +863,14 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
 }
 
 // ------------------------------------------------------------------ K3: output
-// 8 waves; wave w owns output rows 16w .. 16w+15.  The three 32 KiB operand
-// tiles (k^, S_c^T, v_new^T) pass one after another through one LDS buffer,
-// each fetched into registers while the previous one is in use.
-// An A-fragment-order tile, fetched in storage order (16 B per lane, 1 KiB
-// contiguous per wave) and placed row-major in LDS.
+// 8 waves; wave w owns output rows 16w .. 16w+15.  The three operand tiles
+// (k^, S_c^T, v_new^T) pass one after another through one LDS buffer.  The
+// keys are normalised here from the input rows (each wave its own 16 rows);
+// S_c and v_new are fetched into registers up front, while k^ is in use.
+// A tile fetched in storage order: 16 B per lane, 1 KiB contiguous per wave.
 __device__ __forceinline__ void frag_tile_fetch(u32x4 (&rg)[4], const _Float16* src, int tid) {
 #pragma unroll
     for (int n = 0; n < 4; ++n) rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + 512 * n) * 8);
-}
-__device__ __forceinline__ void frag_tile_store(const u32x4 (&rg)[4], _Float16* dst, int tid) {
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        int row, k;
-        frag_piece(tid + 512 * n, row, k);
-        *reinterpret_cast<u32x4*>(dst + row * LD16 + k) = rg[n];
-    }
 }
 // A C-fragment-order tile X [row][col] (fetched in storage order by
 // frag_tile_fetch) placed transposed in LDS, X^T [col][row]: each 16-byte
@@ -915,8 +905,16 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
 
     // All of the item's tiles are fetched up front (one memory latency per
     // item rather than one per phase); the q rows follow the first.
-    u32x4 stK[4], stS[4], stV[4];
-    frag_tile_fetch(stK, p.khat + ((size_t)c * Nqk + hq) * TILE, tid);
+    u32x4 stS[4], stV[4];
+    Raw8<ActT> kr[4];
+    {
+        // k rows of this wave (rows past the chunk's end re-read its last row:
+        // their entries of P lie above the diagonal or in rows never stored)
+        const ActT* K = static_cast<const ActT*>(p.k);
+        const int row = 16 * I + lr, lrow = min(row, max(r - 1, 0));
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) raw_load(kr[ks], K + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+    }
     // q^ (scaled) and q^ e^{g_cum} for rows 16 I + lr
     half8 qh[4], qe[4];
     {
@@ -933,6 +931,27 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         frag_tile_fetch(stV, p.vn + ch * TILE, tid);
         __builtin_amdgcn_sched_barrier(0);
         if (tid < 128) sG[tid] = gmine;
+        {
+            // k^ = k / |k| -> sBuf rows of this wave, [tok][dk]
+            float kx[4][8];
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) raw_cvt(kr[ks], kx[ks]);
+            float ksq = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) ksq = fmaf(kx[ks][e], kx[ks][e], ksq);
+            ksq += __shfl_xor(ksq, 16);
+            ksq += __shfl_xor(ksq, 32);
+            const float kinv = 1.f / sqrtf(ksq + kNormEps);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                float y[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) y[e] = kx[ks][e] * kinv;
+                st_h8(&sBuf[(16 * I + lr) * LD16 + 32 * ks + 8 * lq], to_h8(y));
+            }
+        }
         float ssq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
@@ -950,7 +969,6 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
             qe[ks] = to_h8(z);
         }
     }
-    frag_tile_store(stK, sBuf, tid);   // k^ [tok][dk]
     __syncthreads();
 
     // P = (q^ k^T) . D on the inclusive lower triangle -> sP rows of this wave
@@ -993,12 +1011,14 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     float* so = reinterpret_cast<float*>(&sP[16 * I * LD16]);   // 16 x 68 floats
 #pragma unroll
     for (int hx = 0; hx < 2; ++hx) {
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int ct = 0; ct < 4; ++ct)
 #pragma unroll
             for (int e = 0; e < 4; ++e) so[(4 * lq + e) * 68 + 16 * ct + lr] = o[4 * hx + ct][e];
-        __syncthreads();
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
         const int row = lane >> 2, seg = lane & 3, tok = 16 * I + row;
         if (tok < r) {
 #pragma unroll
@@ -1048,7 +1068,6 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     p.state_in = a.state_in; p.out = a.out; p.state_out = a.state_out;
     p.meta = reinterpret_cast<int32_t*>(a.ws + lay.off_meta);
     p.cmap = reinterpret_cast<int32_t*>(a.ws + lay.off_cmap);
-    p.khat = reinterpret_cast<_Float16*>(a.ws + lay.off_khat);
     p.khatT = reinterpret_cast<_Float16*>(a.ws + lay.off_khatT);
     p.w = reinterpret_cast<_Float16*>(a.ws + lay.off_w);
     p.u = reinterpret_cast<_Float16*>(a.ws + lay.off_u);

@@ -52,9 +52,10 @@ def test_workspace_size_validation_and_monotonicity():
     a = ws_size(8192, 4, 16, 32, 128)[1]
     b = ws_size(8192 + 128, 4, 16, 32, 128)[1]
     assert 0 < a < b
-    # one 32 KiB tile per (chunk, head) and per intermediate, chunks <= (T + B*127) / 128
+    # one 32 KiB tile per (chunk, head) and per intermediate (k^T per qk head;
+    # w, u, v_new, S_c per value head), chunks <= (T + B*127) / 128
     nc = (8192 + 4 * 127) // 128
-    assert a >= nc * 32768 * (2 * 16 + 4 * 32)
+    assert a >= nc * 32768 * (16 + 4 * 32)
     with pytest.raises(ValueError):
         gdr.chunk_prefill_workspace_size(10, 1, 3, 4)
 
