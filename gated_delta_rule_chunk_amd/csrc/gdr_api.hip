@@ -47,8 +47,7 @@ PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
     L.off_w = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_u = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_gc = off;    off = align256(off + sizeof(float) * kChunk * nc * (size_t)Nv);
-    L.off_vn = off;    off = align256(off + tile16 * nc * (size_t)Nv);
-    L.off_Sc = off;    off = align256(off + tile16 * nc * (size_t)Nv);
+    L.off_scvn = off;  off = align256(off + 2 * tile16 * nc * (size_t)Nv);
     L.total = off;
     return L;
 }

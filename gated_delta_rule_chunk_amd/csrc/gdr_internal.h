@@ -57,8 +57,8 @@ struct PrefillLayout {
     size_t off_w;           // fp16  [NC][Nv]  128 tok x 128 dk, fragment order: w = T (k^ beta e^gcum)
     size_t off_u;           // fp16  [NC][Nv]  128 tok x 128 col, fragment order: u = T (v beta)
     size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate
-    size_t off_vn;          // fp16  [NC][Nv]  128 tok x 128 col, fragment order: v_new = u - w S
-    size_t off_Sc;          // fp16  [NC][Nv]  128 dk x 128 col, fragment order: state at chunk start
+    size_t off_scvn;        // fp16  [NC][Nv]  2 x 128 x 128, paired fragment order: state at chunk
+                            //                 start S_c [dk][col] with v_new = u - w S [tok][col]
     size_t total;
 };
 

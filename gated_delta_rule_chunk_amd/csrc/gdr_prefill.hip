@@ -78,8 +78,7 @@ struct PrefillDev {
     _Float16* w;
     _Float16* u;
     float* gc;
-    _Float16* vn;
-    _Float16* Sc;
+    _Float16* scvn;
     int64_t T;
     int64_t nc;
     int32_t B, Nqk, Nv;
@@ -98,8 +97,8 @@ __device__ __forceinline__ half4 ld_h4(const _Float16* p) { return *reinterpret_
 __device__ __forceinline__ void st_h4(_Float16* p, half4 v) { *reinterpret_cast<half4*>(p) = v; }
 // streaming store (evict-first in the caches): for results that no workgroup of
 // the same kernel reads back, so they do not push shared operand tiles out of L2
-__device__ __forceinline__ void st_h4_nt(_Float16* p, half4 v) {
-    __builtin_nontemporal_store(v, reinterpret_cast<half4*>(p));
+__device__ __forceinline__ void st_h8_nt(_Float16* p, half8 v) {
+    __builtin_nontemporal_store(v, reinterpret_cast<half8*>(p));
 }
 
 __device__ __forceinline__ half8 to_h8(const float (&x)[8]) {
@@ -195,11 +194,15 @@ __device__ __forceinline__ int group_slot(int id, int G) {
 // Workspace tiles that are written or read straight from MFMA registers are
 // stored in the order of those registers, so that every such access is
 // 512 B - 1 KiB contiguous (whole cache lines):
-//  * A-fragment order (k^ [tok][dk], k^T [dk][tok], w [tok][dk]): element
-//    (r, k) sits at 16x32 block (r / 16, k / 32), lane 16 ((k / 8) % 4) +
-//    r % 16 of that block, element k % 8 of the lane's 8.
+//  * A-fragment order (k^T [dk][tok], w [tok][dk]): element (r, k) sits at
+//    16x32 block (r / 16, k / 32), lane 16 ((k / 8) % 4) + r % 16 of that
+//    block, element k % 8 of the lane's 8.
 //  * C-fragment order (u [tok][col]): element (r, c) sits at 16x16 block
 //    (r / 16, c / 16), lane 16 ((r / 4) % 4) + c % 16, element r % 4.
+//  * Paired C-fragment order (S_c [dk][col] with v_new [tok][col]): the two
+//    tiles in C-fragment order with their lane runs interleaved -- the 4
+//    elements of S_c at cfrag_off(r, c) and then the 4 of v_new at the same
+//    offset form one 16-byte piece, at element 2 cfrag_off(r, c).
 __device__ __forceinline__ int frag_off(int r, int k) {
     return (((r >> 4) * 4 + (k >> 5)) * 64 + ((k >> 3) & 3) * 16 + (r & 15)) * 8 + (k & 7);
 }
@@ -733,11 +736,13 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
         scan_load_part<CT, 0>(nx, p, cn, h, hq, ln);
         __builtin_amdgcn_sched_barrier(0);
     }
-    // the state at the start of this chunk, for the output kernel (C-fragment
-    // order: straight from the accumulators, 512 B contiguous per store)
+    // the state at the start of this chunk, for the output kernel; it is
+    // stored below together with v_new (paired C-fragment order: straight
+    // from the accumulators, one 16-byte piece per lane, 1 KiB per store)
     const int tok = 16 * wv + 4 * lq;
+    half4 sc[CT];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct) st_h4_nt(p.Sc + ch * TILE + cfrag_off(tok, col0 + 16 * ct + lr), to_h4(S[ct]));
+    for (int ct = 0; ct < CT; ++ct) sc[ct] = to_h4(S[ct]);
     // v_new = u - w S for tokens 16*wv + 4*lq + e
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
@@ -751,7 +756,9 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
             vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
         }
         const int col = 16 * ct + lr;
-        st_h4_nt(p.vn + ch * TILE + cfrag_off(tok, col0 + col), to_h4(vn));
+        const half4 vh = to_h4(vn);
+        st_h8_nt(p.scvn + 2 * (ch * TILE + cfrag_off(tok, col0 + col)),
+                 half8{sc[ct][0], sc[ct][1], sc[ct][2], sc[ct][3], vh[0], vh[1], vh[2], vh[3]});
         st_h4(&sVn[col * LD16 + tok], to_h4(vs));
     }
     if constexpr (LOAD) {
@@ -866,22 +873,22 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
 // 8 waves; wave w owns output rows 16w .. 16w+15.  The three operand tiles
 // (k^, S_c^T, v_new^T) pass one after another through one LDS buffer.  The
 // keys are normalised here from the input rows (each wave its own 16 rows);
-// S_c and v_new are fetched into registers up front, while k^ is in use.
-// A tile fetched in storage order: 16 B per lane, 1 KiB contiguous per wave.
-__device__ __forceinline__ void frag_tile_fetch(u32x4 (&rg)[4], const _Float16* src, int tid) {
+// the S_c / v_new pair is fetched into registers up front, while k^ is in use.
+// The pair is fetched in storage order: 16 B per lane, 1 KiB contiguous per
+// wave; piece e holds the 4-row runs of S_c and of v_new at lane run e.
+__device__ __forceinline__ void pair_tile_fetch(u32x4 (&rg)[8], const _Float16* src, int tid) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + 512 * n) * 8);
+    for (int n = 0; n < 8; ++n) rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + 512 * n) * 8);
 }
-// A C-fragment-order tile X [row][col] (fetched in storage order by
-// frag_tile_fetch) placed transposed in LDS, X^T [col][row]: each 16-byte
-// piece holds two lanes' runs of 4 rows.
-__device__ __forceinline__ void cfrag_tile_store_t(const u32x4 (&rg)[4], _Float16* dst, int tid) {
+// One tile of the pair (HALF 0: S_c, 1: v_new), X [row][col], placed
+// transposed in LDS, X^T [col][row].
+template <int HALF>
+__device__ __forceinline__ void pair_tile_store_t(const u32x4 (&rg)[8], _Float16* dst, int tid) {
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e = tid + 512 * n, blk = e >> 5, l = 2 * (e & 31);
+    for (int n = 0; n < 8; ++n) {
+        const int e = tid + 512 * n, blk = e >> 6, l = e & 63;
         const int r = 16 * (blk >> 3) + 4 * (l >> 4), c = 16 * (blk & 7) + (l & 15);
-        *reinterpret_cast<u32x2*>(dst + c * LD16 + r) = u32x2{rg[n][0], rg[n][1]};
-        *reinterpret_cast<u32x2*>(dst + (c + 1) * LD16 + r) = u32x2{rg[n][2], rg[n][3]};
+        *reinterpret_cast<u32x2*>(dst + c * LD16 + r) = u32x2{rg[n][2 * HALF], rg[n][2 * HALF + 1]};
     }
 }
 
@@ -905,7 +912,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
 
     // All of the item's tiles are fetched up front (one memory latency per
     // item rather than one per phase); the q rows follow the first.
-    u32x4 stS[4], stV[4];
+    u32x4 stSV[8];
     Raw8<ActT> kr[4];
     {
         // k rows of this wave (rows past the chunk's end re-read its last row:
@@ -927,8 +934,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         const float eg = __expf(GC[row]);
         const float gmine = GC[tid & 127];
         __builtin_amdgcn_sched_barrier(0);
-        frag_tile_fetch(stS, p.Sc + ch * TILE, tid);
-        frag_tile_fetch(stV, p.vn + ch * TILE, tid);
+        pair_tile_fetch(stSV, p.scvn + 2 * ch * TILE, tid);
         __builtin_amdgcn_sched_barrier(0);
         if (tid < 128) sG[tid] = gmine;
         {
@@ -988,7 +994,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         for (int e = 0; e < 4; ++e) sP[(16 * I + 4 * lq + e) * LD16 + 16 * (I + 1) + lr] = (_Float16)0.f;
     }
     __syncthreads();
-    cfrag_tile_store_t(stS, sBuf, tid);   // S_c^T [col][dk]
+    pair_tile_store_t<0>(stSV, sBuf, tid);   // S_c^T [col][dk]
     __syncthreads();
 
     f32x4 o[8];
@@ -1000,7 +1006,7 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
         o[ct] = acc;
     }
     __syncthreads();
-    cfrag_tile_store_t(stV, sBuf, tid);   // v_new^T [col][tok]
+    pair_tile_store_t<1>(stSV, sBuf, tid);   // v_new^T [col][tok]
     __syncthreads();
     for (int ks = 0; ks <= I / 2; ++ks) {
         const half8 a = ld_h8(&sP[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
@@ -1072,8 +1078,7 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     p.w = reinterpret_cast<_Float16*>(a.ws + lay.off_w);
     p.u = reinterpret_cast<_Float16*>(a.ws + lay.off_u);
     p.gc = reinterpret_cast<float*>(a.ws + lay.off_gc);
-    p.vn = reinterpret_cast<_Float16*>(a.ws + lay.off_vn);
-    p.Sc = reinterpret_cast<_Float16*>(a.ws + lay.off_Sc);
+    p.scvn = reinterpret_cast<_Float16*>(a.ws + lay.off_scvn);
     p.T = a.T; p.nc = lay.nc; p.B = a.B; p.Nqk = a.Nqk; p.Nv = a.Nv; p.scale = a.scale;
 
     timing_begin(kChunkmap, stream);
