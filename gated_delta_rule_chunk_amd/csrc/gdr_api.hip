@@ -7,6 +7,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <algorithm>
+
 namespace {
 
 thread_local char g_last_error[512] = "";
@@ -48,6 +50,26 @@ PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
     L.off_u = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_gc = off;    off = align256(off + sizeof(float) * kChunk * nc * (size_t)Nv);
     L.off_scvn = off;  off = align256(off + 2 * tile16 * nc * (size_t)Nv);
+    // Two-level scan when the (sequence, value head) streams cannot fill the
+    // GPU (even at 8 column slices each, 16 streams are 128 workgroups) and
+    // the sequences are long: segments are sized so that the segment maps of
+    // all streams make about 256 workgroups (two per stream segment), and
+    // kept at 8 chunks or more.  nc bounds every sequence's chunk count, so
+    // no sequence has more than nseg segments.
+    const int64_t streams = (int64_t)B * Nv;
+    L.nseg = 1;
+    L.seg_len = 1 << 30;
+    if (streams <= 16 && L.nc >= 64 * (int64_t)B) {
+        const int64_t want = std::min<int64_t>(32, std::max<int64_t>(2, 256 / (2 * streams)));
+        const int64_t len = std::max<int64_t>(8, (L.nc + want - 1) / want);
+        L.seg_len = (int32_t)len;
+        L.nseg = (int32_t)((L.nc + len - 1) / len);
+    }
+    const size_t nsd = (size_t)B * (size_t)L.nseg * (size_t)Nv;
+    L.off_mb = off;
+    if (L.nseg > 1) off = align256(off + sizeof(float) * nsd * kHeadDim * 2 * kHeadDim);
+    L.off_sstart = off;
+    if (L.nseg > 1) off = align256(off + sizeof(float) * nsd * kHeadDim * kHeadDim);
     L.total = off;
     return L;
 }

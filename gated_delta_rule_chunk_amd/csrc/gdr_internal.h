@@ -59,6 +59,13 @@ struct PrefillLayout {
     size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate
     size_t off_scvn;        // fp16  [NC][Nv]  2 x 128 x 128, paired fragment order: state at chunk
                             //                 start S_c [dk][col] with v_new = u - w S [tok][col]
+    // Two-level scan for few, long streams (nseg > 1): every sequence is cut
+    // into segments of seg_len chunks (at most nseg of them); each segment's
+    // affine map S_end = M S_start + B is found first, then the start states.
+    int32_t nseg;           // segments per sequence (1: one-level scan)
+    int32_t seg_len;        // chunks per segment
+    size_t off_mb;          // fp32  [B][nseg][Nv] 128 dk x 256: M (cols 0..127) | B (cols 128..255)
+    size_t off_sstart;      // fp32  [B][nseg][Nv] 128 dk x 128: start state of each segment
     size_t total;
 };
 

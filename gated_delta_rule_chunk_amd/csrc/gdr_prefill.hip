@@ -79,9 +79,12 @@ struct PrefillDev {
     _Float16* u;
     float* gc;
     _Float16* scvn;
+    float* mb;       // two-level scan: segment maps [B][nseg][Nv] 128 x 256
+    float* sstart;   // two-level scan: segment start states [B][nseg][Nv] 128 x 128
     int64_t T;
     int64_t nc;
     int32_t B, Nqk, Nv;
+    int32_t nseg, seg_len;
     float scale;
 };
 
@@ -725,11 +728,14 @@ __device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, i
 // operands of chunk cn are fetched into nx in three parts spread over the
 // step (a burst of fetches would stall the waves' in-order issue behind the
 // memory pipeline); scheduling barriers keep the parts where they are.
-template <int DS, bool LOAD>
+// MODE 1 (a segment's affine map, below) records nothing, and its u is
+// scaled by umul (0 for the columns that carry M).
+template <int DS, bool LOAD, int MODE = 0>
 __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[DS / 16], const PrefillDev& p,
                                           int c, int h, _Float16* sST, _Float16* sVn, int tid,
                                           int wv, int lr, int lq, int col0,
-                                          ScanOps<DS / 16>& nx, int cn, int hq, const ScanLane& ln) {
+                                          ScanOps<DS / 16>& nx, int cn, int hq, const ScanLane& ln,
+                                          float umul = 1.f) {
     constexpr int CT = DS / 16;
     const size_t ch = (size_t)c * p.Nv + h;
     if constexpr (LOAD) {
@@ -752,13 +758,15 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
         f32x4 vn, vs;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            vn[e] = (float)o.u4[ct][e] - vp[e];
+            vn[e] = (MODE == 0 ? (float)o.u4[ct][e] : umul * (float)o.u4[ct][e]) - vp[e];
             vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
         }
         const int col = 16 * ct + lr;
-        const half4 vh = to_h4(vn);
-        st_h8_nt(p.scvn + 2 * (ch * TILE + cfrag_off(tok, col0 + col)),
-                 half8{sc[ct][0], sc[ct][1], sc[ct][2], sc[ct][3], vh[0], vh[1], vh[2], vh[3]});
+        if constexpr (MODE == 0) {
+            const half4 vh = to_h4(vn);
+            st_h8_nt(p.scvn + 2 * (ch * TILE + cfrag_off(tok, col0 + col)),
+                     half8{sc[ct][0], sc[ct][1], sc[ct][2], sc[ct][3], vh[0], vh[1], vh[2], vh[3]});
+        }
         st_h4(&sVn[col * LD16 + tok], to_h4(vs));
     }
     if constexpr (LOAD) {
@@ -784,40 +792,66 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
     __syncthreads();
 }
 
-template <int DS>
+// MODE 0: the scan proper.  Each (sequence, value head) stream -- or, with
+//   two-level scanning, each segment of one -- carries its state from the
+//   start state through its chunks, records S_c and v_new for the output
+//   kernel, and the last segment writes the final state.
+// MODE 1: the affine map of a segment that is not its sequence's last,
+//   S_end = M S_start + B.  The scan runs over 256 columns: the first 128
+//   start from I with u = 0 and end as M, the other 128 start from 0 with the
+//   chunk's u and end as B; nothing is recorded.
+template <int DS, int MODE>
 __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
-    constexpr int NS = 128 / DS, CT = DS / 16;
+    constexpr int NCOL = MODE == 0 ? 128 : 256;
+    constexpr int NS = NCOL / DS, CT = DS / 16;
     __shared__ __align__(16) _Float16 sST[DS * LD16];   // S^T [col][dk] (fp16), current chunk's start state
     __shared__ __align__(16) _Float16 sVn[DS * LD16];   // scaled v_new^T [col][tok]
 
-    // XCD-aware placement: the NS slices of a (sequence, value head) stream
-    // read the same w tiles, and the G value heads of one qk head read the
-    // same k^T tiles, so all G*NS workgroups of a (sequence, qk head) group
-    // get ids the hardware dispatches to one XCD (id mod 8), sharing its L2.
-    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
+    // XCD-aware placement: the NS slices of a (sequence, segment, value head)
+    // stream read the same w tiles, and the G value heads of one qk head read
+    // the same k^T tiles, so all G*NS workgroups of a (sequence, segment, qk
+    // head) group get ids the hardware dispatches to one XCD (id mod 8),
+    // sharing its L2.
+    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk, nseg = p.nseg;
     const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
     const int local = j % (G * NS), grp = (j / (G * NS)) * 8 + xcd;
-    if (grp >= p.B * Nqk) return;
-    const int slice = local % NS, stream = grp * G + local / NS;
-    const int b = stream / Nv, h = stream % Nv, hq = h / G;
+    if (grp >= p.B * nseg * Nqk) return;
+    const int hq = grp % Nqk, seg = (grp / Nqk) % nseg, b = grp / Nqk / nseg;
+    const int slice = local % NS, h = hq * G + local / NS;
+    const int stream = b * Nv + h;
     const int col0 = slice * DS;
     const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
 
+    // this segment's chunks; a sequence has at least one segment (an empty
+    // one passes its state through)
+    const int cb = ld_uniform(&p.meta[b]), ce = ld_uniform(&p.meta[b + 1]);
+    const int nsb = ce > cb ? (ce - cb + p.seg_len - 1) / p.seg_len : 1;
+    if (MODE == 0 ? seg >= nsb : seg >= nsb - 1) return;
+    const int c0 = cb + seg * p.seg_len;
+    const int c1 = (int)min<int64_t>(ce, (int64_t)c0 + p.seg_len);
+    const size_t sd = ((size_t)b * nseg + seg) * Nv + h;   // (sequence, segment, head) index
+
     // S rows 16*wv + 4*lq + e (key dims), columns col0 + 16*ct + lr
     f32x4 S[CT];
-    const size_t sbase = (size_t)stream * TILE;
+    const float* sinit = MODE == 1 ? nullptr
+                         : seg == 0 ? (p.state_in ? p.state_in + (size_t)stream * TILE : nullptr)
+                                    : p.sstart + sd * TILE;
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int dk = 16 * wv + 4 * lq + e, col = col0 + 16 * ct + lr;
-            S[ct][e] = p.state_in ? p.state_in[sbase + (size_t)dk * 128 + col] : 0.f;
+            if constexpr (MODE == 1) S[ct][e] = col == dk ? 1.f : 0.f;
+            else S[ct][e] = sinit ? sinit[(size_t)dk * 128 + col] : 0.f;
         }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(S[ct]));
 
-    const int c0 = p.meta[b], c1 = p.meta[b + 1];
-    const ScanLane ln{(uint32_t)(frag_off(16 * wv + lr, 8 * lq)), (uint32_t)(cfrag_off(16 * wv + 4 * lq, col0 + lr)),
+    // the u columns of this slice (MODE 1: the columns that carry B; those
+    // that carry M read the first columns of u, scaled by 0)
+    const int ucol0 = MODE == 0 ? col0 : (col0 >= 128 ? col0 - 128 : 0);
+    const float umul = MODE == 0 || col0 >= 128 ? 1.f : 0.f;
+    const ScanLane ln{(uint32_t)(frag_off(16 * wv + lr, 8 * lq)), (uint32_t)(cfrag_off(16 * wv + 4 * lq, ucol0 + lr)),
                       (uint32_t)(16 * wv + 4 * lq)};
     // Register sets rotate between the chunk being computed and the ones being
     // fetched (no copies between them, so each chunk's compute waits only for
@@ -840,33 +874,128 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
             scan_load(B, p, min(c0 + 1, cl), h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
             for (; c + 3 <= c1; c += 3) {
-                scan_step<DS, true>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq, ln);
-                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 3, cl), hq,
-                                    ln);
-                scan_step<DS, true>(C, S, p, c + 2, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 4, cl), hq,
-                                    ln);
+                scan_step<DS, true, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq,
+                                          ln, umul);
+                scan_step<DS, true, MODE>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 3, cl),
+                                          hq, ln, umul);
+                scan_step<DS, true, MODE>(C, S, p, c + 2, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 4, cl),
+                                          hq, ln, umul);
             }
-            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln);
-            if (c + 1 < c1) scan_step<DS, false>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln);
+            if (c < c1)
+                scan_step<DS, false, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln, umul);
+            if (c + 1 < c1)
+                scan_step<DS, false, MODE>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln, umul);
         } else {
             ScanOps<CT> A, B;
             scan_load(A, p, c0, h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
             for (; c + 2 <= c1; c += 2) {
-                scan_step<DS, true>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq, ln);
-                scan_step<DS, true>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 2, cl), hq,
-                                    ln);
+                scan_step<DS, true, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq,
+                                          ln, umul);
+                scan_step<DS, true, MODE>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 2, cl),
+                                          hq, ln, umul);
             }
-            if (c < c1) scan_step<DS, false>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, 0, hq, ln);
+            if (c < c1)
+                scan_step<DS, false, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, 0, hq, ln, umul);
         }
     }
+    if constexpr (MODE == 1) {
+        // the map as one fp32 [dk][256] tile: M in columns 0..127, B in 128..255
+        float* dst = p.mb + sd * (2 * TILE);
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+        for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int dk = 16 * wv + 4 * lq + e, col = col0 + 16 * ct + lr;
-            p.state_out[sbase + (size_t)dk * 128 + col] = S[ct][e];
+            for (int e = 0; e < 4; ++e) {
+                const int dk = 16 * wv + 4 * lq + e, col = col0 + 16 * ct + lr;
+                dst[(size_t)dk * 256 + col] = S[ct][e];
+            }
+    } else if (seg == nsb - 1) {
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int dk = 16 * wv + 4 * lq + e, col = col0 + 16 * ct + lr;
+                p.state_out[(size_t)stream * TILE + (size_t)dk * 128 + col] = S[ct][e];
+            }
+    }
+}
+
+// Two-level scan, second level: the start state of every segment of a
+// stream, S_0 = the stream's initial state, S_{s+1} = M_s S_s + B_s, in fp32.
+// One workgroup of 256 threads per (stream, 8 state columns); thread t owns
+// rows 2 (t / 4), 2 (t / 4) + 1 and columns 2 (t % 4), 2 (t % 4) + 1 of the
+// slice.  M sits row-major and the S slice transposed in LDS, so four k of
+// the product take four 16-byte reads for 16 FMAs.  The next map is fetched
+// into registers during the product (every fetch is issued: past the last
+// map it re-reads the last one, unused).
+__global__ __launch_bounds__(256) void combine_kernel(PrefillDev p) {
+    __shared__ __align__(16) float sM[128 * 132];   // M_s [dk][k], padded rows
+    __shared__ __align__(16) float sSt[8 * 132];    // S_s slice transposed [col][k]
+    const int Nv = p.Nv, nseg = p.nseg;
+    const int stream = blockIdx.x >> 4, col0 = 8 * (blockIdx.x & 15);
+    if (stream >= p.B * Nv) return;
+    const int b = stream / Nv, h = stream % Nv;
+    const int cb = ld_uniform(&p.meta[b]), ce = ld_uniform(&p.meta[b + 1]);
+    const int nsb = ce > cb ? (ce - cb + p.seg_len - 1) / p.seg_len : 1;
+    if (nsb < 2) return;
+    const int tid = threadIdx.x, r0 = 2 * (tid >> 2), c2 = 2 * (tid & 3);
+    float x[2][2];   // S rows r0 + i, columns col0 + c2 + j
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            x[i][j] = p.state_in ? p.state_in[(size_t)stream * TILE + (size_t)(r0 + i) * 128 + col0 + c2 + j] : 0.f;
+    const int last = nsb - 2;   // the last map used
+    f32x4 mr[16];               // float4 number tid + 256 n of M: row (q / 32), columns 4 (q % 32) ..
+    float2 br[2];               // B, rows r0 + i, this thread's two columns
+    auto fetch = [&](int s) {
+        const float* MB = p.mb + (((size_t)b * nseg + min(s, last)) * Nv + h) * (2 * TILE);
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const int q = tid + 256 * n;
+            mr[n] = *reinterpret_cast<const f32x4*>(MB + (size_t)(q >> 5) * 256 + 4 * (q & 31));
         }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            br[i] = *reinterpret_cast<const float2*>(MB + (size_t)(r0 + i) * 256 + 128 + col0 + c2);
+    };
+    fetch(0);
+    for (int s = 0; s <= last; ++s) {
+        __syncthreads();   // the previous product is done with sM and sSt
+#pragma unroll
+        for (int n = 0; n < 16; ++n) {
+            const int q = tid + 256 * n;
+            *reinterpret_cast<f32x4*>(&sM[(q >> 5) * 132 + 4 * (q & 31)]) = mr[n];
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j) sSt[(c2 + j) * 132 + r0 + i] = x[i][j];
+        float acc[2][2] = {{br[0].x, br[0].y}, {br[1].x, br[1].y}};
+        __syncthreads();
+        fetch(s + 1);
+#pragma unroll 4
+        for (int k4 = 0; k4 < 32; ++k4) {
+            f32x4 a[2], v[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const f32x4*>(&sM[(r0 + i) * 132 + 4 * k4]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) v[j] = *reinterpret_cast<const f32x4*>(&sSt[(c2 + j) * 132 + 4 * k4]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) acc[i][j] = fmaf(a[i][e], v[j][e], acc[i][j]);
+        }
+        float* dst = p.sstart + (((size_t)b * nseg + s + 1) * Nv + h) * TILE + (size_t)r0 * 128 + col0 + c2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) x[i][j] = acc[i][j];
+            *reinterpret_cast<float2*>(dst + (size_t)i * 128) = float2{x[i][0], x[i][1]};
+        }
+    }
 }
 
 // ------------------------------------------------------------------ K3: output
@@ -1079,7 +1208,10 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     p.u = reinterpret_cast<_Float16*>(a.ws + lay.off_u);
     p.gc = reinterpret_cast<float*>(a.ws + lay.off_gc);
     p.scvn = reinterpret_cast<_Float16*>(a.ws + lay.off_scvn);
+    p.mb = reinterpret_cast<float*>(a.ws + lay.off_mb);
+    p.sstart = reinterpret_cast<float*>(a.ws + lay.off_sstart);
     p.T = a.T; p.nc = lay.nc; p.B = a.B; p.Nqk = a.Nqk; p.Nv = a.Nv; p.scale = a.scale;
+    p.nseg = lay.nseg; p.seg_len = lay.seg_len;
 
     timing_begin(kChunkmap, stream);
     hipLaunchKernelGGL(chunkmap_kernel, dim3(1), dim3(256), 0, stream, a.cu, p);
@@ -1097,20 +1229,33 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // State columns are split over NS = 128 / DS workgroups per (sequence,
-    // head) stream.  A narrower slice shortens each serial step (less MFMA
-    // and LDS work per workgroup) but every slice fetches the chunk's whole w
-    // and k^T tiles; on 256 CUs the best measured split keeps streams x NS
-    // between 256 and about 1024 workgroups.
-    const size_t nstream = (size_t)a.B * a.Nv;
-    const int ns = nstream >= 512 ? 1 : nstream >= 256 ? 2 : nstream >= 64 ? 4 : 8;
-    const size_t ngroup = (size_t)a.B * a.Nqk;
-    const size_t nscan = (ngroup + 7) / 8 * 8 * (size_t)(a.Nv / a.Nqk) * ns;
+    // segment, head) stream.  A narrower slice shortens each serial step (less
+    // MFMA and LDS work per workgroup) but every slice fetches the chunk's
+    // whole w and k^T tiles; on 256 CUs the best measured split keeps
+    // streams x NS between 256 and about 1024 workgroups.  Launches cover
+    // every (sequence, segment) pair of the bound; absent segments exit.
+    const size_t G = (size_t)(a.Nv / a.Nqk);
+    const size_t ngroup = ((size_t)a.B * lay.nseg * a.Nqk + 7) / 8 * 8;
     timing_begin(kScan, stream);
+    if (lay.nseg > 1) {
+        // first level: the maps of all segments but each sequence's last
+        hipLaunchKernelGGL((scan_kernel<128, 1>), dim3((unsigned)(ngroup * G * 2)), dim3(512), 0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        // second level: the segments' start states
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((size_t)a.B * a.Nv * 16)), dim3(256), 0, stream, p);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    // (segments have equal lengths, so there their slices are sized to fit
+    // one workgroup per CU)
+    const size_t nstream = (size_t)a.B * a.Nv * lay.nseg;
+    int ns = nstream >= 512 ? 1 : nstream >= 256 ? 2 : nstream >= 64 ? 4 : 8;
+    while (lay.nseg > 1 && ns > 1 && nstream * ns > (size_t)ncu) ns >>= 1;
+    const size_t nscan = ngroup * G * ns;
     switch (ns) {
-        case 1: hipLaunchKernelGGL(scan_kernel<128>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL(scan_kernel<64>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
-        case 4: hipLaunchKernelGGL(scan_kernel<32>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
-        default: hipLaunchKernelGGL(scan_kernel<16>, dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        case 1: hipLaunchKernelGGL((scan_kernel<128, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL((scan_kernel<64, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        case 4: hipLaunchKernelGGL((scan_kernel<32, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        default: hipLaunchKernelGGL((scan_kernel<16, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
     }
     timing_end(kScan, stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -42,6 +42,30 @@ def ws_size(T, B, Nqk, Nv, D):
     return gdr.lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, ctypes.byref(n)), n.value
 
 
+def _one_level_workspace(T, B, Nqk, Nv):
+    """Workspace bytes of the one-level scan: chunk map, k^T per qk head;
+    w, u, g_cum and the (S_c, v_new) pair per value head; regions 256-aligned."""
+    al = lambda x: (x + 255) // 256 * 256
+    nc = (T + B * 127) // 128
+    tile = 128 * 128 * 2
+    return (al(4 * (B + 2)) + al(16 * nc) + al(tile * nc * Nqk) + 2 * al(tile * nc * Nv)
+            + al(4 * 128 * nc * Nv) + al(2 * tile * nc * Nv))
+
+
+def test_workspace_two_level_scan_only_for_few_long_streams():
+    # many streams, or short sequences: one-level
+    assert ws_size(8192, 4, 16, 32, 128)[1] == _one_level_workspace(8192, 4, 16, 32)
+    assert ws_size(4096, 1, 1, 2, 128)[1] == _one_level_workspace(4096, 1, 1, 2)
+    # 2 streams of 256 chunks: 32 segments of 8 chunks, each with a 128x256 fp32
+    # map and a 128x128 fp32 start state per value head
+    extra = ws_size(32768, 1, 1, 2, 128)[1] - _one_level_workspace(32768, 1, 1, 2)
+    assert extra == 32 * 2 * 4 * 128 * (256 + 128)
+    # 12 streams: segments of at least 8 chunks, at most 256 / (2 * 12) = 10 per sequence
+    T = 25003
+    extra = ws_size(T, 3, 1, 4, 128)[1] - _one_level_workspace(T, 3, 1, 4)
+    assert extra == 3 * 10 * 4 * 4 * 128 * (256 + 128)
+
+
 def test_workspace_size_validation_and_monotonicity():
     assert ws_size(256, 1, 2, 4, 128)[0] == gdr.GDR_OK
     assert ws_size(256, 1, 3, 4, 128)[0] == gdr.GDR_ERR_INVALID_ARGUMENT   # Nv % Nqk

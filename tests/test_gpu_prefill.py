@@ -188,3 +188,33 @@ def test_prefill_many_short_sequences():
     lens[299] = 0
     inp = workloads.prefill_inputs(98, lens, Nqk=1, Nv=2, act="bf16")
     check_parity(inp, f"B=300 T={sum(lens)}")
+
+
+# Two-level scan: with few (sequence, value head) streams and long sequences
+# the library cuts each sequence into segments, finds every segment's affine
+# map (S_end = M S_start + B) first, then each segment's start state, then
+# scans the segments side by side (the workspace size shows the extra maps;
+# tests/test_abi.py checks that these shapes select it).
+def _weak_forgetting(inp):
+    """Gates near zero and small beta, so that a segment's map M stays far
+    from zero and an error in it would show in the outputs."""
+    dt = inp["beta"].dtype
+    inp = dict(inp)
+    inp["g"] = inp["g"] * 0.01
+    inp["beta"] = (inp["beta"].float() * 0.1).to(dt)
+    return inp
+
+
+def test_prefill_two_level_scan_one_long_sequence():
+    inp = workloads.prefill_inputs(60, [32768], Nqk=1, Nv=2, act="bf16")
+    check_parity(inp, "two-level T=32768 Nqk=1 Nv=2 bf16")
+
+
+def test_prefill_two_level_scan_mixed_lengths_weak_forgetting():
+    inp = _weak_forgetting(workloads.prefill_inputs(61, [20000, 0, 5003], Nqk=1, Nv=4, act="bf16"))
+    check_parity(inp, "two-level lens [20000, 0, 5003] Nqk=1 Nv=4 bf16, weak forgetting")
+
+
+def test_prefill_two_level_scan_fp32_weak_forgetting():
+    inp = _weak_forgetting(workloads.prefill_inputs(62, [9000], Nqk=1, Nv=1, act="fp32"))
+    check_parity(inp, "two-level T=9000 Nqk=1 Nv=1 fp32, weak forgetting")
