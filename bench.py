@@ -237,8 +237,9 @@ def bench_decode(args, gdr, torch, workloads):
 
 
 def time_config(n, args, gdr, torch, workloads):
-    """Per-call time of one configured workload (inputs resident, one set)."""
-    inp = workloads.config_inputs(n)
+    """Per-call time of one configured workload (inputs resident, one set);
+    n is a config number or the name of an extra workload."""
+    inp = workloads.config_inputs(n) if isinstance(n, int) else workloads.extra_inputs(n)
     dev = "cuda:0"
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     if "cu_seqlens" in inp:
@@ -254,9 +255,10 @@ def time_config(n, args, gdr, torch, workloads):
             gdr.recurrent_decode(d["q"], d["k"], d["v"], d["g"], d["gk"], d["beta"], d["pool"], d["idx"],
                                  d["lens"], d["scale"])
         ntok = int(inp["lens"].sum())
-    steps = 5 if n == 5 else 20
+    steps = 20 if ntok < 65536 else 5
     dt, per, _, _ = timed(f, steps, 2, gdr, torch)
-    return {"config": workloads.CONFIG_NAMES[n], "ms_per_call": dt / steps * 1e3, "tok_s": ntok / (dt / steps),
+    name = workloads.CONFIG_NAMES[n] if isinstance(n, int) else workloads.EXTRA_NAMES[n]
+    return {"config": name, "ms_per_call": dt / steps * 1e3, "tok_s": ntok / (dt / steps),
             "kernels_us": {k: round(v[0] / max(v[1], 1) * 1e3, 1) for k, v in per.items() if v[1]}}
 
 
@@ -355,7 +357,7 @@ def main():
         line["cpu_baseline"] = None
     print(json.dumps(line))
     if args.all_configs:
-        for n in (1, 2, 3, 4, 5):
+        for n in (1, 2, 3, 4, 5, *workloads.EXTRA_NAMES):
             print(json.dumps(time_config(n, args, gdr, torch, workloads)), flush=True)
 
 

@@ -218,3 +218,19 @@ def test_prefill_two_level_scan_mixed_lengths_weak_forgetting():
 def test_prefill_two_level_scan_fp32_weak_forgetting():
     inp = _weak_forgetting(workloads.prefill_inputs(62, [9000], Nqk=1, Nv=1, act="fp32"))
     check_parity(inp, "two-level T=9000 Nqk=1 Nv=1 fp32, weak forgetting")
+
+
+def test_prefill_two_level_scan_long_few_heads_sampled():
+    """Full-size few-head long-context workload (two-level scan); the oracle
+    checks the first and last value heads over all 131072 tokens."""
+    inp = workloads.extra_inputs("long_few_heads")
+    out, st = run_gpu(inp)
+    for h in (0, inp["Nv"] - 1):
+        sub = dict(q=inp["q"], k=inp["k"], v=inp["v"][:, h:h + 1], g=inp["g"][:, h:h + 1],
+                   beta=inp["beta"][:, h:h + 1], state_in=inp["state_in"][:, h:h + 1],
+                   cu_seqlens=inp["cu_seqlens"], scale=inp["scale"])
+        print(f"[prefill parity] two-level T=131072 Nv=4 head {h}", flush=True)
+        o_ref, s_ref = run_oracle(sub)
+        exc, lit = assert_out_close(out[:, h:h + 1], o_ref, True, f"two-level T=131072 head {h} out")
+        es = assert_state_close(st[:, h:h + 1], s_ref, f"two-level T=131072 head {h} state")
+        print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}); state relFro {es:.2e}", flush=True)

@@ -180,3 +180,18 @@ CONFIG_NAMES = {
     4: "decode B=64 S=4 (lens U{1..4}) Nk=Nv=64 Dk=64 Dv=512 gk, bf16 pool 128 slots",
     5: "prefill long-context B=1 T=131072 Nqk=16 Nv=32 D=128 bf16",
 }
+
+
+# Extra workloads beyond the five configured ones, each named for what it
+# exercises.  "long few heads" has too few (sequence, value head) streams to
+# fill the GPU with the one-level scan, so the library scans it in two levels.
+EXTRA_NAMES = {
+    "long_few_heads": "prefill long-context few heads B=1 T=131072 Nqk=1 Nv=4 D=128 bf16",
+}
+
+
+def extra_inputs(name: str):
+    if name == "long_few_heads":
+        return prefill_inputs(6, [131072], Nqk=1, Nv=4, act="bf16")
+    raise ValueError(name)
+
