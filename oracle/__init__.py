@@ -52,7 +52,7 @@ def _load():
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)
         i = ctypes.c_int
-        lib.gdr_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, ip, i, i, i, i, i, i,
+        lib.gdr_oracle_prefill.argtypes = [dp, dp, dp, dp, dp, dp, dp, ip, i, i, i, i, i, i,
                                            ctypes.c_double, i, dp, dp]
         lib.gdr_oracle_prefill.restype = i
         lib.gdr_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, i, ip, ip, ip,
@@ -117,14 +117,16 @@ def round_fp16(x):
 RULES = {"gated_delta": 0, "delta": 1, "gated": 2, "linear": 3}
 
 
-def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, rule="gated_delta"):
+def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, rule="gated_delta", gk=None):
     """Chunked-prefill semantics by the per-token recurrence.
 
     q, k [T,Nqk,Dk]; v [T,Nv,Dv]; g, beta [T,Nv]; state_in [B,Nv,Dk,Dv] or
-    None (zeros); cu_seqlens [B+1]; rule one of RULES.  Returns (out
-    [T,Nv,Dv], state_out [B,Nv,Dk,Dv]) in float64.
+    None (zeros); cu_seqlens [B+1]; rule one of RULES; gk [T,Nv,Dk] or None
+    (the per-key gate: state row i also decays by exp(gk[t,h,i])).  Returns
+    (out [T,Nv,Dv], state_out [B,Nv,Dk,Dv]) in float64.
     """
     q, k, v, g, beta = map(_f64, (q, k, v, g, beta))
+    gk = _f64(gk)
     state_in = _f64(state_in)
     cu = _i32(cu_seqlens)
     T, Nqk, Dk = q.shape
@@ -133,9 +135,11 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, rule="gated_delta"):
     assert k.shape == q.shape and v.shape[0] == T and g.shape == (T, Nv) and beta.shape == (T, Nv)
     if state_in is not None:
         assert state_in.shape == (B, Nv, Dk, Dv)
+    if gk is not None:
+        assert gk.shape == (T, Nv, Dk)
     out = np.zeros((T, Nv, Dv), np.float64)
     state_out = np.zeros((B, Nv, Dk, Dv), np.float64)
-    rc = _load().gdr_oracle_prefill(_dp(q), _dp(k), _dp(v), _dp(g), _dp(beta), _dp(state_in),
+    rc = _load().gdr_oracle_prefill(_dp(q), _dp(k), _dp(v), _dp(g), _dp(gk), _dp(beta), _dp(state_in),
                                     _ip(cu), T, B, Nqk, Nv, Dk, Dv, float(scale), RULES[rule],
                                     _dp(out), _dp(state_out))
     if rc != 0:

@@ -43,6 +43,15 @@ show the alternatives disagree):
     This module takes and returns [Dk, Dv] and transposes internally.
   * A ragged last chunk is processed with its r < L valid rows only.
 
+Per-key gate (the decode page's gk, read as applying to every prefill token):
+state row d decays by exp(g_t + gk_t[d]) at token t, so every scalar decay of
+the chunk becomes a per-key one, with G = T_tril (g + gk) [r, Dk]:
+  A[i,j] = -beta_i sum_d k_i[d] k_j[d] exp(G_i[d] - G_j[d])   (j < i)
+  k_cumdecay = A^-1 (k_beta * exp(G));  o_inter = (q * exp(G)) S
+  o += (sum_d q_i[d] k_j[d] exp(G_i[d] - G_j[d]), j <= i) v_new
+  S_new = diag(exp(G_last)) S + (k * exp(G_last - G))^T v_new
+(chunk_step_gk; with gk = 0 it is chunk_step).
+
 Update rules ("LinearAttention" page, attribute update_rule): the rules
 without a gate (delta, linear) take g = 0; the rules without the delta term
 (gated, linear) have no pre-attention matrix, so its inverse is I, v_out = v
@@ -119,11 +128,34 @@ def chunk_step(q, k, v, g, beta, S_dkdv, inverse=inverse_rows,
     return o, S_new.T
 
 
-def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, rule="gated_delta", **readings):
+def chunk_step_gk(q, k, v, g, gk, beta, S_dkdv, delta=True):
+    """One chunk with the per-key gate gk [r, Dk] (module docstring); the
+    decay factors are formed directly, exp(G_i[d] - G_j[d]) per (i, j, d)."""
+    r = q.shape[0]
+    tril = np.tril(np.ones((r, r)))
+    G = tril @ (g[:, None] + gk)                                           # [r, Dk]
+    E = np.exp(np.where(tril[:, :, None] > 0, G[:, None, :] - G[None, :, :], 0.0)) * tril[:, :, None]
+    k_beta = k * beta[:, None]
+    if delta:
+        A = -np.einsum("id,jd,ijd->ij", k_beta, k, E) * np.tril(np.ones((r, r)), -1)
+        Ainv = inverse_rows(A)
+        v_out = Ainv @ (v * beta[:, None])
+        k_cumdecay = Ainv @ (k_beta * np.exp(G))
+    else:
+        v_out = v
+        k_cumdecay = np.zeros_like(k)
+    v_new = v_out - k_cumdecay @ S_dkdv
+    o = (q * np.exp(G)) @ S_dkdv + (np.einsum("id,jd,ijd->ij", q, k, E) * tril) @ v_new
+    S_new = np.exp(G[-1])[:, None] * S_dkdv + (k * np.exp(G[-1][None, :] - G)).T @ v_new
+    return o, S_new
+
+
+def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, rule="gated_delta", gk=None, **readings):
     """Chunked prefill over packed varlen sequences, fp64.
 
     q, k [T,Nqk,Dk]; v [T,Nv,Dv]; g, beta [T,Nv]; state_in [B,Nv,Dk,Dv] or
-    None; cu_seqlens [B+1].  Value head h uses qk head h // (Nv // Nqk).
+    None; cu_seqlens [B+1]; gk [T,Nv,Dk] or None.  Value head h uses qk head
+    h // (Nv // Nqk).
     """
     q = np.asarray(q, np.float64)
     k = np.asarray(k, np.float64)
@@ -131,6 +163,9 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, rule="gated_de
     g = np.asarray(g, np.float64)
     if rule in ("delta", "linear"):
         g = np.zeros_like(g)
+        gk = None
+    if gk is not None:
+        gk = np.asarray(gk, np.float64)
     beta = np.asarray(beta, np.float64)
     cu = np.asarray(cu_seqlens, np.int64)
     readings = dict(readings, delta=rule in ("gated_delta", "delta"))
@@ -148,8 +183,12 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, L=128, rule="gated_de
             S = np.zeros((Dk, Dv)) if state_in is None else np.array(state_in[b, h], np.float64)
             for c0 in range(cu[b], cu[b + 1], L):
                 c1 = min(c0 + L, cu[b + 1])
-                o, S = chunk_step(qn[c0:c1, hq], kn[c0:c1, hq], v[c0:c1, h], g[c0:c1, h],
-                                  beta[c0:c1, h], S, **readings)
+                if gk is None:
+                    o, S = chunk_step(qn[c0:c1, hq], kn[c0:c1, hq], v[c0:c1, h], g[c0:c1, h],
+                                      beta[c0:c1, h], S, **readings)
+                else:
+                    o, S = chunk_step_gk(qn[c0:c1, hq], kn[c0:c1, hq], v[c0:c1, h], g[c0:c1, h],
+                                         gk[c0:c1, h], beta[c0:c1, h], S, delta=readings["delta"])
                 out[c0:c1, h] = o
             state_out[b, h] = S
     return out, state_out

@@ -145,6 +145,9 @@ static void l2norm(const double *x, int n, double mul, double *y)
  *   q, k      [T][Nqk][Dk]   raw (normalised here)
  *   v         [T][Nv][Dv]
  *   g, beta   [T][Nv]
+ *   gk        [T][Nv][Dk] or NULL (no per-key gate): state row i of value
+ *             head h at token t decays by exp(g[t][h]) * exp(gk[t][h][i]),
+ *             the decode page's per-key gate applied to every prefill token
  *   state_in  [B][Nv][Dk][Dv] or NULL (= zeros)
  *   cu_seqlens[B+1], cu[0] = 0, non-decreasing, cu[B] = T
  *   out       [T][Nv][Dv]
@@ -153,7 +156,7 @@ static void l2norm(const double *x, int n, double mul, double *y)
  * Returns 0 on success, -1 on invalid sizes, -2 on allocation failure.
  */
 int gdr_oracle_prefill(const double *q, const double *k, const double *v,
-                       const double *g, const double *beta,
+                       const double *g, const double *gk, const double *beta,
                        const double *state_in, const int32_t *cu_seqlens,
                        int T, int B, int Nqk, int Nv, int Dk, int Dv,
                        double scale, int rule, double *out, double *state_out)
@@ -176,7 +179,8 @@ int gdr_oracle_prefill(const double *q, const double *k, const double *v,
             l2norm(q + ((size_t)t * Nqk + hq) * Dk, Dk, scale, qs);
             l2norm(k + ((size_t)t * Nqk + hq) * Dk, Dk, 1.0, ks);
             const double a = gated ? exp(g[(size_t)t * Nv + h]) : 1.0;
-            for (int i = 0; i < Dk; ++i) decay[i] = a;   /* no per-key gate in prefill */
+            for (int i = 0; i < Dk; ++i)
+                decay[i] = (gated && gk) ? a * exp(gk[((size_t)t * Nv + h) * Dk + i]) : a;
             token_step(S, Dk, Dv, decay, ks, v + ((size_t)t * Nv + h) * Dv,
                        delta ? beta[(size_t)t * Nv + h] : 0.0, delta, qs,
                        out + ((size_t)t * Nv + h) * Dv, kv);

@@ -59,6 +59,59 @@ def test_chunked_formulas_equal_recurrence(L):
         np.testing.assert_allclose(s_chk, s_ref, rtol=1e-11, atol=1e-11)
 
 
+@pytest.mark.parametrize("L", [1, 3, 8, 128])
+@pytest.mark.parametrize("rule", ["gated_delta", "gated"])
+def test_chunked_per_key_gate_equals_recurrence(L, rule):
+    """Prefill with the per-key gate gk: the chunked per-key form (decays
+    exp(G_i[d] - G_j[d]) per key) equals the recurrence, which applies
+    exp(g) exp(gk[d]) to state row d at every token."""
+    rng = np.random.default_rng(200 + L)
+    for trial in range(4):
+        nseq = int(rng.integers(1, 4))
+        lens = [int(x) for x in rng.integers(0, 23, nseq)]
+        Nqk = int(rng.integers(1, 3))
+        Nv = Nqk * int(rng.integers(1, 3))
+        Dk, Dv = int(rng.integers(2, 6)), int(rng.integers(2, 6))
+        q, k, v, g, beta, s0, cu = rand_prefill(rng, lens, Nqk, Nv, Dk, Dv, with_state=trial % 2 == 0)
+        gk = -rng.uniform(0.0, 1.5, (sum(lens), Nv, Dk))
+        scale = float(rng.uniform(0.2, 1.5))
+        o_ref, s_ref = oracle.prefill(q, k, v, g, beta, s0, cu, scale, rule=rule, gk=gk)
+        o_chk, s_chk = chunked.prefill(q, k, v, g, beta, s0, cu, scale, L=L, rule=rule, gk=gk)
+        np.testing.assert_allclose(o_chk, o_ref, rtol=1e-10, atol=1e-11)
+        np.testing.assert_allclose(s_chk, s_ref, rtol=1e-10, atol=1e-11)
+
+
+def test_per_key_gate_zero_is_no_gate_and_rules_without_decay_ignore_it():
+    rng = np.random.default_rng(201)
+    q, k, v, g, beta, s0, cu = rand_prefill(rng, [7, 5], 1, 2, 4, 3)
+    o0, s_0 = oracle.prefill(q, k, v, g, beta, s0, cu, 0.7)
+    o1, s_1 = oracle.prefill(q, k, v, g, beta, s0, cu, 0.7, gk=np.zeros((12, 2, 4)))
+    np.testing.assert_array_equal(o0, o1)
+    np.testing.assert_array_equal(s_0, s_1)
+    gk = -rng.uniform(0.1, 1.0, (12, 2, 4))
+    for rule in ("delta", "linear"):
+        o2, s2 = oracle.prefill(q, k, v, g, beta, s0, cu, 0.7, rule=rule)
+        o3, s3 = oracle.prefill(q, k, v, g, beta, s0, cu, 0.7, rule=rule, gk=gk)
+        np.testing.assert_array_equal(o2, o3)
+        np.testing.assert_array_equal(s2, s3)
+
+
+def test_per_key_gate_reset_of_one_key_row():
+    """A very negative gk on key row d wipes that row of the state before the
+    token's update, in prefill as in decode: with a key that is zero on rows
+    0 and 2, row 0 of the final state is exactly zero and row 2 is unchanged."""
+    Dk, Dv = 3, 2
+    q = np.array([[[1.0, 0.0, 0.0]]])
+    k = np.array([[[0.0, 1.0, 0.0]]])
+    v = np.array([[[0.5, -0.25]]])
+    s0 = np.arange(Dk * Dv, dtype=float).reshape(1, 1, Dk, Dv) + 1.0
+    gk = np.zeros((1, 1, Dk))
+    gk[0, 0, 0] = -1e4
+    _, s = oracle.prefill(q, k, v, np.zeros((1, 1)), np.full((1, 1), 0.5), s0, [0, 1], 1.0, gk=gk)
+    np.testing.assert_array_equal(s[0, 0, 0], np.zeros(Dv))          # row 0: reset
+    np.testing.assert_allclose(s[0, 0, 2], s0[0, 0, 2], rtol=1e-12)  # row 2: untouched (k_2 = 0)
+
+
 @pytest.mark.parametrize("reading", [dict(mask_sign=+1.0), dict(strict_out_tril=True),
                                      dict(raw_g_last=True), dict(raw_g_in_kgexp=True)])
 def test_alternative_readings_disagree(reading):
@@ -453,6 +506,14 @@ def test_decode_equals_prefill_on_unit_inputs():
     Sm = s0[0, 0]
     for t in range(T):
         o1, Sm = _decode_one(q[t], k[t], v[t], g[t], beta[t], Sm, scale=0.6)
+        np.testing.assert_allclose(o1[0], o_p[t, 0], rtol=1e-5, atol=1e-5)
+    np.testing.assert_allclose(Sm, s_p[0, 0], rtol=1e-5, atol=1e-5)
+    # and with the per-key gate: prefill's gk [T, Nv, Dk] is decode's [B, Nv, S, Dk]
+    gk = -rng.uniform(0.01, 1.0, (T, 1, Dk))
+    o_p, s_p = oracle.prefill(q, k, v, g, beta, s0, [0, T], 0.6, gk=gk)
+    Sm = s0[0, 0]
+    for t in range(T):
+        o1, Sm = _decode_one(q[t], k[t], v[t], g[t], beta[t], Sm, scale=0.6, gk=gk[t])
         np.testing.assert_allclose(o1[0], o_p[t, 0], rtol=1e-5, atol=1e-5)
     np.testing.assert_allclose(Sm, s_p[0, 0], rtol=1e-5, atol=1e-5)
 
