@@ -42,9 +42,9 @@ SIGNATURES = {
     "gdr_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "gdr_last_error": (ctypes.c_char_p, []),
     "gdr_version": (ctypes.c_int, []),
-    "gdr_chunk_prefill_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32,
+    "gdr_chunk_prefill_workspace_size": (ctypes.c_int, [_i64, _i32, _i32, _i32, _i32, _i32,
                                                         ctypes.POINTER(ctypes.c_size_t)]),
-    "gdr_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
+    "gdr_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                          _i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
     "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
@@ -149,21 +149,22 @@ def timing_read() -> dict:
     return {lib().gdr_timing_kernel_name(i).decode(): (ms[i], n[i]) for i in range(TIMING_KERNELS)}
 
 
-def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128) -> int:
+def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128, gk: bool = False) -> int:
     n = ctypes.c_size_t(0)
-    check(lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, ctypes.byref(n)),
+    check(lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, int(bool(gk)), ctypes.byref(n)),
           "gdr_chunk_prefill_workspace_size")
     return int(n.value)
 
 
 def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, state_out=None,
-                  workspace=None, rule="gated_delta"):
+                  workspace=None, rule="gated_delta", gk=None):
     """Chunked Gated Delta Rule prefill ("Qwen3Next Samples" page).
 
-    q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv] (act dtype: bf16 or fp32);
+    q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv] (act dtype: bf16, fp16 or fp32);
     g [T,Nv] fp32; cu_seqlens [B+1] int32; state_in [B,Nv,D,D] fp32 or None;
     rule one of RULES (g may be None without a gate, beta without the delta
-    term).
+    term); gk [T,Nv,D] fp32 or None: the per-key gate (ignored by the rules
+    without decay).
     Returns (out [T,Nv,D] act dtype, state_out [B,Nv,D,D] fp32).  `out`,
     `state_out` and `workspace` (uint8, >= chunk_prefill_workspace_size
     bytes) may be passed in to avoid allocations.
@@ -189,6 +190,11 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
         raise RuntimeError("g must be float32")
     if cu_seqlens.dtype != torch.int32:
         raise RuntimeError("cu_seqlens must be int32")
+    if gk is not None:
+        if gk.shape != (T, Nv, D) or gk.dtype != torch.float32:
+            raise ValueError(f"gk must be [T,Nv,D] = [{T},{Nv},{D}] float32")
+        if rule not in ("gated_delta", "gated"):
+            gk = None
     if state_in is not None:
         if state_in.shape != (B, Nv, D, D):
             raise ValueError(f"state_in must be [B,Nv,D,D] = [{B},{Nv},{D},{D}]")
@@ -203,12 +209,12 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
         raise ValueError("out must be [T,Nv,D] of q's dtype")
     if state_out.shape != (B, Nv, D, D) or state_out.dtype != torch.float32:
         raise ValueError("state_out must be [B,Nv,D,D] float32")
-    nbytes = chunk_prefill_workspace_size(T, B, Nqk, Nv, D)
+    nbytes = chunk_prefill_workspace_size(T, B, Nqk, Nv, D, gk is not None)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-    _dev(dict(q=q, k=k, v=v, g=g, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, out=out,
+    _dev(dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, out=out,
               state_out=state_out, workspace=workspace), device)
-    check(lib().gdr_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+    check(lib().gdr_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), _ptr(state_in),
                                   _ptr(cu_seqlens), T, B, Nqk, Nv, D, float(scale), code, act, _ptr(out),
                                   _ptr(state_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(device)),

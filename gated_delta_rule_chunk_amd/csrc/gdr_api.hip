@@ -37,7 +37,7 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 namespace gdr {
 
-PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
+PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv, bool gk) {
     PrefillLayout L{};
     L.nc = (T + (int64_t)B * (kChunk - 1)) / kChunk;
     const size_t tile16 = (size_t)kChunk * kHeadDim * 2;   // one 128x128 fp16 tile
@@ -45,11 +45,17 @@ PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv) {
     size_t off = 0;
     L.off_meta = off;  off = align256(off + sizeof(int32_t) * ((size_t)B + 2));
     L.off_cmap = off;  off = align256(off + sizeof(int32_t) * 4 * nc);
-    L.off_khatT = off; off = align256(off + tile16 * nc * (size_t)Nqk);
+    L.gk = gk;
+    // with a per-key gate, k^T carries the value head's decays (one per value head)
+    L.off_khatT = off; off = align256(off + tile16 * nc * (size_t)(gk ? Nv : Nqk));
     L.off_w = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_u = off;     off = align256(off + tile16 * nc * (size_t)Nv);
     L.off_gc = off;    off = align256(off + sizeof(float) * kChunk * nc * (size_t)Nv);
     L.off_scvn = off;  off = align256(off + 2 * tile16 * nc * (size_t)Nv);
+    L.off_qt = off;
+    if (gk) off = align256(off + tile16 * nc * (size_t)Nv);
+    L.off_pm = off;
+    if (gk) off = align256(off + tile16 * nc * (size_t)Nv);
     // Two-level scan when the (sequence, value head) streams cannot fill the
     // GPU (even at 8 column slices each, 16 streams are 128 workgroups) and
     // the sequences are long: segments are sized so that the segment maps of
@@ -106,14 +112,14 @@ const char* gdr_status_string(int status) {
 
 const char* gdr_last_error(void) { return g_last_error; }
 
-int gdr_version(void) { return 100; }
+int gdr_version(void) { return 200; }
 
 gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D,
-                                            size_t* bytes) {
+                                            int32_t with_gk, size_t* bytes) {
     if (!bytes) return fail(GDR_ERR_INVALID_ARGUMENT, "bytes must not be NULL");
     gdr_status s = check_prefill_sizes(T, B, Nqk, Nv, D);
     if (s != GDR_OK) return s;
-    *bytes = gdr::prefill_layout(T, B, Nqk, Nv).total;
+    *bytes = gdr::prefill_layout(T, B, Nqk, Nv, with_gk != 0).total;
     return ok();
 }
 
@@ -124,7 +130,8 @@ static bool rule_gated(gdr_update_rule r) { return r == GDR_RULE_GATED_DELTA || 
 static bool rule_delta(gdr_update_rule r) { return r == GDR_RULE_GATED_DELTA || r == GDR_RULE_DELTA; }
 
 gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
-                             const void* beta, const float* state_in, const int32_t* cu_seqlens,
+                             const float* gk, const void* beta, const float* state_in,
+                             const int32_t* cu_seqlens,
                              int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D, float scale,
                              gdr_update_rule rule, gdr_dtype act, void* out, float* state_out,
                              void* workspace, size_t workspace_bytes, void* hip_stream) {
@@ -139,11 +146,13 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
         return fail(GDR_ERR_INVALID_ARGUMENT,
                     "q, k, v, out (and g for the gated rules, beta for the delta rules) must not be NULL "
                     "when T > 0");
-    const gdr::PrefillLayout lay = gdr::prefill_layout(T, B, Nqk, Nv);
+    // the per-key gate applies only to the rules with decay
+    const float* gk_used = rule_gated(rule) ? gk : nullptr;
+    const gdr::PrefillLayout lay = gdr::prefill_layout(T, B, Nqk, Nv, gk_used != nullptr);
     if (!workspace || workspace_bytes < lay.total)
-        return fail(GDR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu, ptr %p)", lay.total,
-                    workspace_bytes, workspace);
-    gdr::PrefillArgs a{q, k, v, g, beta, state_in, cu_seqlens, out, state_out,
+        return fail(GDR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu, ptr %p)%s", lay.total,
+                    workspace_bytes, workspace, gk_used ? " (with a per-key gate)" : "");
+    gdr::PrefillArgs a{q, k, v, g, gk_used, beta, state_in, cu_seqlens, out, state_out,
                        static_cast<char*>(workspace), T, B, Nqk, Nv, scale, (int32_t)rule};
     return from_hip(gdr::prefill_launch(a, lay, (int)act, static_cast<hipStream_t>(hip_stream)),
                     "prefill launch");

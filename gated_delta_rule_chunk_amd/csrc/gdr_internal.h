@@ -53,10 +53,13 @@ struct PrefillLayout {
     int64_t nc;             // chunk bound
     size_t off_meta;        // int32 [B+2]: first chunk of each sequence, then the total
     size_t off_cmap;        // int4  [NC]: (sequence, first token, valid rows, -)
+    bool gk;                // a per-key gate is applied (the tiles below change as noted)
     size_t off_khatT;       // fp16  [NC][Nqk] 128 dk x 128 tok, fragment order: normalised keys, transposed
+                            //       (per-key gate: [NC][Nv], k^ exp(G_last - G) per value head)
     size_t off_w;           // fp16  [NC][Nv]  128 tok x 128 dk, fragment order: w = T (k^ beta e^gcum)
     size_t off_u;           // fp16  [NC][Nv]  128 tok x 128 col, fragment order: u = T (v beta)
     size_t off_gc;          // fp32  [NC][Nv][128]               chunk-local cumulative gate
+                            //       (per-key gate: G_last[dk], the chunk's decay of state row dk)
     size_t off_scvn;        // fp16  [NC][Nv]  2 x 128 x 128, paired fragment order: state at chunk
                             //                 start S_c [dk][col] with v_new = u - w S [tok][col]
     // Two-level scan for few, long streams (nseg > 1): every sequence is cut
@@ -66,16 +69,21 @@ struct PrefillLayout {
     int32_t seg_len;        // chunks per segment
     size_t off_mb;          // fp32  [B][nseg][Nv] 128 dk x 256: M (cols 0..127) | B (cols 128..255)
     size_t off_sstart;      // fp32  [B][nseg][Nv] 128 dk x 128: start state of each segment
+    size_t off_qt;          // per-key gate only: fp16 [NC][Nv] 128 tok x 128 dk, fragment order:
+                            //       q^ exp(G), the decayed queries of the state term
+    size_t off_pm;          // per-key gate only: fp16 [NC][Nv] 128 x 128 tok, fragment order: the
+                            //       decayed intra-chunk scores P (zero above the diagonal)
     size_t total;
 };
 
-PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv);
+PrefillLayout prefill_layout(int64_t T, int32_t B, int32_t Nqk, int32_t Nv, bool gk);
 
 struct PrefillArgs {
     const void* q;
     const void* k;
     const void* v;
     const float* g;
+    const float* gk;       // per-key gate [T, Nv, 128] or NULL (none, or a rule without decay)
     const void* beta;
     const float* state_in;
     const int32_t* cu;

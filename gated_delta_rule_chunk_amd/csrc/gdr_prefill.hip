@@ -79,6 +79,9 @@ struct PrefillDev {
     _Float16* u;
     float* gc;
     _Float16* scvn;
+    const float* gk;   // per-key gate [T][Nv][128] or NULL
+    _Float16* qt;      // per-key gate: q^ exp(G) [NC][Nv] fragment order
+    _Float16* pm;      // per-key gate: decayed scores P [NC][Nv] fragment order
     float* mb;       // two-level scan: segment maps [B][nseg][Nv] 128 x 256
     float* sstart;   // two-level scan: segment start states [B][nseg][Nv] 128 x 128
     int64_t T;
@@ -672,6 +675,402 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     }
 }
 
+// ------------------------------------------------------------------ K1 with a per-key gate
+// One workgroup per (chunk, value head) item, 8 waves, one workgroup per CU
+// (LDS about 145 KiB).  With a per-key gate gk the decay from token j to
+// token i >= j of state row d is exp(G_i[d] - G_j[d]), G the chunk-local
+// inclusive prefix of g + gk[d] ("LinearAttention" page: per-key decay; the
+// decode page's S <- S exp(g) exp(gk) at every token), so the decayed
+// products q_i.k_j and k_i.k_j no longer factor through one scalar per
+// token.  They are formed per pair of 16-token blocks (I, J):
+//   J < I  through G at the token before block I, s = 16 I - 1:
+//          exp(G_i - G_j) = exp(G_i - G_s) exp(G_s - G_j), both factors
+//          <= 1, so the MFMA operands are scaled keys / queries (fp16);
+//   J = I  through G at the block's middle row m = 16 I + 7: factors up to
+//          exp(8 max|g + gk|), so in fp32, on the 16x16x4 fp32 MFMA.
+// The item stores k^T exp(G_last - G) (the scan's k^T, per value head),
+// G_last (the chunk's decay of each state row), q^ exp(G) and the decayed
+// scores P (the output kernel's two operands), and w, u as the intra kernel
+// does, with w's scaling exp(g_cum) per token become exp(G[d]) per key.
+__device__ __forceinline__ f32x4 mma_f32(float a, float b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void ld_f8(const float* p, float (&x)[8]) {
+    const f32x4 a = *reinterpret_cast<const f32x4*>(p), b = *reinterpret_cast<const f32x4*>(p + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) { x[e] = a[e]; x[4 + e] = b[e]; }
+}
+constexpr int LDG = 132;   // fp32 LDS row stride of G (elements): 528 B, 16-byte aligned rows
+
+template <typename ActT, int RULE>
+__global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
+    __shared__ __align__(16) float sG[128 * LDG];          // G [tok][dk]
+    __shared__ __align__(16) _Float16 sK[128 * LD16];      // k^ [tok][dk] -> k^T (swizzled) -> (v beta)^T
+    __shared__ __align__(16) _Float16 sQL[128 * LD16];     // q^ [tok][dk], then L / T
+    __shared__ float sD[8 * 16 * 17];                      // (first: per-quarter prefix totals)
+    __shared__ float sGt[128], sBeta[128], sBw[128];
+    constexpr bool kDelta = Rule<RULE>::delta;
+
+    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
+    const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
+    const int c = item / Nv, h = item % Nv, hq = h / G;
+    if (c >= ld_uniform(&p.meta[p.B])) return;
+    const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int c4 = tid & 31, tg = tid >> 5;
+    const size_t ch = (size_t)c * Nv + h;
+    const int last = max(r - 1, 0);
+
+    // ---- 0. loads: this wave's q and k rows (rows past the end re-read the
+    //         last one; their k^ is zeroed below), v in the transposing
+    //         layout, the gate tile (rows past the end contribute zero)
+    const ActT* Q = static_cast<const ActT*>(p.q);
+    const ActT* K = static_cast<const ActT*>(p.k);
+    const ActT* V = static_cast<const ActT*>(p.v);
+    const ActT* BETA = static_cast<const ActT*>(p.beta);
+    const int row = 16 * wave + lr, lrow = min(row, last);
+    Raw8<ActT> kr[4], qr[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        raw_load(kr[ks], K + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+        raw_load(qr[ks], Q + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+    }
+    Raw4<ActT> vr[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) raw_load(vr[i], V + ((size_t)(t0 + min(8 * tg + i, last)) * Nv + h) * 128 + 4 * c4);
+#pragma unroll
+    for (int n = 0; n < 8; ++n) {
+        const int q = tid + 512 * n, t = q >> 5, d4 = 4 * (q & 31);
+        f32x4 x = *reinterpret_cast<const f32x4*>(p.gk + ((size_t)(t0 + min(t, last)) * Nv + h) * 128 + d4);
+        if (t >= r) x = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4*>(&sG[t * LDG + d4]) = x;
+    }
+    if (tid < 128) {
+        const bool ok = tid < r;
+        const int tt = t0 + min(tid, last);
+        sGt[tid] = ok ? p.g[(size_t)tt * Nv + h] : 0.f;
+        const float b = kDelta ? load1(&BETA[(size_t)tt * Nv + h]) : 1.f;
+        sBeta[tid] = ok ? b : 0.f;                 // u = T (v beta)
+        sBw[tid] = ok && kDelta ? b : 0.f;         // w = T (k^ beta exp(G))
+    }
+    __syncthreads();
+
+    // ---- 1. G: inclusive prefix over tokens of g + gk[d], per key d
+    {
+        const int d = tid & 127, qt = tid >> 7;
+        float run = 0.f;
+        for (int i = 0; i < 32; ++i) {
+            const int t = 32 * qt + i;
+            run += sG[t * LDG + d] + sGt[t];
+            sG[t * LDG + d] = run;
+        }
+        sD[qt * 128 + d] = run;
+    }
+    __syncthreads();
+    {
+        const int d = tid & 127, qt = tid >> 7;
+        float off = 0.f;
+        for (int j = 0; j < qt; ++j) off += sD[j * 128 + d];
+        for (int i = 0; i < 32; ++i) sG[(32 * qt + i) * LDG + d] += off;
+    }
+    __syncthreads();
+    // G_last per key: the scan's decay of each state row over this chunk
+    if (tid < 128) p.gc[ch * 128 + tid] = sG[127 * LDG + tid];
+
+    // ---- 2. k^ and q^ (scaled) of this wave's rows, row-major; k^ = 0 past the end
+    {
+        float kf[4][8], qf[4][8];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            raw_cvt(kr[ks], kf[ks]);
+            raw_cvt(qr[ks], qf[ks]);
+        }
+        float ksq = 0.f, qsq = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                ksq = fmaf(kf[ks][e], kf[ks][e], ksq);
+                qsq = fmaf(qf[ks][e], qf[ks][e], qsq);
+            }
+        ksq += __shfl_xor(ksq, 16);
+        ksq += __shfl_xor(ksq, 32);
+        qsq += __shfl_xor(qsq, 16);
+        qsq += __shfl_xor(qsq, 32);
+        const float kinv = row < r ? 1.f / sqrtf(ksq + kNormEps) : 0.f;
+        const float qinv = p.scale / sqrtf(qsq + kNormEps);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            float a[8], b[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) { a[e] = kf[ks][e] * kinv; b[e] = qf[ks][e] * qinv; }
+            st_h8(&sK[row * LD16 + 32 * ks + 8 * lq], to_h8(a));
+            st_h8(&sQL[row * LD16 + 32 * ks + 8 * lq], to_h8(b));
+        }
+    }
+    __syncthreads();
+
+    // ---- 3. q^ exp(G) -> workspace (fragment order), and P^T tiles: C[j][i] = P[i][j]
+    //         = sum_d q^_i[d] k^_j[d] exp(G_i[d] - G_j[d]) (j <= i), stored as P in
+    //         fragment order (zero above the diagonal where the output kernel reads)
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n;
+        int rw, kc;
+        frag_piece(e_, rw, kc);
+        const half8 x = ld_h8(&sQL[rw * LD16 + kc]);
+        float gv[8], y[8];
+        ld_f8(&sG[rw * LDG + kc], gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (float)x[e] * __expf(gv[e]);
+        st_h8(p.qt + ch * TILE + (size_t)e_ * 8, to_h8(y));
+    }
+    // One off-diagonal block product through the reference row s (the token
+    // before block I): sum over d of (X_a[d] exp(G_a[d] - G_s[d])) (Y_b[d]
+    // exp(G_s[d] - G_b[d])), a = rows of block IA of X, b = rows of block IB of Y.
+    auto off_tile = [&](const _Float16* X, int IA, const _Float16* Y, int IB, int s, bool a_down) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int ra = 16 * IA + lr, rb = 16 * IB + lr;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const int d0 = 32 * ks + 8 * lq;
+            const half8 xa = ld_h8(&X[ra * LD16 + d0]), yb = ld_h8(&Y[rb * LD16 + d0]);
+            float ga[8], gb[8], gs[8];
+            ld_f8(&sG[ra * LDG + d0], ga);
+            ld_f8(&sG[rb * LDG + d0], gb);
+            ld_f8(&sG[s * LDG + d0], gs);
+            float fa[8], fb[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                // a_down: the A rows are the later block (exp(G_a - G_s));
+                // otherwise the B rows are (and A is the earlier block)
+                fa[e] = (float)xa[e] * __expf(a_down ? ga[e] - gs[e] : gs[e] - ga[e]);
+                fb[e] = (float)yb[e] * __expf(a_down ? gs[e] - gb[e] : gb[e] - gs[e]);
+            }
+            acc = mma(to_h8(fa), to_h8(fb), acc);
+        }
+        return acc;
+    };
+    // One diagonal block product in fp32 through the middle row m: lane (lr, lq)
+    // supplies keys d = 32 lq + kk of row 16 I + lr for both operands; the
+    // A rows (X) are the later token (exp(G_a - G_m)) unless `flip`.
+    auto diag_tile = [&](const _Float16* X, const _Float16* Y, int I, bool flip) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const int rw = 16 * I + lr, m = 16 * I + 7;
+#pragma unroll
+        for (int c8 = 0; c8 < 4; ++c8) {
+            const int d0 = 32 * lq + 8 * c8;
+            const half8 xa = ld_h8(&X[rw * LD16 + d0]), yb = ld_h8(&Y[rw * LD16 + d0]);
+            float gr[8], gm[8];
+            ld_f8(&sG[rw * LDG + d0], gr);
+            ld_f8(&sG[m * LDG + d0], gm);
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                acc = mma_f32((float)xa[e] * __expf(flip ? gm[e] - gr[e] : gr[e] - gm[e]),
+                              (float)yb[e] * __expf(flip ? gr[e] - gm[e] : gm[e] - gr[e]), acc);
+        }
+        return acc;
+    };
+    // tiles by row pairs (pp, 7 - pp), as the intra kernel's Gram: every wave
+    // takes 4 or 5 tiles, one of them diagonal
+    const int pp = wave >> 1;
+    const int rowA = (wave & 1) ? 7 - pp : pp, J0A = (wave & 1) ? 4 - pp : 0, J1A = (wave & 1) ? 8 - pp : pp + 1;
+    const int rowB = 7 - pp, J1B = (wave & 1) ? 0 : 4 - pp;   // even waves: a second, off-diagonal run
+    auto p_row = [&](int I, int J0, int J1) {
+        for (int J = J0; J < J1; ++J) {
+            if (J < I) {
+                // A = k^ rows of block J (earlier), B = q^ rows of block I (later)
+                const f32x4 acc = off_tile(sK, J, sQL, I, 16 * I - 1, false);
+                st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * J + 4 * lq), to_h4(acc));
+            } else {
+                // C[j][i]: A = k^ rows j (earlier), B = q^ rows i (later)
+                const f32x4 acc = diag_tile(sK, sQL, I, true);
+                half4 o4;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(4 * lq + e <= lr ? acc[e] : 0.f);
+                st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * I + 4 * lq), o4);
+                if ((I & 1) == 0)   // the next block's columns, read by the output kernel's last k-step
+                    st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * (I + 1) + 4 * lq), half4{0, 0, 0, 0});
+            }
+        }
+    };
+    p_row(rowA, J0A, J1A);
+    p_row(rowB, 0, J1B);
+    __syncthreads();   // q^ is no longer needed: sQL becomes L (and the prefix totals in sD are done)
+
+    // ---- 4. L = strictlower(beta_i sum_d k^_i[d] k^_j[d] exp(G_i[d] - G_j[d]))
+    //         -> sQL (fp16, zeros above the block diagonal), diagonal blocks also fp32 in sD
+    _Float16* sL = sQL;
+    auto l_row = [&](int I, int J0, int J1) {
+        for (int J = J0; J < J1; ++J) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            if constexpr (kDelta) {
+                // C[i][j]: A = k^ rows of block I (later), B = k^ rows of block J
+                acc = J < I ? off_tile(sK, I, sK, J, 16 * I - 1, true) : diag_tile(sK, sK, I, false);
+            }
+            const int j = 16 * J + lr;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 16 * I + 4 * lq + e;
+                const float Lij = (kDelta && i > j) ? sBw[i] * acc[e] : 0.f;
+                sL[i * LD16 + j] = (_Float16)Lij;
+                if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
+            }
+        }
+    };
+    l_row(rowA, J0A, J1A);
+    l_row(rowB, 0, J1B);
+    {
+        const int i = tid >> 2, I = i >> 4;
+        const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+        for (int gg = 2 * (I + 1) + (tid & 3); gg < 16; gg += 4) st_h8(&sL[i * LD16 + 8 * gg], z);
+    }
+    half4 kt[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kt[i] = ld_h4(&sK[(8 * tg + i) * LD16 + 4 * c4]);
+    __syncthreads();
+
+    // ---- 5. k^T into sK (swizzled); inverses of the diagonal blocks T_bb = (I + L_bb)^-1
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        half8 col;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) col[i] = kt[i][e];
+        st_h8(&sK[sw(4 * c4 + e, 8 * tg)], col);
+    }
+    if (tid < 128) {
+        const int bb = tid >> 4, j = tid & 15;
+        float* Lb = &sD[bb * 16 * 17];
+        float t[16];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            float acc = (i == j) ? 1.f : 0.f;
+#pragma unroll
+            for (int kk = 0; kk < i; ++kk) acc = fmaf(-Lb[i * 17 + kk], t[kk], acc);
+            t[i] = acc;
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) Lb[i * 17 + j] = t[i];
+    }
+    __syncthreads();
+
+    // ---- 6. k^T exp(G_last - G) -> workspace (fragment order, per value head);
+    //         column block j = wave of T by forward substitution
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n;
+        int dk, kc;
+        frag_piece(e_, dk, kc);
+        const half8 x = ld_h8(&sK[sw(dk, kc)]);
+        const float gl = sG[127 * LDG + dk];
+        float y[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) y[e] = (float)x[e] * __expf(gl - sG[(kc + e) * LDG + dk]);
+        st_h8(p.khatT + ch * TILE + (size_t)e_ * 8, to_h8(y));
+    }
+    half4 xh[8];
+    {
+        const int j = wave;
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            if (b < j) continue;
+            f32x4 x;
+            if (b == j) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) x[e] = sD[(16 * b + 4 * lq + e) * 17 + lr];
+            } else {
+                f32x4 acc = zero;
+#pragma unroll
+                for (int a = 0; a < b; ++a) {
+                    if (a < j) continue;
+                    acc = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq]), xh[a], acc);
+                }
+                half4 tb;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) tb[e] = (_Float16)sD[(16 * b + lr) * 17 + 4 * lq + e];
+                x = mma16(tb, to_h4(-acc), zero);
+            }
+            xh[b] = to_h4(x);
+        }
+    }
+    __syncthreads();
+
+    // ---- 7. T (fp16) into sL over L; sK scaled in place to (k^ beta exp(G))^T
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        if (b < wave) continue;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sL[(16 * b + 4 * lq + e) * LD16 + 16 * wave + lr] = xh[b][e];
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n, dk = e_ >> 4, gg = e_ & 15;
+        _Float16* pk = &sK[sw(dk, 8 * gg)];
+        half8 x = ld_h8(pk);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int t = 8 * gg + e;
+            x[e] = (_Float16)((float)x[e] * sBw[t] * __expf(sG[t * LDG + dk]));
+        }
+        st_h8(pk, x);
+    }
+    __syncthreads();
+
+    // ---- 8. w^T = (k^ beta exp(G))^T T^T -> w [tok][dk], fragment order
+    const int pr = wave & 3, hsel = wave >> 2;
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const int Jt = which ? 7 - pr : pr;
+        f32x4 acc[4];
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) acc[ii] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks <= Jt / 2; ++ks) {
+            const half8 b = ld_h8(&sL[(16 * Jt + lr) * LD16 + 32 * ks + 8 * lq]);
+#pragma unroll
+            for (int ii = 0; ii < 4; ++ii)
+                acc[ii] = mma(ld_h8(&sK[sw(16 * (4 * hsel + ii) + lr, 32 * ks + 8 * lq)]), b, acc[ii]);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii)
+            st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * (4 * hsel + ii) + 4 * lq), to_h4(acc[ii]));
+    }
+    __syncthreads();
+
+    // ---- 9. (v beta)^T [col][tok] into sK
+    {
+        float vf[8][4];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) raw_cvt(vr[i], vf[i]);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            half8 col;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) col[i] = (_Float16)(vf[i][e] * sBeta[8 * tg + i]);
+            st_h8(&sK[sw(4 * c4 + e, 8 * tg)], col);
+        }
+    }
+    __syncthreads();
+
+    // ---- 10. u = T (v beta) -> u, fragment order
+#pragma unroll
+    for (int which = 0; which < 2; ++which) {
+        const int I = which ? 7 - pr : pr;
+        f32x4 acc[4];
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int ks = 0; ks <= I / 2; ++ks) {
+            const half8 a = ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj)
+                acc[jj] = mma(a, ld_h8(&sK[sw(16 * (4 * hsel + jj) + lr, 32 * ks + 8 * lq)]), acc[jj]);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj)
+            st_h4(p.u + ch * TILE + cfrag_off(16 * I + 4 * lq, 16 * (4 * hsel + jj) + lr), to_h4(acc[jj]));
+    }
+}
+
 // ------------------------------------------------------------------ K2: state scan
 // 8 waves; wave wv owns rows 16*wv .. 16*wv+15 of w (tokens) and of k^T
 // (key dims), i.e. one 16-row MFMA tile of each product, for DS columns.
@@ -694,7 +1093,7 @@ struct ScanLane {
 
 // One chunk's operands, fetched in three parts: w (first needed by v_new),
 // then u and the gates, then k^T (first needed by the state update).
-template <int CT, int PART>
+template <int CT, int PART, bool GK = false>
 __device__ __forceinline__ void scan_load_part(ScanOps<CT>& o, const PrefillDev& p, int c, int h, int hq,
                                                const ScanLane& ln) {
     const size_t ch = (size_t)c * p.Nv + h;
@@ -710,17 +1109,17 @@ __device__ __forceinline__ void scan_load_part(ScanOps<CT>& o, const PrefillDev&
         o.gcr = *reinterpret_cast<const f32x4*>(GC + ln.g);
         o.glast = GC[127];
     } else {
-        const _Float16* KT = p.khatT + ((size_t)c * p.Nqk + hq) * TILE;
+        const _Float16* KT = p.khatT + (GK ? (size_t)c * p.Nv + h : (size_t)c * p.Nqk + hq) * TILE;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) o.ak[ks] = ld_h8(KT + ln.a + 512 * ks);
     }
 }
-template <int CT>
+template <int CT, bool GK>
 __device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, int c, int h, int hq,
                                           const ScanLane& ln) {
-    scan_load_part<CT, 0>(o, p, c, h, hq, ln);
-    scan_load_part<CT, 1>(o, p, c, h, hq, ln);
-    scan_load_part<CT, 2>(o, p, c, h, hq, ln);
+    scan_load_part<CT, 0, GK>(o, p, c, h, hq, ln);
+    scan_load_part<CT, 1, GK>(o, p, c, h, hq, ln);
+    scan_load_part<CT, 2, GK>(o, p, c, h, hq, ln);
 }
 
 // One chunk of the scan: record S_c and v_new for the output kernel, then
@@ -729,8 +1128,10 @@ __device__ __forceinline__ void scan_load(ScanOps<CT>& o, const PrefillDev& p, i
 // step (a burst of fetches would stall the waves' in-order issue behind the
 // memory pipeline); scheduling barriers keep the parts where they are.
 // MODE 1 (a segment's affine map, below) records nothing, and its u is
-// scaled by umul (0 for the columns that carry M).
-template <int DS, bool LOAD, int MODE = 0>
+// scaled by umul (0 for the columns that carry M).  With the per-key gate
+// (GK) the chunk's decays sit in k^T, and S decays row by row by
+// exp(G_last[dk]) (the gate slot holds G_last of this lane's rows).
+template <int DS, bool LOAD, int MODE = 0, bool GK = false>
 __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[DS / 16], const PrefillDev& p,
                                           int c, int h, _Float16* sST, _Float16* sVn, int tid,
                                           int wv, int lr, int lq, int col0,
@@ -739,7 +1140,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
     constexpr int CT = DS / 16;
     const size_t ch = (size_t)c * p.Nv + h;
     if constexpr (LOAD) {
-        scan_load_part<CT, 0>(nx, p, cn, h, hq, ln);
+        scan_load_part<CT, 0, GK>(nx, p, cn, h, hq, ln);
         __builtin_amdgcn_sched_barrier(0);
     }
     // the state at the start of this chunk, for the output kernel; it is
@@ -759,7 +1160,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             vn[e] = (MODE == 0 ? (float)o.u4[ct][e] : umul * (float)o.u4[ct][e]) - vp[e];
-            vs[e] = vn[e] * __expf(o.glast - o.gcr[e]);
+            vs[e] = GK ? vn[e] : vn[e] * __expf(o.glast - o.gcr[e]);
         }
         const int col = 16 * ct + lr;
         if constexpr (MODE == 0) {
@@ -771,16 +1172,23 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
     }
     if constexpr (LOAD) {
         __builtin_amdgcn_sched_barrier(0);
-        scan_load_part<CT, 1>(nx, p, cn, h, hq, ln);
+        scan_load_part<CT, 1, GK>(nx, p, cn, h, hq, ln);
         __builtin_amdgcn_sched_barrier(0);
     }
     __syncthreads();
     if constexpr (LOAD) {
         __builtin_amdgcn_sched_barrier(0);
-        scan_load_part<CT, 2>(nx, p, cn, h, hq, ln);
+        scan_load_part<CT, 2, GK>(nx, p, cn, h, hq, ln);
         __builtin_amdgcn_sched_barrier(0);
     }
-    const float dec = __expf(o.glast);
+    f32x4 dec;
+    if constexpr (GK) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dec[e] = __expf(o.gcr[e]);
+    } else {
+        const float d1 = __expf(o.glast);
+        dec = f32x4{d1, d1, d1, d1};
+    }
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct) {
         f32x4 acc = S[ct] * dec;
@@ -800,7 +1208,7 @@ __device__ __forceinline__ void scan_step(const ScanOps<DS / 16>& o, f32x4 (&S)[
 //   S_end = M S_start + B.  The scan runs over 256 columns: the first 128
 //   start from I with u = 0 and end as M, the other 128 start from 0 with the
 //   chunk's u and end as B; nothing is recorded.
-template <int DS, int MODE>
+template <int DS, int MODE, bool GK = false>
 __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     constexpr int NCOL = MODE == 0 ? 128 : 256;
     constexpr int NS = NCOL / DS, CT = DS / 16;
@@ -869,34 +1277,34 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
         int c = c0;
         if constexpr (DS <= 64) {
             ScanOps<CT> A, B, C;
-            scan_load(A, p, c0, h, hq, ln);
+            scan_load<CT, GK>(A, p, c0, h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
-            scan_load(B, p, min(c0 + 1, cl), h, hq, ln);
+            scan_load<CT, GK>(B, p, min(c0 + 1, cl), h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
             for (; c + 3 <= c1; c += 3) {
-                scan_step<DS, true, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq,
+                scan_step<DS, true, MODE, GK>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, min(c + 2, cl), hq,
                                           ln, umul);
-                scan_step<DS, true, MODE>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 3, cl),
+                scan_step<DS, true, MODE, GK>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 3, cl),
                                           hq, ln, umul);
-                scan_step<DS, true, MODE>(C, S, p, c + 2, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 4, cl),
+                scan_step<DS, true, MODE, GK>(C, S, p, c + 2, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 4, cl),
                                           hq, ln, umul);
             }
             if (c < c1)
-                scan_step<DS, false, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln, umul);
+                scan_step<DS, false, MODE, GK>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln, umul);
             if (c + 1 < c1)
-                scan_step<DS, false, MODE>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln, umul);
+                scan_step<DS, false, MODE, GK>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, C, 0, hq, ln, umul);
         } else {
             ScanOps<CT> A, B;
-            scan_load(A, p, c0, h, hq, ln);
+            scan_load<CT, GK>(A, p, c0, h, hq, ln);
             __builtin_amdgcn_sched_barrier(0);
             for (; c + 2 <= c1; c += 2) {
-                scan_step<DS, true, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq,
+                scan_step<DS, true, MODE, GK>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, min(c + 1, cl), hq,
                                           ln, umul);
-                scan_step<DS, true, MODE>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 2, cl),
+                scan_step<DS, true, MODE, GK>(B, S, p, c + 1, h, sST, sVn, tid, wv, lr, lq, col0, A, min(c + 2, cl),
                                           hq, ln, umul);
             }
             if (c < c1)
-                scan_step<DS, false, MODE>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, 0, hq, ln, umul);
+                scan_step<DS, false, MODE, GK>(A, S, p, c, h, sST, sVn, tid, wv, lr, lq, col0, B, 0, hq, ln, umul);
         }
     }
     if constexpr (MODE == 1) {
@@ -1166,6 +1574,76 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     }
 }
 
+// ------------------------------------------------------------------ K3 with a per-key gate
+// o = (q^ exp(G)) S_c + P v_new, both A operands stored by the intra kernel
+// in fragment order (loaded straight into registers); S_c^T and v_new^T pass
+// through LDS as in the output kernel.
+template <typename ActT>
+__global__ __launch_bounds__(512) void output_gk_kernel(PrefillDev p) {
+    __shared__ __align__(16) _Float16 sBuf[128 * LD16];
+    __shared__ __align__(16) float sStage[8 * 16 * 68];   // each wave's 16 output rows, 64 columns at a time
+    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
+    const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
+    const int c = item / Nv, h = item % Nv;
+    if (c >= ld_uniform(&p.meta[p.B])) return;
+    const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const size_t ch = (size_t)c * Nv + h;
+    const int I = wv;
+    ActT* OUT = static_cast<ActT*>(p.out);
+
+    half8 qe[4], pa[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        qe[ks] = ld_h8(p.qt + ch * TILE + frag_off(16 * I + lr, 32 * ks + 8 * lq));
+        pa[ks] = ld_h8(p.pm + ch * TILE + frag_off(16 * I + lr, 32 * ks + 8 * lq));
+    }
+    u32x4 stSV[8];
+    pair_tile_fetch(stSV, p.scvn + 2 * ch * TILE, tid);
+    pair_tile_store_t<0>(stSV, sBuf, tid);   // S_c^T [col][dk]
+    __syncthreads();
+    f32x4 o[8];
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) acc = mma(qe[ks], ld_h8(&sBuf[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+        o[ct] = acc;
+    }
+    __syncthreads();
+    pair_tile_store_t<1>(stSV, sBuf, tid);   // v_new^T [col][tok]
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        if (ks > I / 2) break;   // P is zero past these columns
+#pragma unroll
+        for (int ct = 0; ct < 8; ++ct)
+            o[ct] = mma(pa[ks], ld_h8(&sBuf[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), o[ct]);
+    }
+    // rows < r -> out, staged through this wave's own rows of sStage, 64 columns at a time
+    float* so = &sStage[I * 16 * 68];
+#pragma unroll
+    for (int hx = 0; hx < 2; ++hx) {
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int ct = 0; ct < 4; ++ct)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) so[(4 * lq + e) * 68 + 16 * ct + lr] = o[4 * hx + ct][e];
+        __builtin_amdgcn_wave_barrier();
+        asm volatile("" ::: "memory");
+        const int row = lane >> 2, seg = lane & 3, tok = 16 * I + row;
+        if (tok < r) {
+#pragma unroll
+            for (int n = 0; n < 2; ++n) {
+                float y[8];
+                lds_row8(&so[row * 68 + 16 * seg + 8 * n], y);
+                store8(OUT + ((size_t)(t0 + tok) * Nv + h) * 128 + 64 * hx + 16 * seg + 8 * n, y);
+            }
+        }
+    }
+}
+
 }  // namespace
 
 // Compute units of the current device (queried once per device).
@@ -1186,6 +1664,18 @@ static void launch_intra_rule(int act, dim3 grid, hipStream_t stream, const Pref
     if (act == kActBf16) hipLaunchKernelGGL((intra_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
     else if (act == kActFp16) hipLaunchKernelGGL((intra_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
     else hipLaunchKernelGGL((intra_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
+}
+template <int RULE>
+static void launch_intra_gk_rule(int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+    if (act == kActBf16) hipLaunchKernelGGL((intra_gk_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
+    else if (act == kActFp16) hipLaunchKernelGGL((intra_gk_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((intra_gk_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
+}
+// The scan launch for a slice width, one- or two-level pass, with or without the per-key gate.
+template <int DS, int MODE>
+static void launch_scan(bool gk, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+    if (gk) hipLaunchKernelGGL((scan_kernel<DS, MODE, true>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((scan_kernel<DS, MODE, false>), grid, dim3(512), 0, stream, p);
 }
 static void launch_intra(int rule, int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
     switch (rule) {
@@ -1208,6 +1698,9 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     p.u = reinterpret_cast<_Float16*>(a.ws + lay.off_u);
     p.gc = reinterpret_cast<float*>(a.ws + lay.off_gc);
     p.scvn = reinterpret_cast<_Float16*>(a.ws + lay.off_scvn);
+    p.gk = a.gk;
+    p.qt = reinterpret_cast<_Float16*>(a.ws + lay.off_qt);
+    p.pm = reinterpret_cast<_Float16*>(a.ws + lay.off_pm);
     p.mb = reinterpret_cast<float*>(a.ws + lay.off_mb);
     p.sstart = reinterpret_cast<float*>(a.ws + lay.off_sstart);
     p.T = a.T; p.nc = lay.nc; p.B = a.B; p.Nqk = a.Nqk; p.Nv = a.Nv; p.scale = a.scale;
@@ -1219,12 +1712,20 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t nwg = (size_t)lay.nc * a.Nv;
+    const bool gk = a.gk != nullptr;   // the API passes it only with a rule that decays
     if (nwg > 0) {
-        // persistent: two workgroups per CU (LDS < 80 KiB each), each walking items
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
-        const size_t nint = ((nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu) + g8 - 1) / g8 * g8;
         timing_begin(kIntra, stream);
-        launch_intra(a.rule, act, dim3((unsigned)nint), stream, p);
+        if (gk) {
+            // one workgroup per item and per CU (LDS about 145 KiB)
+            const dim3 grid((unsigned)((nwg + g8 - 1) / g8 * g8));
+            if (a.rule == 2) launch_intra_gk_rule<2>(act, grid, stream, p);
+            else launch_intra_gk_rule<0>(act, grid, stream, p);
+        } else {
+            // persistent: two workgroups per CU (LDS < 80 KiB each), each walking items
+            const size_t nint = ((nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu) + g8 - 1) / g8 * g8;
+            launch_intra(a.rule, act, dim3((unsigned)nint), stream, p);
+        }
         timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
@@ -1239,7 +1740,7 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     timing_begin(kScan, stream);
     if (lay.nseg > 1) {
         // first level: the maps of all segments but each sequence's last
-        hipLaunchKernelGGL((scan_kernel<128, 1>), dim3((unsigned)(ngroup * G * 2)), dim3(512), 0, stream, p);
+        launch_scan<128, 1>(gk, dim3((unsigned)(ngroup * G * 2)), stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // second level: the segments' start states
         hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((size_t)a.B * a.Nv * 16)), dim3(256), 0, stream, p);
@@ -1252,10 +1753,10 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     while (lay.nseg > 1 && ns > 1 && nstream * ns > (size_t)ncu) ns >>= 1;
     const size_t nscan = ngroup * G * ns;
     switch (ns) {
-        case 1: hipLaunchKernelGGL((scan_kernel<128, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
-        case 2: hipLaunchKernelGGL((scan_kernel<64, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
-        case 4: hipLaunchKernelGGL((scan_kernel<32, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
-        default: hipLaunchKernelGGL((scan_kernel<16, 0>), dim3((unsigned)nscan), dim3(512), 0, stream, p); break;
+        case 1: launch_scan<128, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+        case 2: launch_scan<64, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+        case 4: launch_scan<32, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+        default: launch_scan<16, 0>(gk, dim3((unsigned)nscan), stream, p); break;
     }
     timing_end(kScan, stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1263,9 +1764,16 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
         timing_begin(kOutput, stream);
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         const unsigned nout = (unsigned)((nwg + g8 - 1) / g8 * g8);
-        if (act == kActBf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
-        else if (act == kActFp16) hipLaunchKernelGGL(output_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
-        else hipLaunchKernelGGL(output_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
+        if (gk) {
+            if (act == kActBf16) hipLaunchKernelGGL(output_gk_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+            else if (act == kActFp16)
+                hipLaunchKernelGGL(output_gk_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL(output_gk_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
+        } else {
+            if (act == kActBf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+            else if (act == kActFp16) hipLaunchKernelGGL(output_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
+            else hipLaunchKernelGGL(output_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
+        }
         timing_end(kOutput, stream);
         e = hipGetLastError();
     }

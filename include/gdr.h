@@ -96,11 +96,12 @@ int gdr_version(void);
  * gdr_chunk_prefill_workspace_size
  *   Bytes of device workspace gdr_chunk_prefill needs for these sizes.
  *   T >= 0 total packed tokens; B >= 1 sequences; Nqk >= 1 query/key heads;
- *   Nv a multiple of Nqk; D must be 128.  Writes *bytes; returns
+ *   Nv a multiple of Nqk; D must be 128; with_gk != 0 if the call will pass
+ *   a per-key gate (it needs more workspace).  Writes *bytes; returns
  *   GDR_ERR_INVALID_ARGUMENT / GDR_ERR_UNSUPPORTED on bad sizes.
  */
 gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, int32_t Nv,
-                                            int32_t D, size_t *bytes);
+                                            int32_t D, int32_t with_gk, size_t *bytes);
 
 /*
  * gdr_chunk_prefill -- chunked Gated Delta Rule forward ("Qwen3Next
@@ -111,7 +112,8 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  * state_in[b,h] (zeros if state_in is NULL), the operator computes, token
  * by token (the chunked form with L = 128 is an exact rearrangement):
  *   q^ = q / sqrt(sum q^2 + 1e-6) * scale,  k^ = k / sqrt(sum k^2 + 1e-6)
- *   S = exp(g) S;  S = S + k^ ((v - S^T k^) beta)^T;  out = S^T q^
+ *   S = exp(g) S  (row i also times exp(gk[i]) with a per-key gate);
+ *   S = S + k^ ((v - S^T k^) beta)^T;  out = S^T q^
  * and writes the final S to state_out[b,h].  A sequence of length 0 passes
  * its state through unchanged.  `rule` selects a reduced update (see
  * gdr_update_rule); q and k are L2-normalised inside for every rule.
@@ -119,6 +121,12 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  *   q, k        [T, Nqk, D]   act dtype   (raw; normalised inside)
  *   v           [T, Nv, D]    act dtype
  *   g           [T, Nv]       fp32        log-decay gate (expected < 0)
+ *   gk          [T, Nv, D]    fp32 or NULL: per-key log-decay gate (the decode
+ *                             page's gk, applied at every token; expected < 0
+ *                             and, per token, g + gk >= -11 so that a
+ *                             16-token block's decay stays within fp32);
+ *                             ignored by the rules without decay.  A non-NULL
+ *                             gk needs the workspace queried with with_gk = 1
  *   beta        [T, Nv]       act dtype   (expected in [0, 1])
  *   state_in    [B, Nv, D, D] fp32 or NULL (= zeros); key dim = rows
  *   cu_seqlens  [B + 1]       int32, device; cu[0] = 0, non-decreasing, cu[B] = T
@@ -133,7 +141,8 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  *   hip_stream                hipStream_t the work is enqueued on
  */
 gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const float *g,
-                             const void *beta, const float *state_in, const int32_t *cu_seqlens,
+                             const float *gk, const void *beta, const float *state_in,
+                             const int32_t *cu_seqlens,
                              int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D,
                              float scale, gdr_update_rule rule, gdr_dtype act, void *out,
                              float *state_out, void *workspace, size_t workspace_bytes,

@@ -34,12 +34,12 @@ def test_status_strings_and_version():
     assert lib.gdr_status_string(1) == b"GDR_ERR_INVALID_ARGUMENT"
     assert lib.gdr_status_string(5) == b"GDR_ERR_HIP"
     assert lib.gdr_status_string(99) == b"unknown status"
-    assert lib.gdr_version() >= 100
+    assert lib.gdr_version() >= 200
 
 
-def ws_size(T, B, Nqk, Nv, D):
+def ws_size(T, B, Nqk, Nv, D, gk=0):
     n = ctypes.c_size_t(0)
-    return gdr.lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, ctypes.byref(n)), n.value
+    return gdr.lib().gdr_chunk_prefill_workspace_size(T, B, Nqk, Nv, D, gk, ctypes.byref(n)), n.value
 
 
 def _one_level_workspace(T, B, Nqk, Nv):
@@ -85,11 +85,11 @@ def test_workspace_size_validation_and_monotonicity():
 
 
 def prefill_call(**over):
-    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state_in=None, cu=FAKE, T=256, B=1, Nqk=2,
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, beta=FAKE, state_in=None, cu=FAKE, T=256, B=1, Nqk=2,
              Nv=4, D=128, scale=0.1, rule=0, act=gdr.GDR_BF16, out=FAKE, state_out=FAKE, ws=FAKE,
              ws_bytes=1 << 40, stream=None)
     a.update(over)
-    return gdr.lib().gdr_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"], a["cu"],
+    return gdr.lib().gdr_chunk_prefill(a["q"], a["k"], a["v"], a["g"], a["gk"], a["beta"], a["state_in"], a["cu"],
                                        a["T"], a["B"], a["Nqk"], a["Nv"], a["D"], a["scale"], a["rule"],
                                        a["act"], a["out"], a["state_out"], a["ws"], a["ws_bytes"],
                                        a["stream"])
@@ -116,6 +116,16 @@ def test_prefill_host_validation():
     assert prefill_call(g=None, beta=None, rule=3, ws=None) == E.GDR_ERR_WORKSPACE
     assert prefill_call(beta=None, rule=1) == E.GDR_ERR_INVALID_ARGUMENT
     assert prefill_call(g=None, rule=2) == E.GDR_ERR_INVALID_ARGUMENT
+    # a per-key gate needs the larger workspace (queried with with_gk = 1); the
+    # rules without decay ignore it
+    plain = ws_size(256, 1, 2, 4, 128)[1]
+    with_gk = ws_size(256, 1, 2, 4, 128, 1)[1]
+    assert with_gk > plain
+    assert prefill_call(gk=FAKE, ws_bytes=plain) == E.GDR_ERR_WORKSPACE
+    assert b"per-key gate" in gdr.lib().gdr_last_error()
+    assert prefill_call(gk=FAKE, ws=None) == E.GDR_ERR_WORKSPACE
+    assert prefill_call(gk=FAKE, g=None, rule=1, ws_bytes=plain, ws=None) == E.GDR_ERR_WORKSPACE
+    assert b"per-key gate" not in gdr.lib().gdr_last_error()
 
 
 def decode_call(**over):

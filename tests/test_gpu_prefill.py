@@ -20,20 +20,20 @@ def run_gpu(inp, state_in="from_inputs", rule="gated_delta", drop_unused=True):
         g = None if rule in ("delta", "linear") else g
         beta = None if rule in ("gated", "linear") else beta
     out, st = gdr.chunk_prefill(d["q"], d["k"], d["v"], g, beta, d["cu_seqlens"], d["scale"],
-                                state_in=s_in, rule=rule)
+                                state_in=s_in, rule=rule, gk=d.get("gk"))
     torch.cuda.synchronize()
     return out.cpu(), st.cpu()
 
 
 def run_oracle(inp, rule="gated_delta"):
     return oracle.prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["state_in"],
-                          inp["cu_seqlens"], inp["scale"], rule=rule)
+                          inp["cu_seqlens"], inp["scale"], rule=rule, gk=inp.get("gk"))
 
 
-def check_parity(inp, tag):
+def check_parity(inp, tag, rule="gated_delta"):
     print(f"[prefill parity] {tag}", flush=True)
-    out, st = run_gpu(inp)
-    out_ref, st_ref = run_oracle(inp)
+    out, st = run_gpu(inp, rule=rule)
+    out_ref, st_ref = run_oracle(inp, rule=rule)
     exc, lit = assert_out_close(out, out_ref, out_kind(out), f"{tag} out")
     es = assert_state_close(st, st_ref, f"{tag} state")
     print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}) x RMS; state relFro {es:.2e}", flush=True)
@@ -234,3 +234,41 @@ def test_prefill_two_level_scan_long_few_heads_sampled():
         exc, lit = assert_out_close(out[:, h:h + 1], o_ref, True, f"two-level T=131072 head {h} out")
         es = assert_state_close(st[:, h:h + 1], s_ref, f"two-level T=131072 head {h} state")
         print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}); state relFro {es:.2e}", flush=True)
+
+
+
+# Per-key gate gk [T, Nv, D]: the decay between tokens differs per key, so the
+# intra-chunk products are formed per 16-token block pair (the library's
+# per-key-gate path); "strong" is the decode page's example range, "weak"
+# keeps the state alive across chunks so that the scan's per-row decay shows.
+@pytest.mark.parametrize("act,strength", [("bf16", "strong"), ("bf16", "weak"), ("fp32", "weak"),
+                                          ("fp16", "strong")])
+def test_prefill_per_key_gate_ragged(act, strength):
+    lens = [1, 127, 128, 129, 300, 0, 77]
+    inp = workloads.prefill_inputs(80, lens, Nqk=2, Nv=4, act=act, gk=strength)
+    check_parity(inp, f"gk {strength} ragged varlen {lens} {act}")
+
+
+def test_prefill_per_key_gate_gated_rule():
+    inp = workloads.prefill_inputs(81, [260, 45], Nqk=1, Nv=2, act="bf16", gk="weak")
+    check_parity(inp, "gk weak, gated rule", rule="gated")
+
+
+def test_prefill_per_key_gate_rules_without_decay_ignore_it():
+    inp = workloads.prefill_inputs(82, [200, 77], Nqk=2, Nv=4, act="bf16", gk="strong")
+    plain = dict(inp, gk=None)
+    for rule in ("delta", "linear"):
+        o1, s1 = run_gpu(inp, rule=rule)
+        o2, s2 = run_gpu(plain, rule=rule)
+        assert torch.equal(o1, o2) and torch.equal(s1, s2), rule
+
+
+def test_prefill_per_key_gate_varlen_t8192():
+    inp = workloads.prefill_inputs(83, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", gk="weak")
+    check_parity(inp, "gk weak B=4 T=8192 Nqk=16 Nv=32 bf16")
+
+
+def test_prefill_per_key_gate_two_level_scan():
+    inp = workloads.prefill_inputs(84, [20000], Nqk=1, Nv=2, act="bf16", gk="weak")
+    check_parity(inp, "gk weak two-level T=20000 Nqk=1 Nv=2 bf16")
+

@@ -48,12 +48,15 @@ def _sigmoid(x):
 
 
 def prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128, act: str = "bf16",
-                   init_state: str = "randn", scale: float | None = None):
+                   init_state: str = "randn", scale: float | None = None, gk: str | None = None):
     """Packed varlen prefill inputs.
 
     Returns a dict of CPU tensors: q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv]
     (act dtype); g [T,Nv] fp32; state_in [B,Nv,D,D] fp32 or None;
-    cu_seqlens [B+1] int32; plus scale, T, B, Nqk, Nv, D, act.
+    cu_seqlens [B+1] int32; gk [T,Nv,D] fp32 or None; plus scale, T, B, Nqk,
+    Nv, D, act.  gk: None; "strong", the decode page's example range
+    -U(0.01, 1.01); or "weak", -U(0.001, 0.05), under which the state carries
+    across chunks.  gk is drawn last, so the other inputs do not depend on it.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     seq_lens = [int(x) for x in seq_lens]
@@ -72,9 +75,16 @@ def prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128, act: st
         state_in = _normal_blocks(rng, (B, Nv, D, D), std=0.02, dtype="fp32", block_rows=1)
     else:
         raise ValueError(init_state)
+    if gk is None:
+        gkt = None
+    elif gk in ("strong", "weak"):
+        lo, hi = (0.01, 1.01) if gk == "strong" else (0.001, 0.05)
+        gkt = _cast(-rng.uniform(lo, hi, (T, Nv, D)), "fp32")
+    else:
+        raise ValueError(gk)
     return dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in,
                 cu_seqlens=torch.from_numpy(cu), scale=SCALE_128 if scale is None else scale,
-                T=T, B=B, Nqk=Nqk, Nv=Nv, D=D, act=act)
+                T=T, B=B, Nqk=Nqk, Nv=Nv, D=D, act=act, gk=gkt)
 
 
 def _unit_rows(rng, shape):
