@@ -702,88 +702,139 @@ __device__ __forceinline__ void ld_f8(const float* p, float (&x)[8]) {
 }
 constexpr int LDG = 132;   // fp32 LDS row stride of G (elements): 528 B, 16-byte aligned rows
 
-template <typename ActT, int RULE>
-__global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
-    __shared__ __align__(16) float sG[128 * LDG];          // G [tok][dk]
-    __shared__ __align__(16) _Float16 sK[128 * LD16];      // k^ [tok][dk] -> k^T (swizzled) -> (v beta)^T
-    __shared__ __align__(16) _Float16 sQL[128 * LD16];     // q^ [tok][dk], then L / T
-    __shared__ float sD[8 * 16 * 17];                      // (first: per-quarter prefix totals)
-    __shared__ float sGt[128], sBeta[128], sBw[128];
-    constexpr bool kDelta = Rule<RULE>::delta;
+// Inputs an item holds in registers: the next item's k, q (this wave's rows),
+// g and beta, and the item's own v; every thread issues the same loads on
+// every pass (past the last item they re-read the current one, unused).
+template <typename ActT>
+struct GkStage {
+    Raw8<ActT> k[4], q[4];   // rows 16 wave + lr, keys 32 ks + 8 lq ..
+    Raw4<ActT> v[8];         // rows 8 tg + i, columns 4 c4 ..
+    float g;                 // threads < 128: token tid
+    ActT b;
+    int c, h, t0, r;         // the item k, q, g, beta belong to
+};
 
-    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
-    const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
-    const int c = item / Nv, h = item % Nv, hq = h / G;
-    if (c >= ld_uniform(&p.meta[p.B])) return;
-    const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+// The place of item `item` (chunk * Nv + value head) in the token stream
+template <typename ActT>
+__device__ __forceinline__ void gk_place(GkStage<ActT>& st, const PrefillDev& p, int item) {
+    const int c = item / p.Nv;
+    st.c = c;
+    st.h = item % p.Nv;
+    st.t0 = ld_uniform(&p.cmap[4 * c + 1]);
+    st.r = ld_uniform(&p.cmap[4 * c + 2]);
+}
+
+// Parts of the item in st's place: what = 0: k, 1: q, 2: g and beta (issued
+// at different points of the previous item, so that the loads of all
+// workgroups do not come at once)
+template <typename ActT, int RULE>
+__device__ __forceinline__ void gk_load_in(GkStage<ActT>& st, const PrefillDev& p, int what, int tid) {
+    const int Nv = p.Nv, Nqk = p.Nqk, hq = st.h / (Nv / Nqk), t0 = st.t0, last = max(st.r - 1, 0);
+    const int wave = tid >> 6, lr = tid & 15, lq = (tid >> 4) & 3;
+    const int lrow = min(16 * wave + lr, last);
+    if (what < 2) {
+        const ActT* X = static_cast<const ActT*>(what ? p.q : p.k);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+            raw_load(what ? st.q[ks] : st.k[ks], X + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+    } else {
+        const int tt = t0 + min(tid & 127, last);
+        st.g = p.g[(size_t)tt * Nv + st.h];
+        if constexpr (Rule<RULE>::delta) st.b = static_cast<const ActT*>(p.beta)[(size_t)tt * Nv + st.h];
+        else st.b = ActT(0);
+    }
+}
+
+// Rows 8 tg + 4 hv .. + 3 of v of the item at (t0, h, r)
+template <typename ActT>
+__device__ __forceinline__ void gk_load_v(GkStage<ActT>& st, const PrefillDev& p, int t0, int h, int r, int hv,
+                                          int tid) {
+    const int last = max(r - 1, 0), c4 = tid & 31, tg = tid >> 5;
+    const ActT* V = static_cast<const ActT*>(p.v);
+#pragma unroll
+    for (int i = 4 * hv; i < 4 * hv + 4; ++i)
+        raw_load(st.v[i], V + ((size_t)(t0 + min(8 * tg + i, last)) * p.Nv + h) * 128 + 4 * c4);
+}
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// 16 B per lane from src straight into LDS at dst + 16 lane (dst uniform over
+// the wave).  Written out so that the compiler, which would otherwise wait for
+// it at the next access to the same shared array, leaves it in flight: the
+// caller makes the data visible (s_waitcnt vmcnt(0), then a barrier) and
+// touches the destination neither before that nor while it loads.  It has
+// no register result.
+// (M0 is set here and used by nothing else in this file.)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(const float* src, float* dst) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void_t*)dst);
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(src), "s"(base) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// The gate tile waits in G's region, unpadded [tok][128] fp32: tokens 0..63
+// from float kGateHi on (behind KB, which takes the first 128 LD16 halves'
+// rows), tokens 64..127 from 0 (free once KB is done).
+constexpr int kGateHi = 128 * LD16 / 2;
+static_assert(kGateHi + 64 * 128 <= 128 * LDG, "gate staging fits G's region");
+
+// Quarter q4 of the gate tile of the item at (t0, h, r) (tokens 32 q4 ..
+// 32 q4 + 31) straight from memory into LDS (rows past the end re-read the
+// last row; the scan masks them): each wave 2 loads of two rows (1 KiB,
+// lane l -> bytes 16 l .. 16 l + 15 of the destination).
+__device__ __forceinline__ void gk_gate_dma(const PrefillDev& p, int t0, int h, int r, float* sG, int q4, int tid) {
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, last = max(r - 1, 0);
+    float* dst = sG + (q4 < 2 ? kGateHi + 32 * q4 * 128 : (32 * q4 - 64) * 128);
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+        const int wi = 2 * wave + n, t = 32 * q4 + 2 * wi + (lane >> 5);
+        const float* src = p.gk + ((size_t)(t0 + min(t, last)) * p.Nv + h) * 128 + 4 * (lane & 31);
+        lds_load16(src, dst + wi * 256);
+    }
+}
+
+// Thread indices taken afresh from a laundered copy of the thread id, so that
+// the compiler recomputes a step's index arithmetic instead of keeping it
+// live (and spilling it) from earlier steps.
+#define GK_IDS()                                                                    \
+    int tid = tid_in;                                                               \
+    asm volatile("" : "+v"(tid));                                                   \
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;     \
+    const int lr = lane & 15, lq = lane >> 4, c4 = tid & 31, tg = tid >> 5;         \
+    (void)wave; (void)lr; (void)lq; (void)c4; (void)tg
+
+template <typename ActT, int RULE>
+__device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const PrefillDev& p, float* sG, _Float16* sK,
+                                        _Float16* sQL, float* sD, float* sGb, float* sC, float* sGt, float* sBeta,
+                                        float* sBw, int tid_in) {
+    int tid = tid_in;
+    asm volatile("" : "+v"(tid));
+    constexpr bool kDelta = Rule<RULE>::delta;
+    const int Nv = p.Nv;
+    const int c = st.c, h = st.h, t0 = st.t0, r = st.r;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int c4 = tid & 31, tg = tid >> 5;
     const size_t ch = (size_t)c * Nv + h;
-    const int last = max(r - 1, 0);
+    _Float16* sKB = reinterpret_cast<_Float16*>(sG);   // KB takes G's place once G is done
 
-    // ---- 0. loads: this wave's q and k rows (rows past the end re-read the
-    //         last one; their k^ is zeroed below), v in the transposing
-    //         layout, the gate tile (rows past the end contribute zero)
-    const ActT* Q = static_cast<const ActT*>(p.q);
-    const ActT* K = static_cast<const ActT*>(p.k);
-    const ActT* V = static_cast<const ActT*>(p.v);
-    const ActT* BETA = static_cast<const ActT*>(p.beta);
-    const int row = 16 * wave + lr, lrow = min(row, last);
-    Raw8<ActT> kr[4], qr[4];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-        raw_load(kr[ks], K + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
-        raw_load(qr[ks], Q + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
-    }
-    Raw4<ActT> vr[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) raw_load(vr[i], V + ((size_t)(t0 + min(8 * tg + i, last)) * Nv + h) * 128 + 4 * c4);
-#pragma unroll
-    for (int n = 0; n < 8; ++n) {
-        const int q = tid + 512 * n, t = q >> 5, d4 = 4 * (q & 31);
-        f32x4 x = *reinterpret_cast<const f32x4*>(p.gk + ((size_t)(t0 + min(t, last)) * Nv + h) * 128 + d4);
-        if (t >= r) x = f32x4{0.f, 0.f, 0.f, 0.f};
-        *reinterpret_cast<f32x4*>(&sG[t * LDG + d4]) = x;
-    }
+    __syncthreads();   // the previous item is done with the shared buffers, the gate tile is in
+    // ---- 0. g and beta per token; k^ (zero past the end) and q^ (scaled) of
+    //         this wave's rows, row-major
     if (tid < 128) {
         const bool ok = tid < r;
-        const int tt = t0 + min(tid, last);
-        sGt[tid] = ok ? p.g[(size_t)tt * Nv + h] : 0.f;
-        const float b = kDelta ? load1(&BETA[(size_t)tt * Nv + h]) : 1.f;
+        const float b = kDelta ? load1(&st.b) : 1.f;
+        sGt[tid] = ok ? st.g : 0.f;
         sBeta[tid] = ok ? b : 0.f;                 // u = T (v beta)
         sBw[tid] = ok && kDelta ? b : 0.f;         // w = T (k^ beta exp(G))
     }
-    __syncthreads();
-
-    // ---- 1. G: inclusive prefix over tokens of g + gk[d], per key d
     {
-        const int d = tid & 127, qt = tid >> 7;
-        float run = 0.f;
-        for (int i = 0; i < 32; ++i) {
-            const int t = 32 * qt + i;
-            run += sG[t * LDG + d] + sGt[t];
-            sG[t * LDG + d] = run;
-        }
-        sD[qt * 128 + d] = run;
-    }
-    __syncthreads();
-    {
-        const int d = tid & 127, qt = tid >> 7;
-        float off = 0.f;
-        for (int j = 0; j < qt; ++j) off += sD[j * 128 + d];
-        for (int i = 0; i < 32; ++i) sG[(32 * qt + i) * LDG + d] += off;
-    }
-    __syncthreads();
-    // G_last per key: the scan's decay of each state row over this chunk
-    if (tid < 128) p.gc[ch * 128 + tid] = sG[127 * LDG + tid];
-
-    // ---- 2. k^ and q^ (scaled) of this wave's rows, row-major; k^ = 0 past the end
-    {
+        const int row = 16 * wave + lr;
         float kf[4][8], qf[4][8];
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            raw_cvt(kr[ks], kf[ks]);
-            raw_cvt(qr[ks], qf[ks]);
+            raw_cvt(st.k[ks], kf[ks]);
+            raw_cvt(st.q[ks], qf[ks]);
         }
         float ksq = 0.f, qsq = 0.f;
 #pragma unroll
@@ -808,11 +859,42 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
             st_h8(&sQL[row * LD16 + 32 * ks + 8 * lq], to_h8(b));
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's gate tile loads are in LDS
     __syncthreads();
 
-    // ---- 3. q^ exp(G) -> workspace (fragment order), and P^T tiles: C[j][i] = P[i][j]
-    //         = sum_d q^_i[d] k^_j[d] exp(G_i[d] - G_j[d]) (j <= i), stored as P in
-    //         fragment order (zero above the diagonal where the output kernel reads)
+    // ---- 1. G: inclusive prefix over tokens of g + gk[d], per key d (zero past
+    //         the end); each thread scans 32 tokens of one key in registers,
+    //         then the quarters are joined through sD and G overwrites the
+    //         staged gate tile
+    {
+        const int d = tid & 127, qt = __builtin_amdgcn_readfirstlane(tid >> 7);
+        const float* stg = sG + (qt < 2 ? kGateHi + 32 * qt * 128 : (32 * qt - 64) * 128) + d;
+        float x[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) x[i] = stg[i * 128] + sGt[32 * qt + i];
+        if (32 * qt + 31 >= r) {   // the chunk ends in this quarter
+#pragma unroll
+            for (int i = 0; i < 32; ++i) x[i] = 32 * qt + i < r ? x[i] : 0.f;
+        }
+#pragma unroll
+        for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
+        sD[qt * 128 + d] = x[31];
+        __syncthreads();
+        float off = 0.f;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) off += j < qt ? sD[j * 128 + d] : 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) sG[(32 * qt + i) * LDG + d] = x[i] + off;
+    }
+    __syncthreads();
+
+    // ---- 2. with G at hand: G_last and the block ends G_{16b+15} (sGb); the
+    //         decay between blocks (sC); q^ exp(G) -> workspace; the diagonal
+    //         blocks of P and L in fp32; then the scaled copies
+    //         KA = k^ exp(G - G_s), KB = k^ exp(G_e - G), QA = q^ exp(G - G_s)
+    //         (s: the token before the row's block, e: the block's last token)
+    if (tid < 128) p.gc[ch * 128 + tid] = sG[127 * LDG + tid];
+    for (int i = tid; i < 8 * 128; i += 512) sGb[i] = sG[((i >> 7) * 16 + 15) * LDG + (i & 127)];
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
         const int e_ = tid + 512 * n;
@@ -825,101 +907,136 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
         for (int e = 0; e < 8; ++e) y[e] = (float)x[e] * __expf(gv[e]);
         st_h8(p.qt + ch * TILE + (size_t)e_ * 8, to_h8(y));
     }
-    // One off-diagonal block product through the reference row s (the token
-    // before block I): sum over d of (X_a[d] exp(G_a[d] - G_s[d])) (Y_b[d]
-    // exp(G_s[d] - G_b[d])), a = rows of block IA of X, b = rows of block IB of Y.
-    auto off_tile = [&](const _Float16* X, int IA, const _Float16* Y, int IB, int s, bool a_down) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int ra = 16 * IA + lr, rb = 16 * IB + lr;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const int d0 = 32 * ks + 8 * lq;
-            const half8 xa = ld_h8(&X[ra * LD16 + d0]), yb = ld_h8(&Y[rb * LD16 + d0]);
-            float ga[8], gb[8], gs[8];
-            ld_f8(&sG[ra * LDG + d0], ga);
-            ld_f8(&sG[rb * LDG + d0], gb);
-            ld_f8(&sG[s * LDG + d0], gs);
-            float fa[8], fb[8];
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                // a_down: the A rows are the later block (exp(G_a - G_s));
-                // otherwise the B rows are (and A is the earlier block)
-                fa[e] = (float)xa[e] * __expf(a_down ? ga[e] - gs[e] : gs[e] - ga[e]);
-                fb[e] = (float)yb[e] * __expf(a_down ? gs[e] - gb[e] : gb[e] - gs[e]);
-            }
-            acc = mma(to_h8(fa), to_h8(fb), acc);
-        }
-        return acc;
-    };
-    // One diagonal block product in fp32 through the middle row m: lane (lr, lq)
-    // supplies keys d = 32 lq + kk of row 16 I + lr for both operands; the
-    // A rows (X) are the later token (exp(G_a - G_m)) unless `flip`.
-    auto diag_tile = [&](const _Float16* X, const _Float16* Y, int I, bool flip) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        const int rw = 16 * I + lr, m = 16 * I + 7;
+    // c[I][J][d] = exp(G_{16I-1}[d] - G_{16J+15}[d]) for block pairs J + 1 < I
+    // (pair index (I-2)(I-1)/2 + J), the decay between the blocks
+    for (int i = tid; i < 21 * 128; i += 512) {
+        const int pr_ = i >> 7, d = i & 127;
+        const int I = 2 + (pr_ >= 1) + (pr_ >= 3) + (pr_ >= 6) + (pr_ >= 10) + (pr_ >= 15);
+        const int J = pr_ - (I - 2) * (I - 1) / 2;
+        sC[i] = __expf(sG[(16 * I - 1) * LDG + d] - sG[(16 * J + 15) * LDG + d]);
+    }
+    // diagonal block Id of this wave (rows pair up as (pp, 7 - pp)), P and L
+    // together in fp32 through the block's middle row m: lane (lr, lq) supplies
+    // keys d = 32 lq + kk of row 16 Id + lr to both operands
+    const int pp = wave >> 1;
+    const int Id = (wave & 1) ? 7 - pp : pp;
+    f32x4 pdiag = {0.f, 0.f, 0.f, 0.f}, ldiag = {0.f, 0.f, 0.f, 0.f};
+    {
+        const int rw = 16 * Id + lr, m = 16 * Id + 7;
 #pragma unroll
         for (int c8 = 0; c8 < 4; ++c8) {
             const int d0 = 32 * lq + 8 * c8;
-            const half8 xa = ld_h8(&X[rw * LD16 + d0]), yb = ld_h8(&Y[rw * LD16 + d0]);
+            const half8 kx = ld_h8(&sK[rw * LD16 + d0]), qx = ld_h8(&sQL[rw * LD16 + d0]);
             float gr[8], gm[8];
             ld_f8(&sG[rw * LDG + d0], gr);
             ld_f8(&sG[m * LDG + d0], gm);
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc = mma_f32((float)xa[e] * __expf(flip ? gm[e] - gr[e] : gr[e] - gm[e]),
-                              (float)yb[e] * __expf(flip ? gr[e] - gm[e] : gm[e] - gr[e]), acc);
-        }
-        return acc;
-    };
-    // tiles by row pairs (pp, 7 - pp), as the intra kernel's Gram: every wave
-    // takes 4 or 5 tiles, one of them diagonal
-    const int pp = wave >> 1;
-    const int rowA = (wave & 1) ? 7 - pp : pp, J0A = (wave & 1) ? 4 - pp : 0, J1A = (wave & 1) ? 8 - pp : pp + 1;
-    const int rowB = 7 - pp, J1B = (wave & 1) ? 0 : 4 - pp;   // even waves: a second, off-diagonal run
-    auto p_row = [&](int I, int J0, int J1) {
-        for (int J = J0; J < J1; ++J) {
-            if (J < I) {
-                // A = k^ rows of block J (earlier), B = q^ rows of block I (later)
-                const f32x4 acc = off_tile(sK, J, sQL, I, 16 * I - 1, false);
-                st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * J + 4 * lq), to_h4(acc));
-            } else {
-                // C[j][i]: A = k^ rows j (earlier), B = q^ rows i (later)
-                const f32x4 acc = diag_tile(sK, sQL, I, true);
-                half4 o4;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(4 * lq + e <= lr ? acc[e] : 0.f);
-                st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * I + 4 * lq), o4);
-                if ((I & 1) == 0)   // the next block's columns, read by the output kernel's last k-step
-                    st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * (I + 1) + 4 * lq), half4{0, 0, 0, 0});
+            for (int e = 0; e < 8; ++e) {
+                const float up = __expf(gr[e] - gm[e]), dn = __expf(gm[e] - gr[e]);
+                const float kd = (float)kx[e] * dn;
+                pdiag = mma_f32(kd, (float)qx[e] * up, pdiag);   // C[j][i] = P[i][j]
+                if constexpr (kDelta) ldiag = mma_f32((float)kx[e] * up, kd, ldiag);   // C[i][j]
             }
         }
-    };
-    p_row(rowA, J0A, J1A);
-    p_row(rowB, 0, J1B);
-    __syncthreads();   // q^ is no longer needed: sQL becomes L (and the prefix totals in sD are done)
+    }
+    __syncthreads();   // the diagonal tiles are done with the plain k^, q^
+    half8 kb[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        // each thread rescales its own pieces in place
+        const int e_ = tid + 512 * n, t = e_ >> 4, d0 = 8 * (e_ & 15), I = t >> 4;
+        const half8 kx = ld_h8(&sK[t * LD16 + d0]), qx = ld_h8(&sQL[t * LD16 + d0]);
+        float gt[8], gs[8], ge[8];
+        ld_f8(&sG[t * LDG + d0], gt);
+        ld_f8(&sG[(16 * I + 15) * LDG + d0], ge);
+        if (I > 0) ld_f8(&sG[(16 * I - 1) * LDG + d0], gs);
+        else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) gs[e] = 0.f;
+        }
+        float a[8], b[8], q8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float fs = __expf(gt[e] - gs[e]);
+            a[e] = (float)kx[e] * fs;
+            q8[e] = (float)qx[e] * fs;
+            b[e] = (float)kx[e] * __expf(ge[e] - gt[e]);
+        }
+        st_h8(&sK[t * LD16 + d0], to_h8(a));
+        st_h8(&sQL[t * LD16 + d0], to_h8(q8));
+        kb[n] = to_h8(b);
+    }
+    __syncthreads();   // G is done: KB takes its place, the next gate tile's first half goes behind it
+    gk_place<ActT>(st, p, next);
+    gk_gate_dma(p, st.t0, st.h, st.r, sG, 0, tid);
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int e_ = tid + 512 * n, t = e_ >> 4, d0 = 8 * (e_ & 15);
+        st_h8(&sKB[t * LD16 + d0], kb[n]);
+    }
+    __syncthreads();
 
-    // ---- 4. L = strictlower(beta_i sum_d k^_i[d] k^_j[d] exp(G_i[d] - G_j[d]))
-    //         -> sQL (fp16, zeros above the block diagonal), diagonal blocks also fp32 in sD
-    _Float16* sL = sQL;
-    auto l_row = [&](int I, int J0, int J1) {
-        for (int J = J0; J < J1; ++J) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if constexpr (kDelta) {
-                // C[i][j]: A = k^ rows of block I (later), B = k^ rows of block J
-                acc = J < I ? off_tile(sK, I, sK, J, 16 * I - 1, true) : diag_tile(sK, sK, I, false);
-            }
-            const int j = 16 * J + lr;
+    gk_load_in<ActT, RULE>(st, p, 0, tid);   // the next item's k
+    // ---- 3. off-diagonal blocks J < I of P and L together: with KBc = KB_J c[I][J]
+    //         (c = 1 when J = I - 1), P^T tile C[j][i] = sum_d KBc[j][d] QA[i][d]
+    //         -> workspace; L tile C[i][j] = sum_d KA[i][d] KBc[j][d], kept in
+    //         registers until QA is done
+    const int J0A = (wave & 1) ? 4 - pp : 0, nA = Id - J0A;   // row Id: tiles J0A .. Id - 1
+    const int rowB = 7 - pp, nT = nA + ((wave & 1) ? 0 : 4 - pp);   // even waves: row 7 - pp, tiles 0 ..
+    f32x4 lacc[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 16 * I + 4 * lq + e;
-                const float Lij = (kDelta && i > j) ? sBw[i] * acc[e] : 0.f;
-                sL[i * LD16 + j] = (_Float16)Lij;
-                if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
+    for (int tt = 0; tt < 4; ++tt) {
+        lacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (tt < nT) {
+            const int I = tt < nA ? Id : rowB, J = tt < nA ? J0A + tt : tt - nA;
+            const float* cIJ = &sC[((I - 2) * (I - 1) / 2 + J) * 128];
+            f32x4 pacc = {0.f, 0.f, 0.f, 0.f}, la = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                const int d0 = 32 * ks + 8 * lq;
+                half8 kb = ld_h8(&sKB[(16 * J + lr) * LD16 + d0]);
+                if (J + 1 < I) {
+                    float cc[8], y[8];
+                    ld_f8(&cIJ[d0], cc);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) y[e] = (float)kb[e] * cc[e];
+                    kb = to_h8(y);
+                }
+                pacc = mma(kb, ld_h8(&sQL[(16 * I + lr) * LD16 + d0]), pacc);
+                if constexpr (kDelta) la = mma(ld_h8(&sK[(16 * I + lr) * LD16 + d0]), kb, la);
             }
+            st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * J + 4 * lq), to_h4(pacc));
+            lacc[tt] = la;
+        }
+    }
+    {
+        half4 o4;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(4 * lq + e <= lr ? pdiag[e] : 0.f);
+        st_h4(p.pm + ch * TILE + frag_off(16 * Id + lr, 16 * Id + 4 * lq), o4);
+        if ((Id & 1) == 0)   // the next block's columns, read by the output kernel's last k-step
+            st_h4(p.pm + ch * TILE + frag_off(16 * Id + lr, 16 * (Id + 1) + 4 * lq), half4{0, 0, 0, 0});
+    }
+    __syncthreads();   // QA is done: sQL becomes L
+    gk_gate_dma(p, st.t0, st.h, st.r, sG, 1, tid);
+
+    // ---- 4. L = strictlower(beta_i sum_d k^_i k^_j exp(G_i - G_j)) -> sL (fp16,
+    //         zeros above the block diagonal), diagonal blocks also fp32 in sD
+    _Float16* sL = sQL;
+    auto l_store = [&](int I, int J, const f32x4& acc) {
+        const int j = 16 * J + lr;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int i = 16 * I + 4 * lq + e;
+            const float Lij = (kDelta && i > j) ? sBw[i] * acc[e] : 0.f;
+            sL[i * LD16 + j] = (_Float16)Lij;
+            if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
         }
     };
-    l_row(rowA, J0A, J1A);
-    l_row(rowB, 0, J1B);
+#pragma unroll
+    for (int tt = 0; tt < 4; ++tt)
+        if (tt < nT) l_store(tt < nA ? Id : rowB, tt < nA ? J0A + tt : tt - nA, lacc[tt]);
+    l_store(Id, Id, ldiag);
     {
         const int i = tid >> 2, I = i >> 4;
         const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -930,7 +1047,8 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     for (int i = 0; i < 8; ++i) kt[i] = ld_h4(&sK[(8 * tg + i) * LD16 + 4 * c4]);
     __syncthreads();
 
-    // ---- 5. k^T into sK (swizzled); inverses of the diagonal blocks T_bb = (I + L_bb)^-1
+    // ---- 5. KA^T into sK (swizzled); inverses of the diagonal blocks T_bb = (I + L_bb)^-1
+    gk_load_in<ActT, RULE>(st, p, 1, tid);   // the next item's q
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         half8 col;
@@ -954,18 +1072,18 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     }
     __syncthreads();
 
-    // ---- 6. k^T exp(G_last - G) -> workspace (fragment order, per value head);
-    //         column block j = wave of T by forward substitution
+    // ---- 6. k^T exp(G_last - G) = KB^T exp(G_last - G_e) -> workspace (fragment
+    //         order, per value head); column block j = wave of T by forward substitution
+    gk_load_in<ActT, RULE>(st, p, 2, tid);   // the next item's g and beta
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
         const int e_ = tid + 512 * n;
         int dk, kc;
-        frag_piece(e_, dk, kc);
-        const half8 x = ld_h8(&sK[sw(dk, kc)]);
-        const float gl = sG[127 * LDG + dk];
+        frag_piece(e_, dk, kc);   // 8 tokens kc .. kc + 7, all in block kc / 16
+        const float f = __expf(sGb[7 * 128 + dk] - sGb[(kc >> 4) * 128 + dk]);
         float y[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (float)x[e] * __expf(gl - sG[(kc + e) * LDG + dk]);
+        for (int e = 0; e < 8; ++e) y[e] = (float)sKB[(kc + e) * LD16 + dk] * f;
         st_h8(p.khatT + ch * TILE + (size_t)e_ * 8, to_h8(y));
     }
     half4 xh[8];
@@ -994,9 +1112,14 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
             xh[b] = to_h4(x);
         }
     }
-    __syncthreads();
+    __syncthreads();   // KB is done
+    gk_load_v<ActT>(st, p, t0, h, r, 0, tid);        // this item's v, used in step 9
+    gk_gate_dma(p, st.t0, st.h, st.r, sG, 2, tid);   // the next gate tile's third quarter
 
     // ---- 7. T (fp16) into sL over L; sK scaled in place to (k^ beta exp(G))^T
+    //         = KA^T beta exp(G_s) (8 tokens of one block per piece)
+    {
+    GK_IDS();
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         if (b < wave) continue;
@@ -1005,19 +1128,21 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     }
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, dk = e_ >> 4, gg = e_ & 15;
+        const int e_ = tid + 512 * n, dk = e_ >> 4, gg = e_ & 15, I = gg >> 1;
         _Float16* pk = &sK[sw(dk, 8 * gg)];
         half8 x = ld_h8(pk);
+        const float f = I > 0 ? __expf(sGb[(I - 1) * 128 + dk]) : 1.f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int t = 8 * gg + e;
-            x[e] = (_Float16)((float)x[e] * sBw[t] * __expf(sG[t * LDG + dk]));
-        }
+        for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * sBw[8 * gg + e] * f);
         st_h8(pk, x);
+    }
     }
     __syncthreads();
 
     // ---- 8. w^T = (k^ beta exp(G))^T T^T -> w [tok][dk], fragment order
+    {
+    GK_IDS();
+    gk_load_v<ActT>(st, p, t0, h, r, 1, tid);
     const int pr = wave & 3, hsel = wave >> 2;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
@@ -1035,13 +1160,16 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
         for (int ii = 0; ii < 4; ++ii)
             st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * (4 * hsel + ii) + 4 * lq), to_h4(acc[ii]));
     }
+    }
     __syncthreads();
 
     // ---- 9. (v beta)^T [col][tok] into sK
     {
+        GK_IDS();
+        gk_gate_dma(p, st.t0, st.h, st.r, sG, 3, tid);   // the next gate tile's last quarter
         float vf[8][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) raw_cvt(vr[i], vf[i]);
+        for (int i = 0; i < 8; ++i) raw_cvt(st.v[i], vf[i]);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             half8 col;
@@ -1053,6 +1181,9 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     __syncthreads();
 
     // ---- 10. u = T (v beta) -> u, fragment order
+    {
+    GK_IDS();
+    const int pr = wave & 3, hsel = wave >> 2;
 #pragma unroll
     for (int which = 0; which < 2; ++which) {
         const int I = which ? 7 - pr : pr;
@@ -1069,6 +1200,44 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
         for (int jj = 0; jj < 4; ++jj)
             st_h4(p.u + ch * TILE + cfrag_off(16 * I + 4 * lq, 16 * (4 * hsel + jj) + lr), to_h4(acc[jj]));
     }
+    }
+}
+
+// Persistent over items blockIdx.x, blockIdx.x + gridDim.x, ... (item =
+// chunk * Nv + value head), one workgroup per CU.  Each item fetches the
+// next one's inputs a little at a time over its own pass (the workgroups
+// run in step, and a whole item's worth at once from all of them stalls on
+// memory): the gate tile by quarters into LDS (the first half once G is
+// done, the second once KB is done), k, q, g and beta into registers
+// between; its own v in two halves before it is used.
+template <typename ActT, int RULE>
+__global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
+    __shared__ __align__(16) float sG[128 * LDG];          // gate tile (staged) -> G [tok][dk]; then KB [tok][dk] fp16
+    __shared__ __align__(16) _Float16 sK[128 * LD16];      // k^ -> KA -> KA^T (swizzled) -> (v beta)^T
+    __shared__ __align__(16) _Float16 sQL[128 * LD16];     // q^ -> QA -> L / T
+    __shared__ float sD[8 * 16 * 17];                      // (first: per-quarter prefix totals)
+    __shared__ __align__(16) float sGb[8 * 128];           // G at the blocks' last rows
+    __shared__ __align__(16) float sC[21 * 128];           // decay between blocks J + 1 < I
+    __shared__ float sGt[128], sBeta[128], sBw[128];
+    const int tid = threadIdx.x;
+    const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
+    const int stride = gridDim.x;   // a multiple of 8 G
+    int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
+    if (it >= n_items) return;
+    GkStage<ActT> st;
+    gk_place<ActT>(st, p, it);
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) gk_gate_dma(p, st.t0, st.h, st.r, sG, q4, tid);
+    gk_load_in<ActT, RULE>(st, p, 0, tid);
+    gk_load_in<ActT, RULE>(st, p, 1, tid);
+    gk_load_in<ActT, RULE>(st, p, 2, tid);
+    while (true) {
+        const int nx = it + stride;
+        gk_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sG, sK, sQL, sD, sGb, sC, sGt, sBeta, sBw, tid);
+        if (nx >= n_items) break;
+        it = nx;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no load into LDS outlives the workgroup
 }
 
 // ------------------------------------------------------------------ K2: state scan
@@ -1717,8 +1886,8 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         timing_begin(kIntra, stream);
         if (gk) {
-            // one workgroup per item and per CU (LDS about 145 KiB)
-            const dim3 grid((unsigned)((nwg + g8 - 1) / g8 * g8));
+            // persistent: one workgroup per CU (LDS about 158 KiB), each walking items
+            const dim3 grid((unsigned)(((nwg < (size_t)ncu ? nwg : (size_t)ncu) + g8 - 1) / g8 * g8));
             if (a.rule == 2) launch_intra_gk_rule<2>(act, grid, stream, p);
             else launch_intra_gk_rule<0>(act, grid, stream, p);
         } else {
