@@ -777,6 +777,11 @@ __device__ __forceinline__ void lds_load16(const float* src, float* dst) {
 // from float kGateHi on (behind KB, which takes the first 128 LD16 halves'
 // rows), tokens 64..127 from 0 (free once KB is done).
 constexpr int kGateHi = 128 * LD16 / 2;
+// Largest |G_i - G_m| (G: the chunk-local log decay, m: a 16-token block's
+// middle row) for which the block's diagonal tiles are taken in fp16: the
+// scaled operands then stay within e^6, and a subnormal one errs by at most
+// e^6 2^-25 in a product.
+constexpr float kDiagF16Range = 6.f;
 static_assert(kGateHi + 64 * 128 <= 128 * LDG, "gate staging fits G's region");
 
 // Quarter q4 of the gate tile of the item at (t0, h, r) (tokens 32 q4 ..
@@ -806,8 +811,8 @@ __device__ __forceinline__ void gk_gate_dma(const PrefillDev& p, int t0, int h, 
 
 template <typename ActT, int RULE>
 __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const PrefillDev& p, float* sG, _Float16* sK,
-                                        _Float16* sQL, float* sD, float* sGb, float* sC, float* sGt, float* sBeta,
-                                        float* sBw, int tid_in) {
+                                        _Float16* sQL, float* sD, float* sEs, float* sTail, _Float16* sC, float* sGt,
+                                        float* sBeta, float* sBw, int* sWide, int tid_in) {
     int tid = tid_in;
     asm volatile("" : "+v"(tid));
     constexpr bool kDelta = Rule<RULE>::delta;
@@ -879,6 +884,19 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
 #pragma unroll
         for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
         sD[qt * 128 + d] = x[31];
+        // blocks 2 qt, 2 qt + 1: is every |G_i - G_m| (m: the block's middle
+        // row) within kDiagF16Range, for this wave's 64 keys?
+        bool wide0 = false, wide1 = false;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            wide0 |= !(fabsf(x[i] - x[7]) <= kDiagF16Range);
+            wide1 |= !(fabsf(x[16 + i] - x[23]) <= kDiagF16Range);
+        }
+        const bool w0 = __ballot(wide0) != 0, w1 = __ballot(wide1) != 0;
+        if ((tid & 63) == 0) {
+            sWide[(2 * qt) * 2 + (d >> 6)] = w0;
+            sWide[(2 * qt + 1) * 2 + (d >> 6)] = w1;
+        }
         __syncthreads();
         float off = 0.f;
 #pragma unroll
@@ -888,54 +906,92 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     }
     __syncthreads();
 
-    // ---- 2. with G at hand: G_last and the block ends G_{16b+15} (sGb); the
-    //         decay between blocks (sC); q^ exp(G) -> workspace; the diagonal
-    //         blocks of P and L in fp32; then the scaled copies
-    //         KA = k^ exp(G - G_s), KB = k^ exp(G_e - G), QA = q^ exp(G - G_s)
-    //         (s: the token before the row's block, e: the block's last token)
-    if (tid < 128) p.gc[ch * 128 + tid] = sG[127 * LDG + tid];
-    for (int i = tid; i < 8 * 128; i += 512) sGb[i] = sG[((i >> 7) * 16 + 15) * LDG + (i & 127)];
+    // ---- 2. with G at hand: per key d, from the block ends G_e[K] = G_{16K+15}
+    //         and the block decays D[K] = exp(G_e[K] - G_e[K-1]), by running
+    //         products: exp(G_s) of each block (sEs; s: the token before the
+    //         block), exp(G_last - G_e) (sTail) and the decay between blocks
+    //         J + 1 < I, c = exp(G_s(I) - G_e(J)) (sC, fp16: it only scales
+    //         fp16 products); G_last -> workspace.  Then the diagonal blocks of
+    //         P and L in fp32, and the scaled copies KA = k^ exp(G - G_s),
+    //         KB = k^ exp(G_e - G), QA = q^ exp(G - G_s), with q^ exp(G) =
+    //         QA exp(G_s) -> workspace
+    if (tid < 128) {
+        const int d = tid;
+        float ge[8], D[8];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n;
-        int rw, kc;
-        frag_piece(e_, rw, kc);
-        const half8 x = ld_h8(&sQL[rw * LD16 + kc]);
-        float gv[8], y[8];
-        ld_f8(&sG[rw * LDG + kc], gv);
+        for (int K = 0; K < 8; ++K) ge[K] = sG[(16 * K + 15) * LDG + d];
+        p.gc[ch * 128 + d] = ge[7];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (float)x[e] * __expf(gv[e]);
-        st_h8(p.qt + ch * TILE + (size_t)e_ * 8, to_h8(y));
-    }
-    // c[I][J][d] = exp(G_{16I-1}[d] - G_{16J+15}[d]) for block pairs J + 1 < I
-    // (pair index (I-2)(I-1)/2 + J), the decay between the blocks
-    for (int i = tid; i < 21 * 128; i += 512) {
-        const int pr_ = i >> 7, d = i & 127;
-        const int I = 2 + (pr_ >= 1) + (pr_ >= 3) + (pr_ >= 6) + (pr_ >= 10) + (pr_ >= 15);
-        const int J = pr_ - (I - 2) * (I - 1) / 2;
-        sC[i] = __expf(sG[(16 * I - 1) * LDG + d] - sG[(16 * J + 15) * LDG + d]);
+        for (int K = 1; K < 8; ++K) D[K] = __expf(ge[K] - ge[K - 1]);
+        float es = 1.f, tl = 1.f;
+        sEs[d] = 1.f;
+#pragma unroll
+        for (int I = 1; I < 8; ++I) {
+            es = I == 1 ? __expf(ge[0]) : es * D[I - 1];
+            sEs[I * 128 + d] = es;
+        }
+        sTail[7 * 128 + d] = 1.f;
+#pragma unroll
+        for (int J = 6; J >= 0; --J) {
+            tl *= D[J + 1];
+            sTail[J * 128 + d] = tl;
+        }
+#pragma unroll
+        for (int J = 0; J < 6; ++J) {
+            float cc = 1.f;
+#pragma unroll
+            for (int I = J + 2; I < 8; ++I) {
+                cc *= D[I - 1];
+                sC[((I - 2) * (I - 1) / 2 + J) * 128 + d] = (_Float16)cc;
+            }
+        }
     }
     // diagonal block Id of this wave (rows pair up as (pp, 7 - pp)), P and L
-    // together in fp32 through the block's middle row m: lane (lr, lq) supplies
-    // keys d = 32 lq + kk of row 16 Id + lr to both operands
+    // together through the block's middle row m: lane (lr, lq) supplies keys
+    // d = 32 lq + 8 c8 + e of row 16 Id + lr to both operands, scaled by
+    // exp(+-(G_row - G_m)).  In fp16 when every |G_row - G_m| of the block is
+    // within kDiagF16Range (operands at most e^6, as precise as the other
+    // tiles), else in fp32.
     const int pp = wave >> 1;
     const int Id = (wave & 1) ? 7 - pp : pp;
     f32x4 pdiag = {0.f, 0.f, 0.f, 0.f}, ldiag = {0.f, 0.f, 0.f, 0.f};
     {
         const int rw = 16 * Id + lr, m = 16 * Id + 7;
+        const bool narrow = __builtin_amdgcn_readfirstlane(sWide[2 * Id] | sWide[2 * Id + 1]) == 0;
+        if (narrow) {
 #pragma unroll
-        for (int c8 = 0; c8 < 4; ++c8) {
-            const int d0 = 32 * lq + 8 * c8;
-            const half8 kx = ld_h8(&sK[rw * LD16 + d0]), qx = ld_h8(&sQL[rw * LD16 + d0]);
-            float gr[8], gm[8];
-            ld_f8(&sG[rw * LDG + d0], gr);
-            ld_f8(&sG[m * LDG + d0], gm);
+            for (int c8 = 0; c8 < 4; ++c8) {
+                const int d0 = 32 * lq + 8 * c8;
+                const half8 kx = ld_h8(&sK[rw * LD16 + d0]), qx = ld_h8(&sQL[rw * LD16 + d0]);
+                float gr[8], gm[8], kd[8], qu[8], ku[8];
+                ld_f8(&sG[rw * LDG + d0], gr);
+                ld_f8(&sG[m * LDG + d0], gm);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const float up = __expf(gr[e] - gm[e]), dn = __expf(gm[e] - gr[e]);
-                const float kd = (float)kx[e] * dn;
-                pdiag = mma_f32(kd, (float)qx[e] * up, pdiag);   // C[j][i] = P[i][j]
-                if constexpr (kDelta) ldiag = mma_f32((float)kx[e] * up, kd, ldiag);   // C[i][j]
+                for (int e = 0; e < 8; ++e) {
+                    const float up = __expf(gr[e] - gm[e]), dn = __expf(gm[e] - gr[e]);
+                    kd[e] = (float)kx[e] * dn;
+                    qu[e] = (float)qx[e] * up;
+                    ku[e] = (float)kx[e] * up;
+                }
+                const half8 kdh = to_h8(kd);
+                pdiag = mma(kdh, to_h8(qu), pdiag);                      // C[j][i] = P[i][j]
+                if constexpr (kDelta) ldiag = mma(to_h8(ku), kdh, ldiag);   // C[i][j]
+            }
+        } else {
+#pragma unroll
+            for (int c8 = 0; c8 < 4; ++c8) {
+                const int d0 = 32 * lq + 8 * c8;
+                const half8 kx = ld_h8(&sK[rw * LD16 + d0]), qx = ld_h8(&sQL[rw * LD16 + d0]);
+                float gr[8], gm[8];
+                ld_f8(&sG[rw * LDG + d0], gr);
+                ld_f8(&sG[m * LDG + d0], gm);
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const float up = __expf(gr[e] - gm[e]), dn = __expf(gm[e] - gr[e]);
+                    const float kd = (float)kx[e] * dn;
+                    pdiag = mma_f32(kd, (float)qx[e] * up, pdiag);   // C[j][i] = P[i][j]
+                    if constexpr (kDelta) ldiag = mma_f32((float)kx[e] * up, kd, ldiag);   // C[i][j]
+                }
             }
         }
     }
@@ -946,24 +1002,27 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         // each thread rescales its own pieces in place
         const int e_ = tid + 512 * n, t = e_ >> 4, d0 = 8 * (e_ & 15), I = t >> 4;
         const half8 kx = ld_h8(&sK[t * LD16 + d0]), qx = ld_h8(&sQL[t * LD16 + d0]);
-        float gt[8], gs[8], ge[8];
+        float gt[8], gs[8], ge[8], es[8];
         ld_f8(&sG[t * LDG + d0], gt);
         ld_f8(&sG[(16 * I + 15) * LDG + d0], ge);
+        ld_f8(&sEs[I * 128 + d0], es);
         if (I > 0) ld_f8(&sG[(16 * I - 1) * LDG + d0], gs);
         else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) gs[e] = 0.f;
         }
-        float a[8], b[8], q8[8];
+        float a[8], b[8], q8[8], qt8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float fs = __expf(gt[e] - gs[e]);
             a[e] = (float)kx[e] * fs;
             q8[e] = (float)qx[e] * fs;
+            qt8[e] = q8[e] * es[e];
             b[e] = (float)kx[e] * __expf(ge[e] - gt[e]);
         }
         st_h8(&sK[t * LD16 + d0], to_h8(a));
         st_h8(&sQL[t * LD16 + d0], to_h8(q8));
+        st_h8(p.qt + ch * TILE + frag_off(t, d0), to_h8(qt8));
         kb[n] = to_h8(b);
     }
     __syncthreads();   // G is done: KB takes its place, the next gate tile's first half goes behind it
@@ -989,19 +1048,13 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         lacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tt < nT) {
             const int I = tt < nA ? Id : rowB, J = tt < nA ? J0A + tt : tt - nA;
-            const float* cIJ = &sC[((I - 2) * (I - 1) / 2 + J) * 128];
+            const _Float16* cIJ = &sC[((I - 2) * (I - 1) / 2 + J) * 128];
             f32x4 pacc = {0.f, 0.f, 0.f, 0.f}, la = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) {
                 const int d0 = 32 * ks + 8 * lq;
                 half8 kb = ld_h8(&sKB[(16 * J + lr) * LD16 + d0]);
-                if (J + 1 < I) {
-                    float cc[8], y[8];
-                    ld_f8(&cIJ[d0], cc);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) y[e] = (float)kb[e] * cc[e];
-                    kb = to_h8(y);
-                }
+                if (J + 1 < I) kb = kb * ld_h8(&cIJ[d0]);
                 pacc = mma(kb, ld_h8(&sQL[(16 * I + lr) * LD16 + d0]), pacc);
                 if constexpr (kDelta) la = mma(ld_h8(&sK[(16 * I + lr) * LD16 + d0]), kb, la);
             }
@@ -1080,7 +1133,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         const int e_ = tid + 512 * n;
         int dk, kc;
         frag_piece(e_, dk, kc);   // 8 tokens kc .. kc + 7, all in block kc / 16
-        const float f = __expf(sGb[7 * 128 + dk] - sGb[(kc >> 4) * 128 + dk]);
+        const float f = sTail[(kc >> 4) * 128 + dk];
         float y[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) y[e] = (float)sKB[(kc + e) * LD16 + dk] * f;
@@ -1131,7 +1184,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         const int e_ = tid + 512 * n, dk = e_ >> 4, gg = e_ & 15, I = gg >> 1;
         _Float16* pk = &sK[sw(dk, 8 * gg)];
         half8 x = ld_h8(pk);
-        const float f = I > 0 ? __expf(sGb[(I - 1) * 128 + dk]) : 1.f;
+        const float f = sEs[I * 128 + dk];
 #pragma unroll
         for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * sBw[8 * gg + e] * f);
         st_h8(pk, x);
@@ -1216,9 +1269,11 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sK[128 * LD16];      // k^ -> KA -> KA^T (swizzled) -> (v beta)^T
     __shared__ __align__(16) _Float16 sQL[128 * LD16];     // q^ -> QA -> L / T
     __shared__ float sD[8 * 16 * 17];                      // (first: per-quarter prefix totals)
-    __shared__ __align__(16) float sGb[8 * 128];           // G at the blocks' last rows
-    __shared__ __align__(16) float sC[21 * 128];           // decay between blocks J + 1 < I
+    __shared__ __align__(16) float sEs[8 * 128];           // exp(G) at the token before each block
+    __shared__ __align__(16) float sTail[8 * 128];         // exp(G_last - G) at each block's last token
+    __shared__ __align__(16) _Float16 sC[21 * 128];        // decay between blocks J + 1 < I
     __shared__ float sGt[128], sBeta[128], sBw[128];
+    __shared__ int sWide[16];                              // per block and key half: |G - G_m| too wide for fp16
     const int tid = threadIdx.x;
     const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
     const int stride = gridDim.x;   // a multiple of 8 G
@@ -1233,7 +1288,7 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     gk_load_in<ActT, RULE>(st, p, 2, tid);
     while (true) {
         const int nx = it + stride;
-        gk_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sG, sK, sQL, sD, sGb, sC, sGt, sBeta, sBw, tid);
+        gk_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sG, sK, sQL, sD, sEs, sTail, sC, sGt, sBeta, sBw, sWide, tid);
         if (nx >= n_items) break;
         it = nx;
     }
