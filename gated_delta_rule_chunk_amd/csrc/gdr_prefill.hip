@@ -975,7 +975,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
                 }
                 const half8 kdh = to_h8(kd);
                 pdiag = mma(kdh, to_h8(qu), pdiag);                      // C[j][i] = P[i][j]
-                if constexpr (kDelta) ldiag = mma(to_h8(ku), kdh, ldiag);   // C[i][j]
+                if constexpr (kDelta) ldiag = mma(kdh, to_h8(ku), ldiag);   // C[j][i] = L[i][j]
             }
         } else {
 #pragma unroll
@@ -990,20 +990,18 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
                     const float up = __expf(gr[e] - gm[e]), dn = __expf(gm[e] - gr[e]);
                     const float kd = (float)kx[e] * dn;
                     pdiag = mma_f32(kd, (float)qx[e] * up, pdiag);   // C[j][i] = P[i][j]
-                    if constexpr (kDelta) ldiag = mma_f32((float)kx[e] * up, kd, ldiag);   // C[i][j]
+                    if constexpr (kDelta) ldiag = mma_f32(kd, (float)kx[e] * up, ldiag);   // C[j][i] = L[i][j]
                 }
             }
         }
     }
     __syncthreads();   // the diagonal tiles are done with the plain k^, q^
     half8 kb[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        // each thread rescales its own pieces in place
-        const int e_ = tid + 512 * n, t = e_ >> 4, d0 = 8 * (e_ & 15), I = t >> 4;
-        const half8 kx = ld_h8(&sK[t * LD16 + d0]), qx = ld_h8(&sQL[t * LD16 + d0]);
-        float gt[8], gs[8], ge[8], es[8];
-        ld_f8(&sG[t * LDG + d0], gt);
+    {
+        // each thread rescales its own pieces in place: rows 4 rg .. 4 rg + 3
+        // (one block I), keys d0 .. d0 + 7
+        const int d0 = 8 * (tid & 15), rg = tid >> 4, I = rg >> 2;
+        float gs[8], ge[8], es[8];
         ld_f8(&sG[(16 * I + 15) * LDG + d0], ge);
         ld_f8(&sEs[I * 128 + d0], es);
         if (I > 0) ld_f8(&sG[(16 * I - 1) * LDG + d0], gs);
@@ -1011,6 +1009,12 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
 #pragma unroll
             for (int e = 0; e < 8; ++e) gs[e] = 0.f;
         }
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        const int t = 4 * rg + n;
+        const half8 kx = ld_h8(&sK[t * LD16 + d0]), qx = ld_h8(&sQL[t * LD16 + d0]);
+        float gt[8];
+        ld_f8(&sG[t * LDG + d0], gt);
         float a[8], b[8], q8[8], qt8[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -1025,20 +1029,19 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         st_h8(p.qt + ch * TILE + frag_off(t, d0), to_h8(qt8));
         kb[n] = to_h8(b);
     }
+    }
     __syncthreads();   // G is done: KB takes its place, the next gate tile's first half goes behind it
     gk_place<ActT>(st, p, next);
     gk_gate_dma(p, st.t0, st.h, st.r, sG, 0, tid);
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, t = e_ >> 4, d0 = 8 * (e_ & 15);
-        st_h8(&sKB[t * LD16 + d0], kb[n]);
-    }
+    for (int n = 0; n < 4; ++n) st_h8(&sKB[(4 * (tid >> 4) + n) * LD16 + 8 * (tid & 15)], kb[n]);
     __syncthreads();
 
     gk_load_in<ActT, RULE>(st, p, 0, tid);   // the next item's k
     // ---- 3. off-diagonal blocks J < I of P and L together: with KBc = KB_J c[I][J]
     //         (c = 1 when J = I - 1), P^T tile C[j][i] = sum_d KBc[j][d] QA[i][d]
-    //         -> workspace; L tile C[i][j] = sum_d KA[i][d] KBc[j][d], kept in
+    //         -> workspace; L^T tile C[j][i] = sum_d KBc[j][d] KA[i][d] (a lane
+    //         then holds 4 consecutive columns of a row of L), kept in
     //         registers until QA is done
     const int J0A = (wave & 1) ? 4 - pp : 0, nA = Id - J0A;   // row Id: tiles J0A .. Id - 1
     const int rowB = 7 - pp, nT = nA + ((wave & 1) ? 0 : 4 - pp);   // even waves: row 7 - pp, tiles 0 ..
@@ -1056,7 +1059,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
                 half8 kb = ld_h8(&sKB[(16 * J + lr) * LD16 + d0]);
                 if (J + 1 < I) kb = kb * ld_h8(&cIJ[d0]);
                 pacc = mma(kb, ld_h8(&sQL[(16 * I + lr) * LD16 + d0]), pacc);
-                if constexpr (kDelta) la = mma(ld_h8(&sK[(16 * I + lr) * LD16 + d0]), kb, la);
+                if constexpr (kDelta) la = mma(kb, ld_h8(&sK[(16 * I + lr) * LD16 + d0]), la);
             }
             st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * J + 4 * lq), to_h4(pacc));
             lacc[tt] = la;
@@ -1076,15 +1079,17 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     // ---- 4. L = strictlower(beta_i sum_d k^_i k^_j exp(G_i - G_j)) -> sL (fp16,
     //         zeros above the block diagonal), diagonal blocks also fp32 in sD
     _Float16* sL = sQL;
-    auto l_store = [&](int I, int J, const f32x4& acc) {
-        const int j = 16 * J + lr;
+    auto l_store = [&](int I, int J, const f32x4& acc) {   // acc[e] = L[16 I + lr][16 J + 4 lq + e]
+        const int i = 16 * I + lr, j0 = 16 * J + 4 * lq;
+        const float bi = sBw[i];
+        half4 o;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * lq + e;
-            const float Lij = (kDelta && i > j) ? sBw[i] * acc[e] : 0.f;
-            sL[i * LD16 + j] = (_Float16)Lij;
-            if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
+            const float Lij = (kDelta && i > j0 + e) ? bi * acc[e] : 0.f;
+            o[e] = (_Float16)Lij;
+            if (I == J) sD[i * 17 + 4 * lq + e] = Lij;
         }
+        st_h4(&sL[i * LD16 + j0], o);
     };
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt)
@@ -1126,18 +1131,25 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     __syncthreads();
 
     // ---- 6. k^T exp(G_last - G) = KB^T exp(G_last - G_e) -> workspace (fragment
-    //         order, per value head); column block j = wave of T by forward substitution
+    //         order, per value head: two adjacent pieces, keys dk and dk + 1,
+    //         per thread and pass); column block j = wave of T by forward
+    //         substitution
     gk_load_in<ActT, RULE>(st, p, 2, tid);   // the next item's g and beta
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n;
+    for (int n = 0; n < 2; ++n) {
+        const int e_ = 2 * (tid + 512 * n);
         int dk, kc;
-        frag_piece(e_, dk, kc);   // 8 tokens kc .. kc + 7, all in block kc / 16
-        const float f = sTail[(kc >> 4) * 128 + dk];
-        float y[8];
+        frag_piece(e_, dk, kc);   // dk even; 8 tokens kc .. kc + 7, all in block kc / 16
+        const float f0 = sTail[(kc >> 4) * 128 + dk], f1 = sTail[(kc >> 4) * 128 + dk + 1];
+        float y0[8], y1[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) y[e] = (float)sKB[(kc + e) * LD16 + dk] * f;
-        st_h8(p.khatT + ch * TILE + (size_t)e_ * 8, to_h8(y));
+        for (int e = 0; e < 8; ++e) {
+            const half2v x = *reinterpret_cast<const half2v*>(&sKB[(kc + e) * LD16 + dk]);
+            y0[e] = (float)x[0] * f0;
+            y1[e] = (float)x[1] * f1;
+        }
+        st_h8(p.khatT + ch * TILE + (size_t)e_ * 8, to_h8(y0));
+        st_h8(p.khatT + ch * TILE + (size_t)e_ * 8 + 8, to_h8(y1));
     }
     half4 xh[8];
     {
