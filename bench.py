@@ -243,12 +243,13 @@ def time_config(n, args, gdr, torch, workloads):
     dev = "cuda:0"
     d = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     if "cu_seqlens" in inp:
-        ws = torch.empty(gdr.chunk_prefill_workspace_size(inp["T"], inp["B"], inp["Nqk"], inp["Nv"]),
+        ws = torch.empty(gdr.chunk_prefill_workspace_size(inp["T"], inp["B"], inp["Nqk"], inp["Nv"],
+                                                          gk=inp.get("gk") is not None),
                          dtype=torch.uint8, device=dev)
 
         def f(i):
             gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["scale"],
-                              state_in=d["state_in"], workspace=ws)
+                              state_in=d["state_in"], workspace=ws, gk=d.get("gk"))
         ntok = inp["T"]
     else:
         def f(i):

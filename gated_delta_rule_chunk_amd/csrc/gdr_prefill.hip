@@ -676,8 +676,8 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
 }
 
 // ------------------------------------------------------------------ K1 with a per-key gate
-// One workgroup per (chunk, value head) item, 8 waves, one workgroup per CU
-// (LDS about 145 KiB).  With a per-key gate gk the decay from token j to
+// Persistent workgroups of 8 waves, one per CU (LDS about 157 KiB), walking
+// (chunk, value head) items.  With a per-key gate gk the decay from token j to
 // token i >= j of state row d is exp(G_i[d] - G_j[d]), G the chunk-local
 // inclusive prefix of g + gk[d] ("LinearAttention" page: per-key decay; the
 // decode page's S <- S exp(g) exp(gk) at every token), so the decayed
@@ -687,7 +687,10 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
 //          exp(G_i - G_j) = exp(G_i - G_s) exp(G_s - G_j), both factors
 //          <= 1, so the MFMA operands are scaled keys / queries (fp16);
 //   J = I  through G at the block's middle row m = 16 I + 7: factors up to
-//          exp(8 max|g + gk|), so in fp32, on the 16x16x4 fp32 MFMA.
+//          exp(8 max|g + gk|); in fp16 when every |G_i - G_m| of the block
+//          is within kDiagF16Range, else in fp32 on the 16x16x4 fp32 MFMA.
+// The decay between blocks, exp(G_s(I) - G_e(J)), and the per-block factors
+// come from running products of the block decays, not per element.
 // The item stores k^T exp(G_last - G) (the scan's k^T, per value head),
 // G_last (the chunk's decay of each state row), q^ exp(G) and the decayed
 // scores P (the output kernel's two operands), and w, u as the intra kernel
@@ -1953,7 +1956,7 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         timing_begin(kIntra, stream);
         if (gk) {
-            // persistent: one workgroup per CU (LDS about 158 KiB), each walking items
+            // persistent: one workgroup per CU (LDS about 157 KiB), each walking items
             const dim3 grid((unsigned)(((nwg < (size_t)ncu ? nwg : (size_t)ncu) + g8 - 1) / g8 * g8));
             if (a.rule == 2) launch_intra_gk_rule<2>(act, grid, stream, p);
             else launch_intra_gk_rule<0>(act, grid, stream, p);

@@ -263,9 +263,11 @@ def test_prefill_per_key_gate_rules_without_decay_ignore_it():
         assert torch.equal(o1, o2) and torch.equal(s1, s2), rule
 
 
-def test_prefill_per_key_gate_varlen_t8192():
-    inp = workloads.prefill_inputs(83, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", gk="weak")
-    check_parity(inp, "gk weak B=4 T=8192 Nqk=16 Nv=32 bf16")
+@pytest.mark.parametrize("name", ["varlen_gk", "varlen_gk_small"])
+def test_prefill_per_key_gate_varlen_t8192(name):
+    # the timed per-key-gate workloads, in full: the decode page's gk range
+    # (mostly fp32 diagonal tiles) and a small gate (all fp16)
+    check_parity(workloads.extra_inputs(name), workloads.EXTRA_NAMES[name])
 
 
 def test_prefill_per_key_gate_two_level_scan():

@@ -192,16 +192,27 @@ CONFIG_NAMES = {
 }
 
 
-# Extra workloads beyond the five configured ones, each named for what it
-# exercises.  "long few heads" has too few (sequence, value head) streams to
-# fill the GPU with the one-level scan, so the library scans it in two levels.
+# Extra workloads beyond the five configured ones.  "long few heads" has too
+# few (sequence, value head) streams to fill the GPU with the one-level scan,
+# so the library scans it in two levels.  The two "varlen gk" ones are the
+# T=8192 prefill with a per-key gate: in the decode page's example range,
+# and small (under which every 16-token block's diagonal tiles take the fp16
+# path).
 EXTRA_NAMES = {
     "long_few_heads": "prefill long-context few heads B=1 T=131072 Nqk=1 Nv=4 D=128 bf16",
+    "varlen_gk": "prefill varlen B=4 lens=[1000,4096,300,2796] T=8192 Nqk=16 Nv=32 D=128 bf16, "
+                 "per-key gate gk=-U(0.01,1.01)",
+    "varlen_gk_small": "prefill varlen B=4 lens=[1000,4096,300,2796] T=8192 Nqk=16 Nv=32 D=128 bf16, "
+                       "per-key gate gk=-U(0.001,0.05)",
 }
 
 
 def extra_inputs(name: str):
     if name == "long_few_heads":
         return prefill_inputs(6, [131072], Nqk=1, Nv=4, act="bf16")
+    if name == "varlen_gk":
+        return prefill_inputs(7, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", gk="strong")
+    if name == "varlen_gk_small":
+        return prefill_inputs(8, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", gk="weak")
     raise ValueError(name)
 
