@@ -18,7 +18,9 @@ library records around its kernels on the launch stream (gdr_timing_*).
 Each event pair delays the stream by a few microseconds, so the timed
 region records them around the dominant kernel only (its average is the
 roofline's duration); the per-kernel breakdown comes from a short untimed
-pass with every kernel's events, run before the timed region.
+pass with every kernel's events, run before the timed region.  Kernels that
+a call launches more than once (the phased scan and output) are reported
+per call, summed over their launches.
 
 Roofline: algorithmic flops per kernel (MFMA-bound kernels, fp16 dense peak
 2.5 PFLOP/s) or algorithmic bytes (HBM-bound decode, 8 TB/s); the formulas
@@ -126,8 +128,9 @@ def counter_traffic(kernel):
 def timed(fn, steps, warmup, gdr, torch):
     """Warm up; take the per-kernel breakdown in an untimed pass with every
     kernel's events; then time `steps` steps with events around the dominant
-    kernel only.  Returns (seconds, breakdown {name: (ms, launches)},
-    dominant name, its (ms, launches) over the timed region)."""
+    kernel (the most time per call) only.  Returns (seconds, breakdown
+    {name: (ms per call, launches per call)}, dominant name, its (ms per
+    call, launches per call) over the timed region)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -138,8 +141,8 @@ def timed(fn, steps, warmup, gdr, torch):
         fn(warmup + i)
     torch.cuda.synchronize()
     gdr.timing_enable(False)
-    breakdown = {k: v for k, v in gdr.timing_read().items() if v[1]}
-    dominant = max(breakdown, key=lambda k: breakdown[k][0] / breakdown[k][1])
+    breakdown = {k: (v[0] / probe, v[1] / probe) for k, v in gdr.timing_read().items() if v[1]}
+    dominant = max(breakdown, key=lambda k: breakdown[k][0])
     gdr.timing_enable(True, kernels=[dominant])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -148,8 +151,8 @@ def timed(fn, steps, warmup, gdr, torch):
     torch.cuda.synchronize()
     dt = time.perf_counter() - t0
     gdr.timing_enable(False)
-    live = gdr.timing_read()[dominant]
-    return dt, breakdown, dominant, live
+    ms, n = gdr.timing_read()[dominant]
+    return dt, breakdown, dominant, (ms / steps, n / steps)
 
 
 def roofline(name, avg_s, flops=None, nbytes=None):
@@ -184,12 +187,13 @@ def bench_prefill(args, gdr, torch, workloads):
     kernels = {}
     for name in fl:
         ms, n = per.get(name, (0.0, 0))
-        avg = ms / 1e3 / max(n, 1)
-        kernels[name] = {"avg_us": avg * 1e6, "launches": n, "alg_gflop": fl[name] / 1e9,
-                         "mfma_frac": (fl[name] / avg / MFMA_PEAK_FP16) if avg > 0 and fl[name] else None}
-    # the dominant kernel's average over the timed region itself
-    dom_avg = live[0] / 1e3 / max(live[1], 1)
-    kernels[dominant]["avg_us_timed_region"] = dom_avg * 1e6
+        per_call = ms / 1e3
+        kernels[name] = {"us_per_call": per_call * 1e6, "launches_per_call": n, "alg_gflop": fl[name] / 1e9,
+                         "mfma_frac": (fl[name] / per_call / MFMA_PEAK_FP16) if per_call > 0 and fl[name] else None}
+    # the dominant kernel's time per call over the timed region itself (one
+    # launch per call: its average launch duration)
+    dom_avg = live[0] / 1e3
+    kernels[dominant]["us_per_call_timed_region"] = dom_avg * 1e6
     step_s = dt / args.steps
     f_total = sum(fl.values())
     b_total = bytes_prefill(T, B, Nqk, Nv)
@@ -260,7 +264,7 @@ def time_config(n, args, gdr, torch, workloads):
     dt, per, _, _ = timed(f, steps, 2, gdr, torch)
     name = workloads.CONFIG_NAMES[n] if isinstance(n, int) else workloads.EXTRA_NAMES[n]
     return {"config": name, "ms_per_call": dt / steps * 1e3, "tok_s": ntok / (dt / steps),
-            "kernels_us": {k: round(v[0] / max(v[1], 1) * 1e3, 1) for k, v in per.items() if v[1]}}
+            "kernels_us_per_call": {k: round(v[0] * 1e3, 1) for k, v in per.items()}}
 
 
 def cpu_baseline_prefill(inp):
