@@ -453,26 +453,33 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     //         four tiles of row 7 - pp (4 or 5 tiles per wave).  Row-major k^
     //         is already in the B-fragment layout of k^T.
     {
+        // Each tile is computed transposed (A = rows j, B = rows i), so a
+        // lane holds four consecutive columns 16 J + 4 lq .. of row
+        // i = 16 I + lr: beta_i and g_cum_i are the lane's own, and the row
+        // piece is one 8-byte store.
         auto gram_row = [&](int I, int J0, int J1) {
             half8 a[4];
 #pragma unroll
             for (int ks = 0; ks < 4; ++ks) a[ks] = ld_h8(&sA[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
+            const int i = 16 * I + lr;
+            const float bi = sBeta[i], gi = sGc[i];
             for (int J = J0; J < J1; ++J) {
                 f32x4 acc = {0.f, 0.f, 0.f, 0.f};
                 if constexpr (Rule<RULE>::delta) {
 #pragma unroll
                     for (int ks = 0; ks < 4; ++ks)
-                        acc = mma(a[ks], ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+                        acc = mma(ld_h8(&sA[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), a[ks], acc);
                 }
-                const int j = 16 * J + lr;
+                const int j0 = 16 * J + 4 * lq;
+                const f32x4 gj = *reinterpret_cast<const f32x4*>(&sGc[j0]);
+                half4 o;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const int i = 16 * I + 4 * lq + e;
-                    const float Lij =
-                        (Rule<RULE>::delta && i > j) ? sBeta[i] * acc[e] * __expf(sGc[i] - sGc[j]) : 0.f;
-                    sL[i * LD16 + j] = (_Float16)Lij;
-                    if (I == J) sD[(16 * I + 4 * lq + e) * 17 + lr] = Lij;
+                    const float Lij = (Rule<RULE>::delta && i > j0 + e) ? bi * acc[e] * __expf(gi - gj[e]) : 0.f;
+                    o[e] = (_Float16)Lij;
+                    if (I == J) sD[i * 17 + 4 * lq + e] = Lij;
                 }
+                st_h4(&sL[i * LD16 + j0], o);
             }
         };
         const int pp = wave >> 1;
@@ -640,7 +647,8 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sA[128 * LD16];
     __shared__ __align__(16) _Float16 sL[128 * LD16];
     __shared__ float sD[8 * 16 * 17];
-    __shared__ float sGc[128], sBeta[128], sBE[128];
+    __shared__ __align__(16) float sGc[128];
+    __shared__ float sBeta[128], sBE[128];
     const IntraSmem sm{sA, sL, sD, sGc, sBeta, sBE};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int c4 = tid & 31, tg = tid >> 5;
