@@ -27,7 +27,10 @@ Roofline: algorithmic flops per kernel (MFMA-bound kernels, fp16 dense peak
 are in flops_prefill() / bytes_decode() below.  `traffic` is the HBM byte
 count of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE counter
 runs recorded in profiles/counters.json, reported only while the kernel's
-source file is unchanged since those counters were taken.
+source file is unchanged since those counters were taken; for a contraction
+kernel it is also given as a rate over the same duration and a fraction of
+the 8 TB/s HBM peak (the prefill kernels move their workspace tiles through
+HBM, and that, more than the matrix cores, bounds them).
 
 cpu_baseline: the fp64 oracle (test infrastructure, one call on the full
 workload, timed on this host's cores) -- a reported baseline, not a target.
@@ -158,8 +161,13 @@ def timed(fn, steps, warmup, gdr, torch):
 def roofline(name, avg_s, flops=None, nbytes=None):
     if flops is not None:
         a = flops / avg_s
-        return {"bound": "mfma", "achieved": a / 1e12, "peak": MFMA_PEAK_FP16 / 1e12, "unit": "TFLOP/s",
-                "frac": a / MFMA_PEAK_FP16, "traffic": counter_traffic(name), "kernel": name}
+        tr = counter_traffic(name)
+        r = {"bound": "mfma", "achieved": a / 1e12, "peak": MFMA_PEAK_FP16 / 1e12, "unit": "TFLOP/s",
+             "frac": a / MFMA_PEAK_FP16, "traffic": tr, "kernel": name}
+        if tr:   # the same kernel against HBM: its counter-measured bytes over the same duration
+            r["traffic_rate_GBps"] = tr / avg_s / 1e9
+            r["traffic_hbm_frac"] = tr / avg_s / HBM_PEAK
+        return r
     a = nbytes / avg_s
     return {"bound": "hbm", "achieved": a / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s", "frac": a / HBM_PEAK,
             "traffic": counter_traffic(name), "kernel": name}
