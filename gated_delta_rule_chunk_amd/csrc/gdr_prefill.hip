@@ -304,8 +304,8 @@ __device__ __forceinline__ void raw_cvt(const Raw4<float>& x, float (&y)[4]) {
 // Rows past the chunk's end are loaded from its last row (every lane issues
 // the same loads on every path, which keeps the compiler's memory-counter
 // waits exact) and replaced by zeros when converted.
-// (v is first needed late in the item, so each item loads its own v rows at
-// its start.)
+// (v is first needed late in the item, so each item loads its own v rows
+// during its first steps.)
 template <typename ActT>
 struct IntraStage {
     Raw8<ActT> k[4];
@@ -355,7 +355,7 @@ struct IntraSmem {
 };
 
 template <typename ActT, int RULE>
-__device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const PrefillDev& p, const IntraSmem& sm,
+__device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const PrefillDev& p, const IntraSmem& sm,
                                            int tid_in) {
     // The item loop would otherwise hoist every per-lane offset derived from
     // the thread index out of the loop and keep them all live; an opaque copy
@@ -376,18 +376,19 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     const bool writes_keys = (h % G) == 0;   // one value head per group stores k^T
     const int c4 = tid & 31, tg = tid >> 5;   // transposing layout: tokens 8*tg.., columns 4*c4..
 
-    // v rows of this item (first used in step 7; the load overlaps steps 1-6).
-    // Rows past the chunk's end re-read its last row: they are multiplied by
-    // beta = 0 there.
+    // v rows of this item, first used in step 7, loaded in two halves at steps
+    // 2 and 4 (the workgroups' loads then come spread over the item, not in one
+    // burst with the next item's k).  Rows past the chunk's end re-read its last
+    // row: they are multiplied by beta = 0 there.
     Raw4<ActT> vr[8];
-    {
+    auto load_v = [&](int i0) {
         const ActT* V = static_cast<const ActT*>(p.v);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = i0; i < i0 + 4; ++i) {
             const int row = min(8 * tg + i, max(r - 1, 0));
             raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4);
         }
-    }
+    };
     __syncthreads();   // the previous item is done with the shared buffers
     // ---- 1. gate cumulative sum and beta (wave 0); k rows normalised -> sA (row-major)
     if (wave == 0) {   // lane owns rows 2l, 2l+1
@@ -444,6 +445,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     }
     __syncthreads();
 
+    load_v(0);
     // ---- 2. Gram k^ k^T on the lower 16-tiles -> L (fp16 in sL, diagonal
     //         blocks also fp32 in sD); zeros above the block diagonal of sL;
     //         k^ read back transposed (8 tokens x 4 dk per thread).
@@ -525,6 +527,7 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     }
     __syncthreads();
 
+    load_v(4);
     // ---- 4. unscaled k^T -> workspace (fragment order); column block j = wave of T by forward substitution
     if (writes_keys) {
 #pragma unroll
@@ -564,7 +567,10 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
     __syncthreads();
 
     // ---- 5. T (fp16) into sL over L (zeros above the block diagonal stay);
-    //         sA scaled in place to (k^ beta e^gcum)^T
+    //         sA scaled in place to (k^ beta e^gcum)^T.  The next item's k, g
+    //         and beta load into the stage now (this item took its own in step
+    //         1); fp32 inputs, twice the registers, load at the item's start
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, next, wave, lane, lr, lq, c4, tg);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         if (b < wave) continue;
@@ -640,8 +646,8 @@ __device__ __forceinline__ void intra_item(const IntraStage<ActT>& st, const Pre
 }
 
 // Persistent: each workgroup walks items blockIdx.x, blockIdx.x + gridDim.x, ...
-// (item = chunk * Nv + value head).  With bf16 activations two register
-// stages alternate, so the next item's inputs load while this one computes.
+// (item = chunk * Nv + value head), the next item's inputs loading while this
+// one computes.
 template <typename ActT, int RULE>
 __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sA[128 * LD16];
@@ -656,30 +662,17 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     const int stride = gridDim.x;   // a multiple of 8 G
     int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
     if (it >= n_items) return;
-    if constexpr (sizeof(ActT) == 2) {
-        IntraStage<ActT> A, B;
-        intra_load<ActT, RULE>(A, p, it, wave, lane, lr, lq, c4, tg);
-        // The next item's loads are issued on every pass (after the last
-        // item they re-read the current one, unused), so that the waits the
-        // compiler places for the current item's data never cover them.
-        while (true) {
-            const int nx = it + stride;
-            intra_load<ActT, RULE>(B, p, nx < n_items ? nx : it, wave, lane, lr, lq, c4, tg);
-            intra_item<ActT, RULE>(A, p, sm, tid);
-            if (nx >= n_items) break;
-            it = nx;
-            const int nx2 = it + stride;
-            intra_load<ActT, RULE>(A, p, nx2 < n_items ? nx2 : it, wave, lane, lr, lq, c4, tg);
-            intra_item<ActT, RULE>(B, p, sm, tid);
-            if (nx2 >= n_items) break;
-            it = nx2;
-        }
-    } else {
-        for (; it < n_items; it += stride) {
-            IntraStage<ActT> A;
-            intra_load<ActT, RULE>(A, p, it, wave, lane, lr, lq, c4, tg);
-            intra_item<ActT, RULE>(A, p, sm, tid);
-        }
+    // One register stage: the item loads the next one's k, g and beta into it
+    // once it has used its own (after the last item they re-read the current
+    // one, unused); with fp32 inputs each item loads its own at its start.
+    IntraStage<ActT> st;
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
+    while (true) {
+        if constexpr (sizeof(ActT) == 4) intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
+        const int nx = it + stride;
+        intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
+        if (nx >= n_items) break;
+        it = nx;
     }
 }
 
