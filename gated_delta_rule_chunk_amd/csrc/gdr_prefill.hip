@@ -1670,10 +1670,10 @@ __device__ __forceinline__ void pair_tile_store_t(const u32x4 (&rg)[8], _Float16
 }
 
 template <typename ActT>
-__global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
+__global__ __launch_bounds__(512, 4) void output_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sBuf[128 * LD16];
     __shared__ __align__(16) _Float16 sP[128 * LD16];
-    __shared__ float sG[128];   // g_cum of the chunk
+    __shared__ __align__(16) float sG[128];   // g_cum of the chunk
 
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
     const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
@@ -1754,21 +1754,26 @@ __global__ __launch_bounds__(512) void output_kernel(PrefillDev p) {
     }
     __syncthreads();
 
-    // P = (q^ k^T) . D on the inclusive lower triangle -> sP rows of this wave
-    for (int J = 0; J <= I; ++J) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // P = (q^ k^T) . D on the inclusive lower triangle -> sP rows of this wave.
+    // Each tile is computed transposed (A = k^ rows j, B = q^ rows i), so a
+    // lane holds four consecutive columns 16 J + 4 lq .. of row i = 16 I + lr.
+    {
+        const int i = 16 * I + lr;
+        const float gi = sG[i];
+        for (int J = 0; J <= I; ++J) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) acc = mma(qh[ks], ld_h8(&sBuf[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), acc);
-        const int j = 16 * J + lr;
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mma(ld_h8(&sBuf[(16 * J + lr) * LD16 + 32 * ks + 8 * lq]), qh[ks], acc);
+            const int j0 = 16 * J + 4 * lq;
+            const f32x4 gj = *reinterpret_cast<const f32x4*>(&sG[j0]);
+            half4 o4;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int i = 16 * I + 4 * lq + e;
-            sP[i * LD16 + j] = (_Float16)(i >= j ? acc[e] * __expf(sG[i] - sG[j]) : 0.f);
+            for (int e = 0; e < 4; ++e) o4[e] = (_Float16)(i >= j0 + e ? acc[e] * __expf(gi - gj[e]) : 0.f);
+            st_h4(&sP[i * LD16 + j0], o4);
         }
-    }
-    if ((I & 1) == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sP[(16 * I + 4 * lq + e) * LD16 + 16 * (I + 1) + lr] = (_Float16)0.f;
+        // the next block's columns, read by the last k-step of P v_new
+        if ((I & 1) == 0) st_h4(&sP[i * LD16 + 16 * (I + 1) + 4 * lq], half4{0, 0, 0, 0});
     }
     __syncthreads();
     pair_tile_store_t<0>(stSV, sBuf, tid);   // S_c^T [col][dk]
