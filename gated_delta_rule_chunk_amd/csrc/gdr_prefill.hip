@@ -316,7 +316,8 @@ struct IntraStage {
 
 template <typename ActT, int RULE>
 __device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, int item, int wave, int lane,
-                                           int lr, int lq, int c4, int tg) {
+                                           int lr, int lq, int c4, int tg, int part = 3) {
+    // part 1: k dims 0..63; part 2: k dims 64..127, g and beta; 3: all
     const int Nv = p.Nv, Nqk = p.Nqk;
     const int c = item / Nv, h = item % Nv, hq = h / (Nv / Nqk);
     const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
@@ -326,7 +327,10 @@ __device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDe
     const int last = max(r - 1, 0);   // every mapped chunk has r >= 1
     const int row = min(16 * wave + lr, last);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) raw_load(st.k[ks], K + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+    for (int ks = 0; ks < 4; ++ks)
+        if (((part & 1) && ks < 2) || ((part & 2) && ks >= 2))
+            raw_load(st.k[ks], K + ((size_t)(t0 + row) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
+    if (!(part & 2)) return;
     // only wave 0 uses the gates; the other waves issue the same loads at one
     // lane-uniform address (a single cache line each)
     const int i0 = wave == 0 ? min(2 * lane, last) : 0, i1 = wave == 0 ? min(2 * lane + 1, last) : 0;
@@ -568,9 +572,10 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
 
     // ---- 5. T (fp16) into sL over L (zeros above the block diagonal stay);
     //         sA scaled in place to (k^ beta e^gcum)^T.  The next item's k, g
-    //         and beta load into the stage now (this item took its own in step
-    //         1); fp32 inputs, twice the registers, load at the item's start
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, next, wave, lane, lr, lq, c4, tg);
+    //         and beta load into the stage in two parts, now and in step 6 (this
+    //         item took its own in step 1); fp32 inputs, twice the registers,
+    //         load at the item's start
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, next, wave, lane, lr, lq, c4, tg, 1);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         if (b < wave) continue;
@@ -588,6 +593,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     }
     __syncthreads();
 
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, next, wave, lane, lr, lq, c4, tg, 2);
     // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk], fragment order  (lower-triangular K
     //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
     //         The wave's four output tiles share each B fragment (row Jt of T).
