@@ -358,6 +358,38 @@ struct IntraSmem {
     float* sBE;
 };
 
+// Column block j of T = (I + L)^-1 by forward substitution over 16-row
+// blocks: X_jj = T_jj, X_bj = -T_bb sum_{j <= a < b} L_ba X_aj.  Each solved
+// block at once adds its term to every later block's sum (right-looking), so
+// the L reads and most products are off the chain that runs from one solved
+// block to the next; each sum still adds its terms in ascending a.  T_bb (the
+// inverted diagonal blocks, fp32, row stride 17) is in sD, L (fp16) in sL.
+// xh[b] receives X_bj in the 16x16x16 MFMA's accumulator (= B operand) layout.
+__device__ __forceinline__ void block_column_solve(const float* sD, const _Float16* sL, int j, int lr, int lq,
+                                                   half4 (&xh)[8]) {
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[b] = zero;
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+        if (a < j) continue;
+        f32x4 x;
+        if (a == j) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[e] = sD[(16 * a + 4 * lq + e) * 17 + lr];
+        } else {
+            half4 ta;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) ta[e] = (_Float16)sD[(16 * a + lr) * 17 + 4 * lq + e];
+            x = mma16(ta, to_h4(-acc[a]), zero);
+        }
+        xh[a] = to_h4(x);
+#pragma unroll
+        for (int b = a + 1; b < 8; ++b) acc[b] = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq]), xh[a], acc[b]);
+    }
+}
+
 template <typename ActT, int RULE>
 __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const PrefillDev& p, const IntraSmem& sm,
                                            int tid_in) {
@@ -543,31 +575,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
         }
     }
     half4 xh[8];
-    {
-        const int j = wave;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if (b < j) continue;
-            f32x4 x;
-            if (b == j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = sD[(16 * b + 4 * lq + e) * 17 + lr];
-            } else {
-                f32x4 acc = zero;
-#pragma unroll
-                for (int a = 0; a < b; ++a) {
-                    if (a < j) continue;
-                    acc = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq]), xh[a], acc);
-                }
-                half4 tb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tb[e] = (_Float16)sD[(16 * b + lr) * 17 + 4 * lq + e];
-                x = mma16(tb, to_h4(-acc), zero);
-            }
-            xh[b] = to_h4(x);
-        }
-    }
+    block_column_solve(sD, sL, wave, lr, lq, xh);
     __syncthreads();
 
     // ---- 5. T (fp16) into sL over L (zeros above the block diagonal stay);
@@ -1162,31 +1170,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         st_h8(p.khatT + ch * TILE + (size_t)e_ * 8 + 8, to_h8(y1));
     }
     half4 xh[8];
-    {
-        const int j = wave;
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            if (b < j) continue;
-            f32x4 x;
-            if (b == j) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) x[e] = sD[(16 * b + 4 * lq + e) * 17 + lr];
-            } else {
-                f32x4 acc = zero;
-#pragma unroll
-                for (int a = 0; a < b; ++a) {
-                    if (a < j) continue;
-                    acc = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq]), xh[a], acc);
-                }
-                half4 tb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) tb[e] = (_Float16)sD[(16 * b + lr) * 17 + 4 * lq + e];
-                x = mma16(tb, to_h4(-acc), zero);
-            }
-            xh[b] = to_h4(x);
-        }
-    }
+    block_column_solve(sD, sL, wave, lr, lq, xh);
     __syncthreads();   // KB is done
     gk_load_v<ActT>(st, p, t0, h, r, 0, tid);        // this item's v, used in step 9
     gk_gate_dma(p, st.t0, st.h, st.r, sG, 2, tid);   // the next gate tile's third quarter
