@@ -1064,11 +1064,19 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     const int J0A = (wave & 1) ? 4 - pp : 0, nA = Id - J0A;   // row Id: tiles J0A .. Id - 1
     const int rowB = 7 - pp, nT = nA + ((wave & 1) ? 0 : 4 - pp);   // even waves: row 7 - pp, tiles 0 ..
     f32x4 lacc[4];
+    half8 qa[4], ka[4];   // QA and KA fragments of the current tile row, loaded once per row
 #pragma unroll
     for (int tt = 0; tt < 4; ++tt) {
         lacc[tt] = f32x4{0.f, 0.f, 0.f, 0.f};
         if (tt < nT) {
             const int I = tt < nA ? Id : rowB, J = tt < nA ? J0A + tt : tt - nA;
+            if (tt == 0 || tt == nA) {
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) {
+                    qa[ks] = ld_h8(&sQL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
+                    if constexpr (kDelta) ka[ks] = ld_h8(&sK[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
+                }
+            }
             const _Float16* cIJ = &sC[((I - 2) * (I - 1) / 2 + J) * 128];
             f32x4 pacc = {0.f, 0.f, 0.f, 0.f}, la = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1076,8 +1084,8 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
                 const int d0 = 32 * ks + 8 * lq;
                 half8 kb = ld_h8(&sKB[(16 * J + lr) * LD16 + d0]);
                 if (J + 1 < I) kb = kb * ld_h8(&cIJ[d0]);
-                pacc = mma(kb, ld_h8(&sQL[(16 * I + lr) * LD16 + d0]), pacc);
-                if constexpr (kDelta) la = mma(kb, ld_h8(&sK[(16 * I + lr) * LD16 + d0]), la);
+                pacc = mma(kb, qa[ks], pacc);
+                if constexpr (kDelta) la = mma(kb, ka[ks], la);
             }
             st_h4(p.pm + ch * TILE + frag_off(16 * I + lr, 16 * J + 4 * lq), to_h4(pacc));
             lacc[tt] = la;
