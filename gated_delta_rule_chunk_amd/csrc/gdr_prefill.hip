@@ -416,13 +416,14 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     // 2 and 4 (the workgroups' loads then come spread over the item, not in one
     // burst with the next item's k).  Rows past the chunk's end re-read its last
     // row: they are multiplied by beta = 0 there.
-    Raw4<ActT> vr[8];
+    Raw8<ActT> vr[4];   // rows 4 tq + i, columns 8 c8 .. 8 c8 + 7
     auto load_v = [&](int i0) {
         const ActT* V = static_cast<const ActT*>(p.v);
+        const int c8 = tid & 15, tq = tid >> 4;
 #pragma unroll
-        for (int i = i0; i < i0 + 4; ++i) {
-            const int row = min(8 * tg + i, max(r - 1, 0));
-            raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 4 * c4);
+        for (int i = i0 / 2; i < i0 / 2 + 2; ++i) {
+            const int row = min(4 * tq + i, max(r - 1, 0));
+            raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 8 * c8);
         }
     };
     __syncthreads();   // the previous item is done with the shared buffers
@@ -626,15 +627,17 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
 
     // ---- 7. (v beta)^T [col][tok] into sA
     {
-        float vf[8][4];
+        const int c8 = tid & 15, tq = tid >> 4;
+        float vf[4][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) raw_cvt(vr[i], vf[i]);
+        for (int i = 0; i < 4; ++i) raw_cvt(vr[i], vf[i]);
+        const f32x4 bt = *reinterpret_cast<const f32x4*>(&sBeta[4 * tq]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            half8 col;
+        for (int e = 0; e < 8; ++e) {
+            half4 col;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) col[i] = (_Float16)(vf[i][e] * sBeta[8 * tg + i]);
-            st_h8(&sA[sw(4 * c4 + e, 8 * tg)], col);
+            for (int i = 0; i < 4; ++i) col[i] = (_Float16)(vf[i][e] * bt[i]);
+            st_h4(&sA[sw(8 * c8 + e, 4 * tq)], col);
         }
     }
     __syncthreads();
@@ -668,7 +671,8 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sL[128 * LD16];
     __shared__ float sD[8 * 16 * 17];
     __shared__ __align__(16) float sGc[128];
-    __shared__ float sBeta[128], sBE[128];
+    __shared__ __align__(16) float sBeta[128];
+    __shared__ float sBE[128];
     const IntraSmem sm{sA, sL, sD, sGc, sBeta, sBE};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int c4 = tid & 31, tg = tid >> 5;
