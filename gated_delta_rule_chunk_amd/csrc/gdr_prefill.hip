@@ -358,6 +358,30 @@ struct IntraSmem {
     float* sBE;
 };
 
+// Four 16x16 accumulator tiles acc[ii] of w (rows 16 Jt + lr, columns
+// 16 (4 hsel + ii) + 4 lq + e) into the tile's fragment order.  A 16-byte piece
+// there holds 8 consecutive columns of one row, which two lanes 16 apart (lq,
+// lq ^ 1) hold half each; v_permlane16_swap over a pair of tiles (2m, 2m + 1)
+// gives the even-row lane tile 2m's whole piece and the odd-row lane tile
+// 2m + 1's, so each lane writes one 16-byte piece per pair.
+__device__ __forceinline__ void store_w_tiles(_Float16* dst, const f32x4 (&acc)[4], int Jt, int hsel, int lr,
+                                              int lq) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+        const half4 a = to_h4(acc[2 * m]), b = to_h4(acc[2 * m + 1]);
+        const u32x2 ua = __builtin_bit_cast(u32x2, a), ub = __builtin_bit_cast(u32x2, b);
+        u32x4 piece;
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane16_swap(ua[d], ub[d], false, false);
+            piece[d] = r[0];
+            piece[2 + d] = r[1];
+        }
+        const int ii = 2 * m + (lq & 1);
+        st_h8(dst + frag_off(16 * Jt + lr, 16 * (4 * hsel + ii) + 8 * (lq >> 1)), __builtin_bit_cast(half8, piece));
+    }
+}
+
 // Column block j of T = (I + L)^-1 by forward substitution over 16-row
 // blocks: X_jj = T_jj, X_bj = -T_bb sum_{j <= a < b} L_ba X_aj.  Each solved
 // block at once adds its term to every later block's sum (right-looking), so
@@ -619,9 +643,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
             for (int ii = 0; ii < 4; ++ii)
                 acc[ii] = mma(ld_h8(&sA[sw(16 * (4 * hsel + ii) + lr, 32 * ks + 8 * lq)]), b, acc[ii]);
         }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * (4 * hsel + ii) + 4 * lq), to_h4(acc[ii]));
+        store_w_tiles(p.w + ch * TILE, acc, Jt, hsel, lr, lq);
     }
     __syncthreads();
 
@@ -1227,9 +1249,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
             for (int ii = 0; ii < 4; ++ii)
                 acc[ii] = mma(ld_h8(&sK[sw(16 * (4 * hsel + ii) + lr, 32 * ks + 8 * lq)]), b, acc[ii]);
         }
-#pragma unroll
-        for (int ii = 0; ii < 4; ++ii)
-            st_h4(p.w + ch * TILE + frag_off(16 * Jt + lr, 16 * (4 * hsel + ii) + 4 * lq), to_h4(acc[ii]));
+        store_w_tiles(p.w + ch * TILE, acc, Jt, hsel, lr, lq);
     }
     }
     __syncthreads();
