@@ -1727,9 +1727,9 @@ __global__ __launch_bounds__(512, 4) void output_kernel(PrefillDev p) {
         // rows past the chunk's end re-read its last row (their outputs are
         // never stored, and P is zero above the diagonal)
         const int row = 16 * I + lr, lrow = min(row, max(r - 1, 0));
-        float x[4][8];
+        Raw8<ActT> qr[4];   // held raw until used (as fp32 they would cost twice the registers)
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) load8(Q + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq, x[ks]);
+        for (int ks = 0; ks < 4; ++ks) raw_load(qr[ks], Q + ((size_t)(t0 + lrow) * Nqk + hq) * 128 + 32 * ks + 8 * lq);
         const float eg = __expf(GC[row]);
         const float gmine = GC[tid & 127];
         __builtin_amdgcn_sched_barrier(0);
@@ -1757,6 +1757,9 @@ __global__ __launch_bounds__(512, 4) void output_kernel(PrefillDev p) {
                 st_h8(&sBuf[(16 * I + lr) * LD16 + 32 * ks + 8 * lq], to_h8(y));
             }
         }
+        float x[4][8];
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) raw_cvt(qr[ks], x[ks]);
         float ssq = 0.f;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks)
