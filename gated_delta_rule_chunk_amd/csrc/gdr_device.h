@@ -52,6 +52,15 @@ __device__ __forceinline__ void store8(float* p, const float (&x)[8]) {
     *reinterpret_cast<f32x4*>(p + 4) = f32x4{x[4], x[5], x[6], x[7]};
 }
 
+// 4-element vector store: bf16 one 8-byte access, fp32 one 16-byte access.
+__device__ __forceinline__ void store4(uint16_t* p, f32x4 x) {
+    u32x2 r;
+    r[0] = uint32_t(f32_to_bf16(x[0])) | (uint32_t(f32_to_bf16(x[1])) << 16);
+    r[1] = uint32_t(f32_to_bf16(x[2])) | (uint32_t(f32_to_bf16(x[3])) << 16);
+    *reinterpret_cast<u32x2*>(p) = r;
+}
+__device__ __forceinline__ void store4(float* p, f32x4 x) { *reinterpret_cast<f32x4*>(p) = x; }
+
 // 4-element vector load: bf16 one 8-byte access, fp32 one 16-byte access.
 __device__ __forceinline__ void load4(const uint16_t* p, float (&x)[4]) {
     const u32x2 r = *reinterpret_cast<const u32x2*>(p);
@@ -104,6 +113,9 @@ __device__ __forceinline__ void load8(const _Float16* p, float (&x)[8]) {
     const half8 r = *reinterpret_cast<const half8*>(p);
 #pragma unroll
     for (int i = 0; i < 8; ++i) x[i] = (float)r[i];
+}
+__device__ __forceinline__ void store4(_Float16* p, f32x4 x) {
+    *reinterpret_cast<half4*>(p) = half4{(_Float16)x[0], (_Float16)x[1], (_Float16)x[2], (_Float16)x[3]};
 }
 __device__ __forceinline__ void store8(_Float16* p, const float (&x)[8]) {
     half8 r;

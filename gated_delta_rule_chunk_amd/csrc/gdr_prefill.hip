@@ -30,6 +30,9 @@
 //             v_new and the chunk's starting state for K3.
 //   output    K3, one workgroup per (chunk, value head): o = (q^ e^g) S_c +
 //             P v_new, fully parallel over chunks again.
+//   With a per-key gate the intra kernel also stores the output's two A
+//   operands (q^ e^G and P), and the one-level scan forms the output itself
+//   (scan_gk_out): S_c and v_new never leave the chip and K3 does not run.
 //
 // Matrix products run on the gfx950 MFMA v_mfma_f32_16x16x32_f16 (fp16
 // operands, fp32 accumulation).  fp16 rather than bf16 operands: at the
@@ -1914,6 +1917,177 @@ __global__ __launch_bounds__(512) void output_gk_kernel(PrefillDev p) {
     }
 }
 
+
+// ------------------------------------------------------------------ K2 with K3 fused, per-key gate
+// With a per-key gate the intra kernel stores both A operands of the output
+// (q^ exp(G) and P, fragment order), so the one-level scan forms each chunk's
+// output itself, where S_c and v_new are on chip: neither is written to
+// memory and no output pass runs.  For this slice's columns
+//   o^T = S_c^T (q^ e^G)^T + v_new^T P^T.
+// Wave wv owns output rows i = 16 wv + lr.  Both products are taken
+// transposed -- A = S^T or v_new^T fragments from LDS, B = the stored row
+// fragments, whose A-operand layout is the B-operand layout of the transposed
+// product -- so that a lane holds four consecutive columns of one row.  The
+// first shares the S^T fragments that v_new = u - w S reads; the second reads
+// the v_new^T tile that the state update reads (with this gate v_new enters
+// the update unscaled: the chunk's decays sit in k^T).
+template <int CT>
+struct GkOutOps {
+    ScanOps<CT> s;        // w, k^T (with its decays), u and G_last of the chunk
+    half8 qe[4], pa[4];   // q^ e^G and P, rows 16 wv + lr (key blocks of 32)
+    int t0, r;            // the chunk's first token and its number of rows
+};
+
+// Parts as in the scan (0: w, 1: u and the gates, 2: k^T), with q^ e^G in
+// part 0 (needed first) and P in part 2 (needed after the first barrier).
+// Key blocks of P past wv / 2 are zero and never used: their fetch re-reads
+// block wv / 2.
+template <int CT, int PART>
+__device__ __forceinline__ void gk_out_load_part(GkOutOps<CT>& o, const PrefillDev& p, int c, int h, int hq,
+                                                 const ScanLane& ln, int wvu) {
+    const size_t ch = (size_t)c * p.Nv + h;
+    if constexpr (PART == 0) {
+        o.t0 = ld_uniform(&p.cmap[4 * c + 1]);
+        o.r = ld_uniform(&p.cmap[4 * c + 2]);
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o.qe[ks] = ld_h8(p.qt + ch * TILE + ln.a + 512 * ks);
+    }
+    if constexpr (PART == 2) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) o.pa[ks] = ld_h8(p.pm + ch * TILE + ln.a + 512 * min(ks, wvu >> 1));
+    }
+    scan_load_part<CT, PART, true>(o.s, p, c, h, hq, ln);
+}
+
+template <int DS, bool LOAD, typename ActT>
+__device__ __forceinline__ void scan_gk_out_step(const GkOutOps<DS / 16>& o, f32x4 (&S)[DS / 16],
+                                                 const PrefillDev& p, int h, _Float16* sST, _Float16* sVn, int wv,
+                                                 int wvu, int lr, int lq, int col0, GkOutOps<DS / 16>& nx, int cn,
+                                                 int hq, const ScanLane& ln) {
+    constexpr int CT = DS / 16;
+    if constexpr (LOAD) {
+        gk_out_load_part<CT, 0>(nx, p, cn, h, hq, ln, wvu);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // v_new = u - w S (tokens 16 wv + 4 lq + e) and (q^ e^G S_c)^T (rows
+    // i = 16 wv + lr), from the same S^T fragments
+    const int tok = 16 * wv + 4 * lq;
+    f32x4 oT[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+        f32x4 vp = {0.f, 0.f, 0.f, 0.f}, oi = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const half8 b = ld_h8(&sST[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]);
+            vp = mma(o.s.aw[ks], b, vp);
+            oi = mma(b, o.qe[ks], oi);
+        }
+        oT[ct] = oi;
+        f32x4 vn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) vn[e] = (float)o.s.u4[ct][e] - vp[e];
+        st_h4(&sVn[(16 * ct + lr) * LD16 + tok], to_h4(vn));
+    }
+    if constexpr (LOAD) {
+        __builtin_amdgcn_sched_barrier(0);
+        gk_out_load_part<CT, 1>(nx, p, cn, h, hq, ln, wvu);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();
+    if constexpr (LOAD) {
+        __builtin_amdgcn_sched_barrier(0);
+        gk_out_load_part<CT, 2>(nx, p, cn, h, hq, ln, wvu);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // S <- exp(G_last) S + k^T v_new, row by row (the gate slot holds G_last
+    // of this lane's rows)
+    {
+        f32x4 dec;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dec[e] = __expf(o.s.gcr[e]);
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) {
+            f32x4 acc = S[ct] * dec;
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                acc = mma(o.s.ak[ks], ld_h8(&sVn[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), acc);
+            S[ct] = acc;
+            st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(acc));
+        }
+    }
+    // o^T += v_new^T P^T over the key blocks ks <= wv / 2; rows < r -> out
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        if (ks > (wvu >> 1)) break;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct)
+            oT[ct] = mma(ld_h8(&sVn[(16 * ct + lr) * LD16 + 32 * ks + 8 * lq]), o.pa[ks], oT[ct]);
+    }
+    const int i = 16 * wv + lr;
+    if (i < o.r) {
+        ActT* OUT = static_cast<ActT*>(p.out) + ((size_t)(o.t0 + i) * p.Nv + h) * 128 + col0 + 4 * lq;
+#pragma unroll
+        for (int ct = 0; ct < CT; ++ct) store4(OUT + 16 * ct, oT[ct]);
+    }
+    __syncthreads();
+}
+
+// One workgroup per (sequence, value head, slice of DS state columns), placed
+// as the scan's.  Two register sets rotate between the chunk being computed
+// and the one being fetched; every fetch is issued (past the last chunk it
+// re-reads the last chunk, unused), as in the scan.
+template <int DS, typename ActT>
+__global__ __launch_bounds__(512) void scan_gk_out_kernel(PrefillDev p) {
+    constexpr int NS = 128 / DS, CT = DS / 16;
+    __shared__ __align__(16) _Float16 sST[DS * LD16];   // S^T [col][dk] (fp16), the chunk's start state
+    __shared__ __align__(16) _Float16 sVn[DS * LD16];   // v_new^T [col][tok]
+
+    const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
+    const int id = blockIdx.x, xcd = id & 7, j = id >> 3;
+    const int local = j % (G * NS), grp = (j / (G * NS)) * 8 + xcd;
+    if (grp >= p.B * Nqk) return;
+    const int hq = grp % Nqk, b = grp / Nqk;
+    const int slice = local % NS, h = hq * G + local / NS;
+    const int stream = b * Nv + h;
+    const int col0 = slice * DS;
+    const int tid = threadIdx.x, wv = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);
+    const int c0 = ld_uniform(&p.meta[b]), c1 = ld_uniform(&p.meta[b + 1]);
+
+    f32x4 S[CT];
+    const float* sinit = p.state_in ? p.state_in + (size_t)stream * TILE : nullptr;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            S[ct][e] = sinit ? sinit[(size_t)(16 * wv + 4 * lq + e) * 128 + col0 + 16 * ct + lr] : 0.f;
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) st_h4(&sST[(16 * ct + lr) * LD16 + 16 * wv + 4 * lq], to_h4(S[ct]));
+
+    const ScanLane ln{(uint32_t)(frag_off(16 * wv + lr, 8 * lq)), (uint32_t)(cfrag_off(16 * wv + 4 * lq, col0 + lr)),
+                      (uint32_t)(16 * wv + 4 * lq)};
+    __syncthreads();
+    if (c0 < c1) {
+        const int cl = c1 - 1;
+        int c = c0;
+        GkOutOps<CT> A, B;
+        gk_out_load_part<CT, 0>(A, p, c0, h, hq, ln, wvu);
+        gk_out_load_part<CT, 1>(A, p, c0, h, hq, ln, wvu);
+        gk_out_load_part<CT, 2>(A, p, c0, h, hq, ln, wvu);
+        __builtin_amdgcn_sched_barrier(0);
+        for (; c + 2 <= c1; c += 2) {
+            scan_gk_out_step<DS, true, ActT>(A, S, p, h, sST, sVn, wv, wvu, lr, lq, col0, B, min(c + 1, cl), hq, ln);
+            scan_gk_out_step<DS, true, ActT>(B, S, p, h, sST, sVn, wv, wvu, lr, lq, col0, A, min(c + 2, cl), hq, ln);
+        }
+        if (c < c1) scan_gk_out_step<DS, false, ActT>(A, S, p, h, sST, sVn, wv, wvu, lr, lq, col0, B, 0, hq, ln);
+    }
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            p.state_out[(size_t)stream * TILE + (size_t)(16 * wv + 4 * lq + e) * 128 + col0 + 16 * ct + lr] = S[ct][e];
+}
+
 }  // namespace
 
 // Compute units of the current device (queried once per device).
@@ -1946,6 +2120,13 @@ template <int DS, int MODE>
 static void launch_scan(bool gk, dim3 grid, hipStream_t stream, const PrefillDev& p) {
     if (gk) hipLaunchKernelGGL((scan_kernel<DS, MODE, true>), grid, dim3(512), 0, stream, p);
     else hipLaunchKernelGGL((scan_kernel<DS, MODE, false>), grid, dim3(512), 0, stream, p);
+}
+// The per-key-gate scan with the output fused in, for a slice width.
+template <int DS>
+static void launch_scan_gk_out(int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
+    if (act == kActBf16) hipLaunchKernelGGL((scan_gk_out_kernel<DS, uint16_t>), grid, dim3(512), 0, stream, p);
+    else if (act == kActFp16) hipLaunchKernelGGL((scan_gk_out_kernel<DS, _Float16>), grid, dim3(512), 0, stream, p);
+    else hipLaunchKernelGGL((scan_gk_out_kernel<DS, float>), grid, dim3(512), 0, stream, p);
 }
 static void launch_intra(int rule, int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
     switch (rule) {
@@ -2021,16 +2202,29 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     const size_t nstream = (size_t)a.B * a.Nv * lay.nseg;
     int ns = nstream >= 512 ? 1 : nstream >= 256 ? 2 : nstream >= 64 ? 4 : 8;
     while (lay.nseg > 1 && ns > 1 && nstream * ns > (size_t)ncu) ns >>= 1;
+    // With a per-key gate the one-level scan forms the output itself (slices
+    // of at most 64 columns, which fit its registers); the other cases record
+    // S_c and v_new for the output pass.
+    const bool fused = gk && lay.nseg == 1;
+    if (fused && ns == 1) ns = 2;
     const size_t nscan = ngroup * G * ns;
-    switch (ns) {
-        case 1: launch_scan<128, 0>(gk, dim3((unsigned)nscan), stream, p); break;
-        case 2: launch_scan<64, 0>(gk, dim3((unsigned)nscan), stream, p); break;
-        case 4: launch_scan<32, 0>(gk, dim3((unsigned)nscan), stream, p); break;
-        default: launch_scan<16, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+    if (fused) {
+        switch (ns) {
+            case 2: launch_scan_gk_out<64>(act, dim3((unsigned)nscan), stream, p); break;
+            case 4: launch_scan_gk_out<32>(act, dim3((unsigned)nscan), stream, p); break;
+            default: launch_scan_gk_out<16>(act, dim3((unsigned)nscan), stream, p); break;
+        }
+    } else {
+        switch (ns) {
+            case 1: launch_scan<128, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+            case 2: launch_scan<64, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+            case 4: launch_scan<32, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+            default: launch_scan<16, 0>(gk, dim3((unsigned)nscan), stream, p); break;
+        }
     }
     timing_end(kScan, stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    if (nwg > 0) {
+    if (nwg > 0 && !fused) {
         timing_begin(kOutput, stream);
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         const unsigned nout = (unsigned)((nwg + g8 - 1) / g8 * g8);
