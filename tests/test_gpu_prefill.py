@@ -270,6 +270,17 @@ def test_prefill_per_key_gate_varlen_t8192(name):
     check_parity(workloads.extra_inputs(name), workloads.EXTRA_NAMES[name])
 
 
+@pytest.mark.parametrize("B,Nqk,Nv", [(2, 16, 32), (8, 16, 32), (16, 8, 32)])
+def test_prefill_per_key_gate_every_scan_slice_width(B, Nqk, Nv):
+    """With the per-key gate the one-level scan forms the output itself; its
+    column split (16, 32 or 64 state columns per workgroup, 64 also standing
+    in for a whole-row split) follows the B * Nv streams, and each is checked
+    (16 by the ragged cases above)."""
+    lens = [150 + 37 * i for i in range(B)]
+    inp = workloads.prefill_inputs(86 + B, lens, Nqk=Nqk, Nv=Nv, act="bf16", gk="weak")
+    check_parity(inp, f"gk weak B={B} Nv={Nv} ({B * Nv} streams)")
+
+
 def test_prefill_per_key_gate_two_level_scan():
     inp = workloads.prefill_inputs(84, [20000], Nqk=1, Nv=2, act="bf16", gk="weak")
     check_parity(inp, "gk weak two-level T=20000 Nqk=1 Nv=2 bf16")
