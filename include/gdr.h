@@ -217,8 +217,9 @@ gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, con
  * summed duration total_ms[i] and the number of launches launches[i]
  * recorded since the previous read, and forgets them.  Kernel ids:
  * 0 gdr_chunkmap, 1 gdr_intra, 2 gdr_scan, 3 gdr_output (the prefill
- * kernels, in launch order) and 4 gdr_decode.  Off is the default; the hooks
- * then cost nothing measurable.
+ * kernels, in launch order) and 4 gdr_decode.  With a per-key gate and a
+ * one-level scan the scan forms the output itself and gdr_output records no
+ * launch.  Off is the default; the hooks then cost nothing measurable.
  */
 #define GDR_TIMING_KERNELS 5
 #define GDR_TIMING_ALL (-1)
