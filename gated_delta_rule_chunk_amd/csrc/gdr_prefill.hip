@@ -1320,8 +1320,14 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     const int stride = gridDim.x;   // a multiple of 8 G
     int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
     if (it >= n_items) return;
+    // Slot it holds item n_items - 1 - it: the last chunks first, so that the
+    // first chunks, which the scan reads first, are the freshest in the
+    // last-level cache when it starts (n_items is a multiple of G, so the G
+    // value heads of a chunk keep consecutive slots).  Measured faster for
+    // this scan, which also fetches q^ e^G and P each step; the intra kernel
+    // without the gate keeps chunk order, which measured faster for its scan.
     GkStage<ActT> st;
-    gk_place<ActT>(st, p, it);
+    gk_place<ActT>(st, p, n_items - 1 - it);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) gk_gate_dma(p, st.t0, st.h, st.r, sG, q4, tid);
     gk_load_in<ActT, RULE>(st, p, 0, tid);
@@ -1329,7 +1335,8 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     gk_load_in<ActT, RULE>(st, p, 2, tid);
     while (true) {
         const int nx = it + stride;
-        gk_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sG, sK, sQL, sD, sEs, sTail, sC, sGt, sBeta, sBw, sWide, tid);
+        gk_item<ActT, RULE>(st, n_items - 1 - (nx < n_items ? nx : it), p, sG, sK, sQL, sD, sEs, sTail, sC, sGt, sBeta,
+                            sBw, sWide, tid);
         if (nx >= n_items) break;
         it = nx;
     }
@@ -1701,7 +1708,10 @@ __global__ __launch_bounds__(512, 4) void output_kernel(PrefillDev p) {
     __shared__ __align__(16) float sG[128];   // g_cum of the chunk
 
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
-    const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
+    // the grid is a multiple of 8 G; items are taken last chunk first, the
+    // ones whose S_c and v_new the scan wrote last and the last-level cache
+    // most likely still holds
+    const int item = (int)gridDim.x - 1 - group_slot(blockIdx.x, G);
     const int c = item / Nv, h = item % Nv, hq = h / G;
     if (c >= ld_uniform(&p.meta[p.B])) return;
     const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
@@ -1856,7 +1866,10 @@ __global__ __launch_bounds__(512) void output_gk_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sBuf[128 * LD16];
     __shared__ __align__(16) float sStage[8 * 16 * 68];   // each wave's 16 output rows, 64 columns at a time
     const int Nv = p.Nv, Nqk = p.Nqk, G = Nv / Nqk;
-    const int item = group_slot(blockIdx.x, G);   // the grid is a multiple of 8 G
+    // the grid is a multiple of 8 G; items are taken last chunk first, the
+    // ones whose S_c and v_new the scan wrote last and the last-level cache
+    // most likely still holds
+    const int item = (int)gridDim.x - 1 - group_slot(blockIdx.x, G);
     const int c = item / Nv, h = item % Nv;
     if (c >= ld_uniform(&p.meta[p.B])) return;
     const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
