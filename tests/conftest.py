@@ -13,8 +13,8 @@ def pytest_configure(config):
 
 
 def pytest_collection_modifyitems(config, items):
-    # GPU tests are skipped, not failed, where no GPU is visible; on a GPU machine
-    # they run (and a missing HIP library is a hard failure inside them).
+    # GPU tests are skipped, not failed, where no GPU is visible; on a machine
+    # with one they run (and a missing HIP library is a hard failure inside them).
     try:
         import torch
         have_gpu = torch.cuda.is_available()
