@@ -179,15 +179,17 @@ def test_prefill_gqa_group_sizes(Nqk, Nv):
     check_parity(inp, f"Nqk={Nqk} Nv={Nv}")
 
 
-def test_prefill_many_short_sequences():
+@pytest.mark.parametrize("gk", [None, "strong"])
+def test_prefill_many_short_sequences(gk):
     """300 sequences (more than one 256-wide pass of the chunk-map prefix),
-    lengths 0..200 including empty ones."""
+    lengths 0..200 including empty ones; with gk, 600 one- or two-chunk
+    streams through the scan that forms the output itself."""
     rng = np.random.default_rng(99)
     lens = rng.integers(0, 201, 300).tolist()
     lens[5] = 0
     lens[299] = 0
-    inp = workloads.prefill_inputs(98, lens, Nqk=1, Nv=2, act="bf16")
-    check_parity(inp, f"B=300 T={sum(lens)}")
+    inp = workloads.prefill_inputs(98, lens, Nqk=1, Nv=2, act="bf16", gk=gk)
+    check_parity(inp, f"B=300 T={sum(lens)} gk={gk}")
 
 
 # Two-level scan: with few (sequence, value head) streams and long sequences
