@@ -55,6 +55,14 @@ namespace {
 constexpr int LD16 = 136;   // fp16 LDS row stride (elements): 272 B, 16-byte aligned rows
 constexpr int TILE = 128 * 128;
 constexpr float kNormEps = 1e-6f;
+// Per-token log-decays (g, or g + gk[d] with a per-key gate) below
+// -kLogDecayFloor act as -kLogDecayFloor.  exp(-80) = 1.8e-35, so a term that
+// passes through such a decay is already below fp32 resolution next to any
+// term that does not, and the result cannot change; the floor keeps the
+// chunk-local prefix sums G small enough (|G| <= 128 * 80) that differences
+// G_i - G_j of tokens behind a reset (a gate of, say, -1e4) keep fp32
+// precision.
+constexpr float kLogDecayFloor = 80.f;
 
 // Update rules ("LinearAttention" page, update_rule; codes as in the C ABI):
 // 0 gated_delta, 1 delta (no decay), 2 gated (no delta term), 3 linear
@@ -457,7 +465,8 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     // ---- 1. gate cumulative sum and beta (wave 0); k rows normalised -> sA (row-major)
     if (wave == 0) {   // lane owns rows 2l, 2l+1
         const int i0 = 2 * lane, i1 = i0 + 1;
-        const float g0 = i0 < r ? st.g0 : 0.f, g1 = i1 < r ? st.g1 : 0.f;
+        const float g0 = i0 < r ? fmaxf(st.g0, -kLogDecayFloor) : 0.f;
+        const float g1 = i1 < r ? fmaxf(st.g1, -kLogDecayFloor) : 0.f;
         // without the delta term beta is 1 for u = T v and 0 for w (below)
         const float b0 = i0 < r ? (Rule<RULE>::delta ? load1(&st.b0) : 1.f) : 0.f;
         const float b1 = i1 < r ? (Rule<RULE>::delta ? load1(&st.b1) : 1.f) : 0.f;
@@ -732,7 +741,10 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
 //          <= 1, so the MFMA operands are scaled keys / queries (fp16);
 //   J = I  through G at the block's middle row m = 16 I + 7: factors up to
 //          exp(8 max|g + gk|); in fp16 when every |G_i - G_m| of the block
-//          is within kDiagF16Range, else in fp32 on the 16x16x4 fp32 MFMA.
+//          is within kDiagF16Range, in fp32 on the 16x16x4 fp32 MFMA when
+//          within kDiagF32Range, and past that (a strong gate or a reset of
+//          some keys) element by element, exp(G_i[d] - G_j[d]) <= 1 per
+//          term, so nothing over- or underflows whatever the gates.
 // The decay between blocks, exp(G_s(I) - G_e(J)), and the per-block factors
 // come from running products of the block decays, not per element.
 // The item stores k^T exp(G_last - G) (the scan's k^T, per value head),
@@ -829,6 +841,10 @@ constexpr int kGateHi = 128 * LD16 / 2;
 // scaled operands then stay within e^6, and a subnormal one errs by at most
 // e^6 2^-25 in a product.
 constexpr float kDiagF16Range = 6.f;
+// Largest |G_i - G_m| for which the block's diagonal tiles are taken on the
+// fp32 MFMA: both factors exp(+-(G_i - G_m)) then stay normal fp32 numbers
+// (e^60 = 1.1e26); wider blocks are formed element by element.
+constexpr float kDiagF32Range = 60.f;
 static_assert(kGateHi + 64 * 128 <= 128 * LDG, "gate staging fits G's region");
 
 // Quarter q4 of the gate tile of the item at (t0, h, r) (tokens 32 q4 ..
@@ -923,7 +939,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         const float* stg = sG + (qt < 2 ? kGateHi + 32 * qt * 128 : (32 * qt - 64) * 128) + d;
         float x[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) x[i] = stg[i * 128] + sGt[32 * qt + i];
+        for (int i = 0; i < 32; ++i) x[i] = fmaxf(stg[i * 128] + sGt[32 * qt + i], -kLogDecayFloor);
         if (32 * qt + 31 >= r) {   // the chunk ends in this quarter
 #pragma unroll
             for (int i = 0; i < 32; ++i) x[i] = 32 * qt + i < r ? x[i] : 0.f;
@@ -932,17 +948,22 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
         for (int i = 1; i < 32; ++i) x[i] += x[i - 1];
         sD[qt * 128 + d] = x[31];
         // blocks 2 qt, 2 qt + 1: is every |G_i - G_m| (m: the block's middle
-        // row) within kDiagF16Range, for this wave's 64 keys?
-        bool wide0 = false, wide1 = false;
+        // row) within kDiagF16Range (tier 0), within kDiagF32Range (tier 1)
+        // or neither (tier 2), for this wave's 64 keys?
+        bool wide0 = false, wide1 = false, huge0 = false, huge1 = false;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            wide0 |= !(fabsf(x[i] - x[7]) <= kDiagF16Range);
-            wide1 |= !(fabsf(x[16 + i] - x[23]) <= kDiagF16Range);
+            const float a0 = fabsf(x[i] - x[7]), a1 = fabsf(x[16 + i] - x[23]);
+            wide0 |= !(a0 <= kDiagF16Range);
+            wide1 |= !(a1 <= kDiagF16Range);
+            huge0 |= !(a0 <= kDiagF32Range);
+            huge1 |= !(a1 <= kDiagF32Range);
         }
         const bool w0 = __ballot(wide0) != 0, w1 = __ballot(wide1) != 0;
+        const bool h0 = __ballot(huge0) != 0, h1 = __ballot(huge1) != 0;
         if ((tid & 63) == 0) {
-            sWide[(2 * qt) * 2 + (d >> 6)] = w0;
-            sWide[(2 * qt + 1) * 2 + (d >> 6)] = w1;
+            sWide[(2 * qt) * 2 + (d >> 6)] = h0 ? 2 : w0 ? 1 : 0;
+            sWide[(2 * qt + 1) * 2 + (d >> 6)] = h1 ? 2 : w1 ? 1 : 0;
         }
         __syncthreads();
         float off = 0.f;
@@ -998,14 +1019,14 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     // d = 32 lq + 8 c8 + e of row 16 Id + lr to both operands, scaled by
     // exp(+-(G_row - G_m)).  In fp16 when every |G_row - G_m| of the block is
     // within kDiagF16Range (operands at most e^6, as precise as the other
-    // tiles), else in fp32.
+    // tiles), in fp32 when within kDiagF32Range, else element by element.
     const int pp = wave >> 1;
     const int Id = (wave & 1) ? 7 - pp : pp;
     f32x4 pdiag = {0.f, 0.f, 0.f, 0.f}, ldiag = {0.f, 0.f, 0.f, 0.f};
     {
         const int rw = 16 * Id + lr, m = 16 * Id + 7;
-        const bool narrow = __builtin_amdgcn_readfirstlane(sWide[2 * Id] | sWide[2 * Id + 1]) == 0;
-        if (narrow) {
+        const int tier = __builtin_amdgcn_readfirstlane(max(sWide[2 * Id], sWide[2 * Id + 1]));
+        if (tier == 0) {
 #pragma unroll
             for (int c8 = 0; c8 < 4; ++c8) {
                 const int d0 = 32 * lq + 8 * c8;
@@ -1024,7 +1045,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
                 pdiag = mma(kdh, to_h8(qu), pdiag);                      // C[j][i] = P[i][j]
                 if constexpr (kDelta) ldiag = mma(kdh, to_h8(ku), ldiag);   // C[j][i] = L[i][j]
             }
-        } else {
+        } else if (tier == 1) {
 #pragma unroll
             for (int c8 = 0; c8 < 4; ++c8) {
                 const int d0 = 32 * lq + 8 * c8;
@@ -1038,6 +1059,33 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
                     const float kd = (float)kx[e] * dn;
                     pdiag = mma_f32(kd, (float)qx[e] * up, pdiag);   // C[j][i] = P[i][j]
                     if constexpr (kDelta) ldiag = mma_f32(kd, (float)kx[e] * up, ldiag);   // C[j][i] = L[i][j]
+                }
+            }
+        } else {
+            // element by element: lane (lr, lq) forms P[i][j] and L[i][j] for
+            // i = 16 Id + lr and j = 16 Id + 4 lq + e, the entries its
+            // accumulators hold in the MFMA tiers, as sum_d q^_i[d] k^_j[d]
+            // exp(G_i[d] - G_j[d]) (and k^_i for L); only j <= i are used, and
+            // there each exponent is <= 0 (it is clamped to 0, so the
+            // unused entries stay finite too)
+            const int i = rw;
+            for (int d0 = 0; d0 < 128; d0 += 8) {
+                const half8 qi = ld_h8(&sQL[i * LD16 + d0]), ki = ld_h8(&sK[i * LD16 + d0]);
+                float gi[8];
+                ld_f8(&sG[i * LDG + d0], gi);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 16 * Id + 4 * lq + e;
+                    if (j > i) continue;
+                    const half8 kj = ld_h8(&sK[j * LD16 + d0]);
+                    float gj[8];
+                    ld_f8(&sG[j * LDG + d0], gj);
+#pragma unroll
+                    for (int x = 0; x < 8; ++x) {
+                        const float kf = (float)kj[x] * __expf(fminf(gi[x] - gj[x], 0.f));
+                        pdiag[e] = fmaf((float)qi[x], kf, pdiag[e]);
+                        if constexpr (kDelta) ldiag[e] = fmaf((float)ki[x], kf, ldiag[e]);
+                    }
                 }
             }
         }
@@ -1314,7 +1362,7 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     __shared__ __align__(16) float sTail[8 * 128];         // exp(G_last - G) at each block's last token
     __shared__ __align__(16) _Float16 sC[21 * 128];        // decay between blocks J + 1 < I
     __shared__ float sGt[128], sBeta[128], sBw[128];
-    __shared__ int sWide[16];                              // per block and key half: |G - G_m| too wide for fp16
+    __shared__ int sWide[16];                              // per block and key half: tier of the diagonal tiles
     const int tid = threadIdx.x;
     const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
     const int stride = gridDim.x;   // a multiple of 8 G
@@ -1512,10 +1560,15 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
     const size_t sd = ((size_t)b * nseg + seg) * Nv + h;   // (sequence, segment, head) index
 
     // S rows 16*wv + 4*lq + e (key dims), columns col0 + 16*ct + lr
+    // A sequence cut into several segments starts every segment from the
+    // start state the combine pass wrote, segment 0's included (a copy of
+    // the initial state): the last segment writes state_out during this same
+    // launch, and state_out may alias state_in.  A sequence of one segment
+    // reads state_in and writes state_out from the same threads.
     f32x4 S[CT];
     const float* sinit = MODE == 1 ? nullptr
-                         : seg == 0 ? (p.state_in ? p.state_in + (size_t)stream * TILE : nullptr)
-                                    : p.sstart + sd * TILE;
+                         : nsb > 1 ? p.sstart + sd * TILE
+                                   : (p.state_in ? p.state_in + (size_t)stream * TILE : nullptr);
 #pragma unroll
     for (int ct = 0; ct < CT; ++ct)
 #pragma unroll
@@ -1602,6 +1655,8 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
 
 // Two-level scan, second level: the start state of every segment of a
 // stream, S_0 = the stream's initial state, S_{s+1} = M_s S_s + B_s, in fp32.
+// S_0 is written too, so that the scan proper reads no segment's start from
+// state_in (state_out may alias it and is written by the last segment).
 // One workgroup of 256 threads per (stream, 8 state columns); thread t owns
 // rows 2 (t / 4), 2 (t / 4) + 1 and columns 2 (t % 4), 2 (t % 4) + 1 of the
 // slice.  M sits row-major and the S slice transposed in LDS, so four k of
@@ -1625,6 +1680,11 @@ __global__ __launch_bounds__(256) void combine_kernel(PrefillDev p) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             x[i][j] = p.state_in ? p.state_in[(size_t)stream * TILE + (size_t)(r0 + i) * 128 + col0 + c2 + j] : 0.f;
+    {
+        float* dst0 = p.sstart + (((size_t)b * nseg) * Nv + h) * TILE + (size_t)r0 * 128 + col0 + c2;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) *reinterpret_cast<float2*>(dst0 + (size_t)i * 128) = float2{x[i][0], x[i][1]};
+    }
     const int last = nsb - 2;   // the last map used
     f32x4 mr[16];               // float4 number tid + 256 n of M: row (q / 32), columns 4 (q % 32) ..
     float2 br[2];               // B, rows r0 + i, this thread's two columns

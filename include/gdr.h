@@ -42,11 +42,21 @@
 extern "C" {
 #endif
 
+/* The enums below are passed and returned as C ints.  In C++ they get int as
+ * their fixed underlying type, so that an implementation may receive any int
+ * value (and reject the unknown ones) without undefined behaviour; in C an
+ * enum with these values is an int already. */
+#ifdef __cplusplus
+#define GDR_ENUM_INT : int
+#else
+#define GDR_ENUM_INT
+#endif
+
 /* Status codes.  The Python binding maps GDR_ERR_INVALID_ARGUMENT to
  * ValueError (shape / count / grouping errors, as the decode page's
  * exceptions section assigns them) and every other failure to RuntimeError
  * (dtype errors and backend failures, as the same section assigns them). */
-typedef enum gdr_status {
+typedef enum gdr_status GDR_ENUM_INT {
     GDR_OK = 0,
     GDR_ERR_INVALID_ARGUMENT = 1, /* bad size, count, head grouping or NULL pointer */
     GDR_ERR_UNSUPPORTED = 2,      /* allowed by the pages but not built here (e.g. D != 128) */
@@ -59,7 +69,7 @@ typedef enum gdr_status {
 /* Element dtypes.  GDR_FP16 is IEEE binary16 (the LinearAttention page
  * allows float16 or float32 activations and state); GDR_BF16 is the
  * recurrent_gated_delta_rule page's dtype. */
-typedef enum gdr_dtype {
+typedef enum gdr_dtype GDR_ENUM_INT {
     GDR_FP32 = 0,
     GDR_BF16 = 1,
     GDR_FP16 = 2
@@ -74,7 +84,7 @@ typedef enum gdr_dtype {
  *   GDR_RULE_GATED        no delta term: S = S exp(g) exp(gk) + k v^T
  *                         (beta is ignored and may be NULL)
  *   GDR_RULE_LINEAR       neither: S = S + k v^T */
-typedef enum gdr_update_rule {
+typedef enum gdr_update_rule GDR_ENUM_INT {
     GDR_RULE_GATED_DELTA = 0,
     GDR_RULE_DELTA = 1,
     GDR_RULE_GATED = 2,
@@ -122,11 +132,14 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  *   v           [T, Nv, D]    act dtype
  *   g           [T, Nv]       fp32        log-decay gate (expected < 0)
  *   gk          [T, Nv, D]    fp32 or NULL: per-key log-decay gate (the decode
- *                             page's gk, applied at every token; expected < 0
- *                             and, per token, g + gk >= -11 so that a
- *                             16-token block's decay stays within fp32);
- *                             ignored by the rules without decay.  A non-NULL
- *                             gk needs the workspace queried with with_gk = 1
+ *                             page's gk, applied at every token; expected < 0,
+ *                             of any magnitude: a gk of -1e4 resets its key
+ *                             row of the state); ignored by the rules without
+ *                             decay.  A non-NULL gk needs the workspace
+ *                             queried with with_gk = 1.  Per-token log-decays
+ *                             (g, or g + gk) below -80 act as -80: exp(-80) is
+ *                             below fp32 resolution, so this changes nothing
+ *                             visible and keeps the chunk sums in range
  *   beta        [T, Nv]       act dtype   (expected in [0, 1])
  *   state_in    [B, Nv, D, D] fp32 or NULL (= zeros); key dim = rows
  *   cu_seqlens  [B + 1]       int32, device; cu[0] = 0, non-decreasing, cu[B] = T
