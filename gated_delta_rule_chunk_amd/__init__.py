@@ -22,7 +22,10 @@ import os
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgdr.so")
+# GDR_LIBRARY may name another build of the same C ABI (the tests use it for
+# a host-side sanitizer build of the validation layer); unset, the in-tree
+# library is loaded.
+LIB_PATH = os.environ.get("GDR_LIBRARY") or os.path.join(_HERE, "libgdr.so")
 
 GDR_OK = 0
 GDR_ERR_INVALID_ARGUMENT = 1

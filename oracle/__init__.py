@@ -28,26 +28,36 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "gdr_oracle.c")
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_PLAIN_LIB = os.path.join(_HERE, "liboracle.so")
+# A build instrumented with AddressSanitizer and UndefinedBehaviorSanitizer
+# (every finding aborts); selected with GDR_ORACLE_SANITIZED=1, in a process
+# that preloads the sanitizer runtimes.
+_SAN_LIB = os.path.join(_HERE, "liboracle_san.so")
+SANITIZED = os.environ.get("GDR_ORACLE_SANITIZED") == "1"
+_LIB_PATH = _SAN_LIB if SANITIZED else _PLAIN_LIB
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile the oracle with gcc (-O2, OpenMP, IEEE fp64 semantics)."""
-    if force or not os.path.exists(_LIB_PATH):
-        tmp = _LIB_PATH + ".tmp"
+def build(force: bool = True, sanitized: bool = False) -> str:
+    """Compile the oracle with gcc (-O2, OpenMP, IEEE fp64 semantics); with
+    `sanitized`, the ASan + UBSan build instead."""
+    path = _SAN_LIB if sanitized else _PLAIN_LIB
+    if force or not os.path.exists(path):
+        tmp = path + ".tmp"
+        san = ["-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+               "-fno-sanitize-recover=all"] if sanitized else []
         subprocess.check_call(
-            ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", "-shared", "-fPIC",
+            ["gcc", "-O2", "-fopenmp", "-ffp-contract=off", *san, "-shared", "-fPIC",
              "-o", tmp, _SRC, "-lm"])
-        os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+        os.replace(tmp, path)
+    return path
 
 
 def _load():
     global _lib
     if _lib is None:
         if not os.path.exists(_LIB_PATH):
-            build(force=True)
+            build(force=True, sanitized=SANITIZED)
         lib = ctypes.CDLL(_LIB_PATH)
         dp = ctypes.POINTER(ctypes.c_double)
         ip = ctypes.POINTER(ctypes.c_int32)

@@ -60,22 +60,60 @@ def test_prefill_varlen_b4_t8192_nqk16_nv32_bf16():
     check_parity(workloads.config_inputs(2), "B=4 T=8192 Nqk=16 Nv=32 bf16")
 
 
-def test_prefill_long_context_t131072_sampled_heads():
-    """Full-size long-context workload on the GPU; the oracle checks two value
-    heads (the first and last, different qk heads) over all 131072 tokens."""
-    inp = workloads.config_inputs(5)
+def test_prefill_long_context_t131072_all_heads():
+    """Full-size long-context workload (B=1, T=131072, Nqk=16, Nv=32): every
+    value head over all 131072 tokens against the oracle."""
+    check_parity(workloads.config_inputs(5), "T=131072 Nqk=16 Nv=32 bf16, all heads")
+
+
+def test_prefill_element_offsets_past_2_31():
+    """Token offsets past 2^31 elements of v and out ([T, 32, 128] at
+    T = 540672) and workspace tiles past 2^31 elements: two sequences,
+    532480 + 8192 tokens.  The oracle checks the second sequence on every
+    value head (its tokens all lie past element 2^31) and the first sequence
+    on its first and last value heads over all its tokens."""
+    lens = [532480, 8192]
+    inp = workloads.large_prefill_inputs(12, lens, Nqk=16, Nv=32)
+    assert inp["T"] * inp["Nv"] * 128 > 2 ** 31 and lens[0] * inp["Nv"] * 128 > 2 ** 31
+    print(f"[prefill parity] offsets past 2^31: lens {lens}", flush=True)
     out, st = run_gpu(inp)
+    t1 = lens[0]
+    second = dict(inp, q=inp["q"][t1:], k=inp["k"][t1:], v=inp["v"][t1:], g=inp["g"][t1:],
+                  beta=inp["beta"][t1:], state_in=inp["state_in"][1:],
+                  cu_seqlens=torch.tensor([0, lens[1]], dtype=torch.int32))
+    o_ref, s_ref = run_oracle(second)
+    exc, lit = assert_out_close(out[t1:], o_ref, True, "second sequence out")
+    es = assert_state_close(st[1:], s_ref, "second sequence state")
+    print(f"    second sequence, all heads: out {exc:.2e} (literal {lit:.2e}); state {es:.2e}", flush=True)
     G = inp["Nv"] // inp["Nqk"]
     for h in (0, inp["Nv"] - 1):
         hq = h // G
-        sub = dict(q=inp["q"][:, hq:hq + 1], k=inp["k"][:, hq:hq + 1], v=inp["v"][:, h:h + 1],
-                   g=inp["g"][:, h:h + 1], beta=inp["beta"][:, h:h + 1],
-                   state_in=inp["state_in"][:, h:h + 1], cu_seqlens=inp["cu_seqlens"], scale=inp["scale"])
-        print(f"[prefill parity] T=131072 head {h}", flush=True)
+        sub = dict(q=inp["q"][:t1, hq:hq + 1], k=inp["k"][:t1, hq:hq + 1], v=inp["v"][:t1, h:h + 1],
+                   g=inp["g"][:t1, h:h + 1], beta=inp["beta"][:t1, h:h + 1],
+                   state_in=inp["state_in"][:1, h:h + 1], cu_seqlens=torch.tensor([0, t1], dtype=torch.int32),
+                   scale=inp["scale"])
         o_ref, s_ref = run_oracle(sub)
-        exc, lit = assert_out_close(out[:, h:h + 1], o_ref, True, f"T=131072 head {h} out")
-        es = assert_state_close(st[:, h:h + 1], s_ref, f"T=131072 head {h} state")
-        print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}); state relFro {es:.2e}", flush=True)
+        exc, lit = assert_out_close(out[:t1, h:h + 1], o_ref, True, f"first sequence head {h} out")
+        es = assert_state_close(st[:1, h:h + 1], s_ref, f"first sequence head {h} state")
+        print(f"    first sequence head {h}: out {exc:.2e} (literal {lit:.2e}); state {es:.2e}", flush=True)
+
+
+def test_prefill_strong_gate_without_per_key_gate():
+    """The decode page's gate range g = -U(0.01, 1.01) in the prefill: the
+    chunk-local decays reach e^-128, so k^ beta e^{g_cum} underflows fp16 in
+    the stored w tile and most intra-chunk terms vanish."""
+    inp = workloads.prefill_inputs(63, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", g_range=(0.01, 1.01))
+    check_parity(inp, "T=8192 varlen, g = -U(0.01, 1.01)")
+
+
+@pytest.mark.parametrize("rule,g_range", [("linear", (0.001, 0.1)), ("gated_delta", (1e-6, 1e-5))])
+def test_prefill_long_sequence_without_forgetting(rule, g_range):
+    """32768 tokens with no decay (the linear rule, whose state only grows)
+    and with a gate of about 1e-5 per token: the state carried across 256
+    chunks stays large, which the fp16 copy of S inside the scan must
+    hold."""
+    inp = workloads.prefill_inputs(64, [32768], Nqk=1, Nv=2, act="bf16", g_range=g_range)
+    check_parity(inp, f"T=32768 rule {rule} g=-U{g_range}", rule=rule)
 
 
 def test_prefill_empty_sequences_pass_state_through():
@@ -222,21 +260,25 @@ def test_prefill_two_level_scan_fp32_weak_forgetting():
     check_parity(inp, "two-level T=9000 Nqk=1 Nv=1 fp32, weak forgetting")
 
 
-def test_prefill_two_level_scan_long_few_heads_sampled():
-    """Full-size few-head long-context workload (two-level scan); the oracle
-    checks the first and last value heads over all 131072 tokens."""
-    inp = workloads.extra_inputs("long_few_heads")
-    out, st = run_gpu(inp)
-    for h in (0, inp["Nv"] - 1):
-        sub = dict(q=inp["q"], k=inp["k"], v=inp["v"][:, h:h + 1], g=inp["g"][:, h:h + 1],
-                   beta=inp["beta"][:, h:h + 1], state_in=inp["state_in"][:, h:h + 1],
-                   cu_seqlens=inp["cu_seqlens"], scale=inp["scale"])
-        print(f"[prefill parity] two-level T=131072 Nv=4 head {h}", flush=True)
-        o_ref, s_ref = run_oracle(sub)
-        exc, lit = assert_out_close(out[:, h:h + 1], o_ref, True, f"two-level T=131072 head {h} out")
-        es = assert_state_close(st[:, h:h + 1], s_ref, f"two-level T=131072 head {h} state")
-        print(f"    out err beyond rounding {exc:.2e} (literal {lit:.2e}); state relFro {es:.2e}", flush=True)
+def test_prefill_two_level_scan_long_few_heads_all_heads():
+    """Full-size few-head long-context workload (two-level scan): every value
+    head over all 131072 tokens against the oracle."""
+    check_parity(workloads.extra_inputs("long_few_heads"), "two-level T=131072 Nqk=1 Nv=4, all heads")
 
+
+def test_prefill_two_level_scan_state_out_may_alias_state_in():
+    """On the two-level path the last segment writes state_out in the same
+    launch in which the first segment starts; with state_out aliasing
+    state_in the result must not change."""
+    inp = workloads.prefill_inputs(65, [20000, 3000], Nqk=1, Nv=2, act="bf16")
+    d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
+    s = d["state_in"].clone()
+    out, _ = gdr.chunk_prefill(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], d["scale"],
+                               state_in=s, state_out=s)
+    torch.cuda.synchronize()
+    out_ref, st_ref = run_oracle(inp)
+    assert_out_close(out.cpu(), out_ref, True, "two-level aliased out")
+    assert_state_close(s.cpu(), st_ref, "two-level aliased state")
 
 
 # Per-key gate gk [T, Nv, D]: the decay between tokens differs per key, so the
@@ -287,3 +329,20 @@ def test_prefill_per_key_gate_two_level_scan():
     inp = workloads.prefill_inputs(84, [20000], Nqk=1, Nv=2, act="bf16", gk="weak")
     check_parity(inp, "gk weak two-level T=20000 Nqk=1 Nv=2 bf16")
 
+
+
+@pytest.mark.parametrize("strength", ["extreme", "reset"])
+def test_prefill_per_key_gate_any_magnitude(strength):
+    """Per-key gates far outside the decode page's example range: g + gk down
+    to about -40 per token ("extreme"), and a reset gk = -1e4 on about one
+    (token, head, key) in a hundred ("reset"), which wipes that key row of
+    the state.  The diagonal 16-token blocks then need the element-by-element
+    tier (and the others the fp32 and fp16 ones)."""
+    lens = [1, 127, 128, 129, 300, 0, 77, 1000]
+    inp = workloads.prefill_inputs(66, lens, Nqk=2, Nv=4, act="bf16", gk=strength)
+    check_parity(inp, f"gk {strength} ragged varlen {lens}")
+
+
+def test_prefill_per_key_gate_reset_t8192():
+    inp = workloads.prefill_inputs(67, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", gk="reset")
+    check_parity(inp, "gk reset T=8192 varlen Nqk=16 Nv=32")

@@ -48,15 +48,19 @@ def _sigmoid(x):
 
 
 def prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128, act: str = "bf16",
-                   init_state: str = "randn", scale: float | None = None, gk: str | None = None):
+                   init_state: str = "randn", scale: float | None = None, gk: str | None = None,
+                   g_range=(0.001, 0.1)):
     """Packed varlen prefill inputs.
 
     Returns a dict of CPU tensors: q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv]
     (act dtype); g [T,Nv] fp32; state_in [B,Nv,D,D] fp32 or None;
     cu_seqlens [B+1] int32; gk [T,Nv,D] fp32 or None; plus scale, T, B, Nqk,
-    Nv, D, act.  gk: None; "strong", the decode page's example range
-    -U(0.01, 1.01); or "weak", -U(0.001, 0.05), under which the state carries
-    across chunks.  gk is drawn last, so the other inputs do not depend on it.
+    Nv, D, act.  g = -U(g_range).  gk: None; "strong", the decode page's
+    example range -U(0.01, 1.01); "weak", -U(0.001, 0.05), under which the
+    state carries across chunks; "extreme", -U(0.01, 40); or "reset", weak
+    everywhere except about one (token, value head, key) entry in a hundred,
+    where it is -1e4 (that key row of the state is wiped before the token's
+    update).  gk is drawn last, so the other inputs do not depend on it.
     """
     rng = np.random.Generator(np.random.PCG64(seed))
     seq_lens = [int(x) for x in seq_lens]
@@ -68,7 +72,7 @@ def prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128, act: st
     k = _normal_blocks(rng, (T, Nqk, D), dtype=act)
     v = _normal_blocks(rng, (T, Nv, D), dtype=act)
     beta = _cast(_sigmoid(rng.standard_normal((T, Nv))), act)
-    g = _cast(-rng.uniform(0.001, 0.1, (T, Nv)), "fp32")
+    g = _cast(-rng.uniform(g_range[0], g_range[1], (T, Nv)), "fp32")
     if init_state == "zeros":
         state_in = None
     elif init_state == "randn":
@@ -77,14 +81,48 @@ def prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128, act: st
         raise ValueError(init_state)
     if gk is None:
         gkt = None
-    elif gk in ("strong", "weak"):
-        lo, hi = (0.01, 1.01) if gk == "strong" else (0.001, 0.05)
+    elif gk in ("strong", "weak", "extreme"):
+        lo, hi = {"strong": (0.01, 1.01), "weak": (0.001, 0.05), "extreme": (0.01, 40.0)}[gk]
         gkt = _cast(-rng.uniform(lo, hi, (T, Nv, D)), "fp32")
+    elif gk == "reset":
+        x = -rng.uniform(0.001, 0.05, (T, Nv, D))
+        x[rng.random((T, Nv, D)) < 0.01] = -1e4
+        gkt = _cast(x, "fp32")
     else:
         raise ValueError(gk)
     return dict(q=q, k=k, v=v, g=g, beta=beta, state_in=state_in,
                 cu_seqlens=torch.from_numpy(cu), scale=SCALE_128 if scale is None else scale,
                 T=T, B=B, Nqk=Nqk, Nv=Nv, D=D, act=act, gk=gkt)
+
+
+def large_prefill_inputs(seed: int, seq_lens, Nqk: int, Nv: int, D: int = 128):
+    """Packed varlen bf16 prefill inputs too large to draw in fp64 in
+    reasonable time (hundreds of thousands of tokens): the same
+    distributions as prefill_inputs (q, k, v ~ N(0,1); beta =
+    sigmoid(N(0,1)); g = -U(0.001, 0.1); state_in ~ N(0, 0.02^2)), drawn in
+    fp32 from torch's seeded CPU generator and cast to bf16.  Same dict
+    layout as prefill_inputs (gk None)."""
+    gen = torch.Generator().manual_seed(seed)
+    seq_lens = [int(x) for x in seq_lens]
+    B, T = len(seq_lens), int(sum(seq_lens))
+    cu = torch.zeros(B + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(torch.tensor(seq_lens, dtype=torch.int64), 0).to(torch.int32)
+
+    def normal(shape, std=1.0, dtype=torch.bfloat16, rows=65536):
+        out = torch.empty(shape, dtype=dtype)
+        for r0 in range(0, shape[0], rows):
+            r1 = min(shape[0], r0 + rows)
+            out[r0:r1] = (torch.randn((r1 - r0,) + tuple(shape[1:]), generator=gen) * std).to(dtype)
+        return out
+
+    q = normal((T, Nqk, D))
+    k = normal((T, Nqk, D))
+    v = normal((T, Nv, D))
+    beta = torch.sigmoid(torch.randn((T, Nv), generator=gen)).to(torch.bfloat16)
+    g = -(0.001 + 0.099 * torch.rand((T, Nv), generator=gen))
+    state_in = normal((B, Nv, D, D), std=0.02, dtype=torch.float32, rows=1)
+    return dict(q=q, k=k, v=v, g=g.contiguous(), beta=beta.contiguous(), state_in=state_in, cu_seqlens=cu,
+                scale=SCALE_128, T=T, B=B, Nqk=Nqk, Nv=Nv, D=D, act="bf16", gk=None)
 
 
 def _unit_rows(rng, shape):
