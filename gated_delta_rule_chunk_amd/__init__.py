@@ -8,6 +8,7 @@ fallback.
 
 Functions mirror the C entry points:
   chunk_prefill(...)                 gdr_chunk_prefill
+  chunk_prefill_noalloc(...)         gdr_chunk_prefill_noalloc
   chunk_prefill_workspace_size(...)  gdr_chunk_prefill_workspace_size
   recurrent_decode(...)              gdr_recurrent_decode
 Errors follow the decode page's exceptions section: shape and grouping
@@ -50,6 +51,9 @@ SIGNATURES = {
     "gdr_chunk_prefill": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32,
                                          _i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp, _vp, _vp,
                                          ctypes.c_size_t, _vp]),
+    "gdr_chunk_prefill_noalloc": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32,
+                                                 _i32, _i32, ctypes.c_float, ctypes.c_int, ctypes.c_int, _vp,
+                                                 _vp, _vp]),
     "gdr_recurrent_decode": (ctypes.c_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _i32,
                                             _i32, _i32, _i32, _i32, _i32, ctypes.c_float,
                                             ctypes.c_int, ctypes.c_int, ctypes.c_int, _vp, _vp]),
@@ -159,19 +163,9 @@ def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128
     return int(n.value)
 
 
-def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, state_out=None,
-                  workspace=None, rule="gated_delta", gk=None):
-    """Chunked Gated Delta Rule prefill ("Qwen3Next Samples" page).
-
-    q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv] (act dtype: bf16, fp16 or fp32);
-    g [T,Nv] fp32; cu_seqlens [B+1] int32; state_in [B,Nv,D,D] fp32 or None;
-    rule one of RULES (g may be None without a gate, beta without the delta
-    term); gk [T,Nv,D] fp32 or None: the per-key gate (ignored by the rules
-    without decay).
-    Returns (out [T,Nv,D] act dtype, state_out [B,Nv,D,D] fp32).  `out`,
-    `state_out` and `workspace` (uint8, >= chunk_prefill_workspace_size
-    bytes) may be passed in to avoid allocations.
-    """
+def _prefill_checked(q, k, v, g, beta, cu_seqlens, state_in, out, state_out, rule, gk):
+    """Shape, dtype and device checks shared by the prefill entry points;
+    returns (sizes, rule code, act code, gk used, out, state_out)."""
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3 or v.shape[0] != q.shape[0]:
         raise ValueError(f"q, k must be [T,Nqk,D] and v [T,Nv,D] (got {tuple(q.shape)}, "
                          f"{tuple(k.shape)}, {tuple(v.shape)})")
@@ -212,16 +206,52 @@ def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, 
         raise ValueError("out must be [T,Nv,D] of q's dtype")
     if state_out.shape != (B, Nv, D, D) or state_out.dtype != torch.float32:
         raise ValueError("state_out must be [B,Nv,D,D] float32")
+    _dev(dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, out=out,
+              state_out=state_out), device)
+    return (T, B, Nqk, Nv, D), code, act, gk, out, state_out
+
+
+def chunk_prefill(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, state_out=None,
+                  workspace=None, rule="gated_delta", gk=None):
+    """Chunked Gated Delta Rule prefill ("Qwen3Next Samples" page).
+
+    q, k [T,Nqk,D]; v [T,Nv,D]; beta [T,Nv] (act dtype: bf16, fp16 or fp32);
+    g [T,Nv] fp32; cu_seqlens [B+1] int32; state_in [B,Nv,D,D] fp32 or None;
+    rule one of RULES (g may be None without a gate, beta without the delta
+    term); gk [T,Nv,D] fp32 or None: the per-key gate (ignored by the rules
+    without decay).
+    Returns (out [T,Nv,D] act dtype, state_out [B,Nv,D,D] fp32).  `out`,
+    `state_out` and `workspace` (uint8, >= chunk_prefill_workspace_size
+    bytes) may be passed in to avoid allocations.
+    """
+    (T, B, Nqk, Nv, D), code, act, gk, out, state_out = _prefill_checked(
+        q, k, v, g, beta, cu_seqlens, state_in, out, state_out, rule, gk)
+    device = q.device
     nbytes = chunk_prefill_workspace_size(T, B, Nqk, Nv, D, gk is not None)
     if workspace is None:
         workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
-    _dev(dict(q=q, k=k, v=v, g=g, gk=gk, beta=beta, cu_seqlens=cu_seqlens, state_in=state_in, out=out,
-              state_out=state_out, workspace=workspace), device)
+    _dev(dict(workspace=workspace), device)
     check(lib().gdr_chunk_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta), _ptr(state_in),
                                   _ptr(cu_seqlens), T, B, Nqk, Nv, D, float(scale), code, act, _ptr(out),
                                   _ptr(state_out), _ptr(workspace),
                                   workspace.numel() * workspace.element_size(), _stream(device)),
           "gdr_chunk_prefill")
+    return out, state_out
+
+
+def chunk_prefill_noalloc(q, k, v, g, beta, cu_seqlens, scale, state_in=None, out=None, state_out=None,
+                          rule="gated_delta", gk=None):
+    """gdr_chunk_prefill_noalloc: the prefill of chunk_prefill in the
+    library's per-GPU scratch array, with no workspace (for callers that
+    cannot allocate; sizes whose workspace exceeds the scratch raise
+    RuntimeError).  Pass `out` and `state_out` to allocate nothing here
+    either."""
+    (T, B, Nqk, Nv, D), code, act, gk, out, state_out = _prefill_checked(
+        q, k, v, g, beta, cu_seqlens, state_in, out, state_out, rule, gk)
+    check(lib().gdr_chunk_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(gk), _ptr(beta),
+                                          _ptr(state_in), _ptr(cu_seqlens), T, B, Nqk, Nv, D, float(scale),
+                                          code, act, _ptr(out), _ptr(state_out), _stream(q.device)),
+          "gdr_chunk_prefill_noalloc")
     return out, state_out
 
 

@@ -8,6 +8,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <mutex>
 
 namespace {
 
@@ -129,12 +130,47 @@ static bool rule_ok(gdr_update_rule r) {
 static bool rule_gated(gdr_update_rule r) { return r == GDR_RULE_GATED_DELTA || r == GDR_RULE_GATED; }
 static bool rule_delta(gdr_update_rule r) { return r == GDR_RULE_GATED_DELTA || r == GDR_RULE_DELTA; }
 
-gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
-                             const float* gk, const void* beta, const float* state_in,
-                             const int32_t* cu_seqlens,
-                             int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D, float scale,
-                             gdr_update_rule rule, gdr_dtype act, void* out, float* state_out,
-                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+// Device scratch of gdr_chunk_prefill_noalloc: one copy of this array per GPU,
+// resident from the library's load until the process ends.  Host code never
+// passes the array's name to a kernel (on the host it is a stand-in, not a
+// device address); it uses the address hipGetSymbolAddress returns for the
+// current device, looked up once per device and kept in g_scratch.
+static __device__ __align__(256) unsigned char scratch[GDR_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's address of `scratch`.
+gdr_status scratch_address(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return from_hip(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(GDR_ERR_HIP, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return from_hip(e, "hipGetSymbolAddress(scratch)");
+        if (!p) return fail(GDR_ERR_HIP, "hipGetSymbolAddress(scratch) returned NULL");
+        g_scratch[dev] = p;
+    }
+    *ptr = g_scratch[dev];
+    return ok();
+}
+
+// Validation and launch shared by both prefill entry points.  With
+// `use_scratch`, the workspace is this device's scratch array (the size
+// check against its capacity comes before any HIP call).
+gdr_status prefill_entry(const void* q, const void* k, const void* v, const float* g, const float* gk,
+                         const void* beta, const float* state_in, const int32_t* cu_seqlens, int64_t T,
+                         int32_t B, int32_t Nqk, int32_t Nv, int32_t D, float scale, gdr_update_rule rule,
+                         gdr_dtype act, void* out, float* state_out, void* workspace, size_t workspace_bytes,
+                         bool use_scratch, void* hip_stream) {
     gdr_status s = check_prefill_sizes(T, B, Nqk, Nv, D);
     if (s != GDR_OK) return s;
     if (act != GDR_BF16 && act != GDR_FP32 && act != GDR_FP16)
@@ -149,6 +185,16 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
     // the per-key gate applies only to the rules with decay
     const float* gk_used = rule_gated(rule) ? gk : nullptr;
     const gdr::PrefillLayout lay = gdr::prefill_layout(T, B, Nqk, Nv, gk_used != nullptr);
+    if (use_scratch) {
+        if (lay.total > (size_t)GDR_NOALLOC_SCRATCH_BYTES)
+            return fail(GDR_ERR_WORKSPACE,
+                        "these sizes need %zu bytes of workspace%s, more than the %zu-byte scratch of "
+                        "gdr_chunk_prefill_noalloc; use gdr_chunk_prefill with a caller workspace",
+                        lay.total, gk_used ? " (with a per-key gate)" : "", (size_t)GDR_NOALLOC_SCRATCH_BYTES);
+        s = scratch_address(&workspace);
+        if (s != GDR_OK) return s;
+        workspace_bytes = GDR_NOALLOC_SCRATCH_BYTES;
+    }
     if (!workspace || workspace_bytes < lay.total)
         return fail(GDR_ERR_WORKSPACE, "workspace of %zu bytes needed (got %zu, ptr %p)%s", lay.total,
                     workspace_bytes, workspace, gk_used ? " (with a per-key gate)" : "");
@@ -156,6 +202,29 @@ gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const 
                        static_cast<char*>(workspace), T, B, Nqk, Nv, scale, (int32_t)rule};
     return from_hip(gdr::prefill_launch(a, lay, (int)act, static_cast<hipStream_t>(hip_stream)),
                     "prefill launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+gdr_status gdr_chunk_prefill(const void* q, const void* k, const void* v, const float* g,
+                             const float* gk, const void* beta, const float* state_in,
+                             const int32_t* cu_seqlens,
+                             int64_t T, int32_t B, int32_t Nqk, int32_t Nv, int32_t D, float scale,
+                             gdr_update_rule rule, gdr_dtype act, void* out, float* state_out,
+                             void* workspace, size_t workspace_bytes, void* hip_stream) {
+    return prefill_entry(q, k, v, g, gk, beta, state_in, cu_seqlens, T, B, Nqk, Nv, D, scale, rule, act, out,
+                         state_out, workspace, workspace_bytes, false, hip_stream);
+}
+
+gdr_status gdr_chunk_prefill_noalloc(const void* q, const void* k, const void* v, const float* g,
+                                     const float* gk, const void* beta, const float* state_in,
+                                     const int32_t* cu_seqlens, int64_t T, int32_t B, int32_t Nqk, int32_t Nv,
+                                     int32_t D, float scale, gdr_update_rule rule, gdr_dtype act, void* out,
+                                     float* state_out, void* hip_stream) {
+    return prefill_entry(q, k, v, g, gk, beta, state_in, cu_seqlens, T, B, Nqk, Nv, D, scale, rule, act, out,
+                         state_out, nullptr, 0, true, hip_stream);
 }
 
 gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, const float* g,

@@ -161,6 +161,35 @@ gdr_status gdr_chunk_prefill(const void *q, const void *k, const void *v, const 
                              float *state_out, void *workspace, size_t workspace_bytes,
                              void *hip_stream);
 
+/*
+ * gdr_chunk_prefill_noalloc -- gdr_chunk_prefill without a caller workspace,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *
+ * The library keeps one scratch array of GDR_NOALLOC_SCRATCH_BYTES per GPU
+ * (a static device array, resident on every GPU the library runs on from
+ * its load until the process ends) and runs the prefill in it.  Sizes whose
+ * workspace (gdr_chunk_prefill_workspace_size) exceeds that return
+ * GDR_ERR_WORKSPACE before any HIP call.  The call allocates and frees no
+ * memory; the first call on a device looks up that device's address of the
+ * array (hipGetSymbolAddress) and keeps it.
+ *
+ * Every call on one GPU shares that GPU's array, which keeps the last call's
+ * contents (no part of it needs to start at zero: each call writes every
+ * region before reading it).  Calls ordered on one stream are safe; calls
+ * that may overlap in time on one GPU (different streams, or threads without
+ * ordering between them) race on the array and give wrong results.
+ *
+ * Arguments, results and errors are those of gdr_chunk_prefill, without
+ * workspace and workspace_bytes.
+ */
+#define GDR_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+gdr_status gdr_chunk_prefill_noalloc(const void *q, const void *k, const void *v, const float *g,
+                                     const float *gk, const void *beta, const float *state_in,
+                                     const int32_t *cu_seqlens, int64_t T, int32_t B, int32_t Nqk,
+                                     int32_t Nv, int32_t D, float scale, gdr_update_rule rule,
+                                     gdr_dtype act, void *out, float *state_out, void *hip_stream);
+
 /* ------------------------------------------------------------------ decode
  *
  * gdr_recurrent_decode -- token-by-token Gated Delta Rule over a state pool

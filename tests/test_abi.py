@@ -184,3 +184,34 @@ def test_binding_shape_checks_precede_device_work():
         gd = torch.zeros(2, 1, 3)
         gdr.recurrent_decode(qd, qd, vd, gd, None, gd.bfloat16(), torch.zeros(4, 1, 64, 64),
                              torch.zeros(5, dtype=torch.int32), torch.ones(2, dtype=torch.int32))
+
+
+def noalloc_call(**over):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, gk=None, beta=FAKE, state_in=None, cu=FAKE, T=8192, B=4, Nqk=16,
+             Nv=32, D=128, scale=0.1, rule=0, act=gdr.GDR_BF16, out=FAKE, state_out=FAKE, stream=None)
+    a.update(over)
+    return gdr.lib().gdr_chunk_prefill_noalloc(a["q"], a["k"], a["v"], a["g"], a["gk"], a["beta"],
+                                               a["state_in"], a["cu"], a["T"], a["B"], a["Nqk"], a["Nv"],
+                                               a["D"], a["scale"], a["rule"], a["act"], a["out"],
+                                               a["state_out"], a["stream"])
+
+
+def test_noalloc_prefill_rejects_sizes_beyond_its_scratch():
+    """The allocation-free prefill checks every argument as gdr_chunk_prefill
+    does, then the workspace these sizes need against its fixed scratch, all
+    before any HIP call (none of these calls reaches a launch)."""
+    E = gdr
+    scratch = 128 << 20
+    assert ws_size(8192, 4, 16, 32, 128)[1] > scratch
+    assert noalloc_call() == E.GDR_ERR_WORKSPACE
+    msg = gdr.lib().gdr_last_error()
+    assert b"scratch" in msg and str(scratch).encode() in msg
+    assert noalloc_call(Nqk=3) == E.GDR_ERR_INVALID_ARGUMENT
+    assert noalloc_call(q=None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert noalloc_call(act=7) == E.GDR_ERR_DTYPE
+    assert noalloc_call(D=64) == E.GDR_ERR_UNSUPPORTED
+    # a workload that fits without a per-key gate can exceed it with one
+    T = 3000
+    assert ws_size(T, 1, 16, 32, 128)[1] <= scratch < ws_size(T, 1, 16, 32, 128, 1)[1]
+    assert noalloc_call(T=T, B=1, gk=FAKE) == E.GDR_ERR_WORKSPACE
+    assert b"per-key gate" in gdr.lib().gdr_last_error()
