@@ -195,10 +195,187 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
     }
 }
 
+// One token per row (S = 1, the ordinary decode step) with a 16-bit pool:
+// the slab stays in its packed 16-bit form in registers (half the registers
+// of the fp32 copy the multi-token chain needs), so more workgroups fit on a
+// CU and more of the stream is in flight.  Every value is widened exactly
+// when used: the decay and the reductions read the packed rows once, the
+// update reads them again and writes the new state.  The arithmetic per
+// element is the same as in decode_kernel.
+__device__ __forceinline__ void unpack8(const u32x4& r, uint16_t, float (&x)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        x[2 * i] = __uint_as_float(r[i] << 16);
+        x[2 * i + 1] = __uint_as_float(r[i] & 0xffff0000u);
+    }
+}
+__device__ __forceinline__ void unpack8(const u32x4& r, _Float16, float (&x)[8]) {
+    const half8 h = __builtin_bit_cast(half8, r);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)h[i];
+}
+
+// (the register bound asks for four waves per SIMD where a lane holds at
+// most 8 packed rows, which fits without spilling)
+template <int DK, int CW, typename ActT, typename StT, bool ANY_RULE>
+__global__ __launch_bounds__(256, DK * CW <= 128 * 128 ? 4 : 2) void decode1_kernel(DecodeArgs a) {
+    constexpr int NT = 256;
+    constexpr int WAVES = NT / 64;
+    constexpr int LPR = CW / 8;
+    constexpr int RP = NT / LPR;
+    constexpr int RPT = DK / RP;
+    static_assert(CW % 8 == 0 && LPR <= 64 && DK % RP == 0 && RPT >= 1, "bad decode tiling");
+    static_assert(sizeof(StT) == 2, "packed slabs are 16-bit");
+    constexpr int NRED = 17;
+
+    __shared__ float s_k[DK];
+    __shared__ float s_q[DK];
+    __shared__ float s_a[DK];
+    __shared__ float s_red[NRED][WAVES][LPR];
+
+    const int Nv = a.Nv, Dv = a.Dv;
+    const int nslice = Dv / CW;
+    const int wg = blockIdx.x;
+    const int slice = wg % nslice;
+    const int bh = wg / nslice;
+    const int h = bh % Nv;
+    const int b = bh / Nv;
+    const int hk = h / (Nv / a.Nk);
+    const int tid = threadIdx.x;
+    const int cg = tid % LPR;
+    const int rg = tid / LPR;
+    const int wave = tid / 64, lane = tid % 64;
+    const int col = slice * CW + cg * 8;
+
+    const ActT* q = static_cast<const ActT*>(a.q);
+    const ActT* k = static_cast<const ActT*>(a.k);
+    const ActT* v = static_cast<const ActT*>(a.v);
+    const ActT* beta = static_cast<const ActT*>(a.beta);
+    ActT* out = static_cast<ActT*>(a.out);
+    StT* pool = static_cast<StT*>(a.pool);
+
+    int len = a.lens[b];
+    len = len < 0 ? 0 : (len > 1 ? 1 : len);
+    const size_t tok0 = (size_t)b * Nv + h;   // [B,Nv,1]
+    const size_t slab = (size_t)DK * Dv;
+    const size_t slot_stride = (size_t)Nv * slab;
+    const int slot = len > 0 ? a.idx[b] : -1;   // the read slot is the written slot
+    const bool in_pool = slot >= 0 && slot < a.num_slots;
+
+    u32x4 raw[RPT];
+    if (in_pool) {
+        const StT* base = pool + (size_t)slot * slot_stride + (size_t)h * slab + col;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m)
+            raw[m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(base + (size_t)(rg + RP * m) * Dv));
+    } else {
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) raw[m] = u32x4{0u, 0u, 0u, 0u};
+    }
+    if (len == 0) {
+        if (rg == 0) {
+            float z[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            store8(out + tok0 * Dv + col, z);
+        }
+        return;
+    }
+
+    const bool gated = !ANY_RULE || a.rule == 0 || a.rule == 2;
+    const bool delta = !ANY_RULE || a.rule == 0 || a.rule == 1;
+    const float kvw = delta ? 1.f : 0.f;
+    if (tid < DK) {
+        const size_t qi = ((size_t)b * a.Nk + hk) * DK + tid;
+        s_k[tid] = load1(k + qi);
+        s_q[tid] = load1(q + qi) * a.scale;
+        const float eg = gated ? expf(a.g[tok0]) : 1.f;
+        s_a[tid] = (gated && a.gk) ? eg * expf(a.gk[tok0 * DK + tid]) : eg;
+    }
+    float vv[8];
+    load8(v + tok0 * Dv + col, vv);
+    const float bt = delta ? load1(beta + tok0) : 1.f;
+    __syncthreads();
+
+    float pk[8], pq[8], pkq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { pk[c] = 0.f; pq[c] = 0.f; }
+#pragma unroll
+    for (int m = 0; m < RPT; ++m) {
+        const int i = rg + RP * m;
+        const float ai = s_a[i], ki = s_k[i], qi = s_q[i];
+        float x[8];
+        unpack8(raw[m], StT(), x);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            const float sd = x[c] * ai;
+            pk[c] = fmaf(sd, ki, pk[c]);
+            pq[c] = fmaf(sd, qi, pq[c]);
+        }
+        pkq = fmaf(ki, qi, pkq);
+    }
+#pragma unroll
+    for (int off = LPR; off < 64; off <<= 1) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            pk[c] += __shfl_xor(pk[c], off);
+            pq[c] += __shfl_xor(pq[c], off);
+        }
+        pkq += __shfl_xor(pkq, off);
+    }
+    if (lane < LPR) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            s_red[c][wave][lane] = pk[c];
+            s_red[8 + c][wave][lane] = pq[c];
+        }
+        s_red[16][wave][lane] = pkq;
+    }
+    __syncthreads();
+    float kv[8], qs[8], kq = 0.f;
+#pragma unroll
+    for (int c = 0; c < 8; ++c) { kv[c] = 0.f; qs[c] = 0.f; }
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) {
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            kv[c] += s_red[c][w][cg];
+            qs[c] += s_red[8 + c][w][cg];
+        }
+        kq += s_red[16][w][cg];
+    }
+    float d[8], o[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        d[c] = bt * (vv[c] - kvw * kv[c]);
+        o[c] = fmaf(d[c], kq, qs[c]);
+    }
+    if (rg == 0) store8(out + tok0 * Dv + col, o);
+    if (in_pool) {
+        StT* base = pool + (size_t)slot * slot_stride + (size_t)h * slab + col;
+#pragma unroll
+        for (int m = 0; m < RPT; ++m) {
+            const int i = rg + RP * m;
+            const float ai = s_a[i], ki = s_k[i];
+            float x[8];
+            unpack8(raw[m], StT(), x);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) x[c] = fmaf(ki, d[c], x[c] * ai);
+            store8_nt(base + (size_t)(rg + RP * m) * Dv, x);
+        }
+    }
+}
+
 template <int DK, int CW, typename ActT, typename StT>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const size_t nwg = (size_t)a.B * a.Nv * (a.Dv / CW);
     timing_begin(kDecode, stream);
+    if constexpr (sizeof(StT) == 2) {
+        if (a.S == 1) {
+            if (a.rule == 0) hipLaunchKernelGGL((decode1_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+            else hipLaunchKernelGGL((decode1_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+            timing_end(kDecode, stream);
+            return hipGetLastError();
+        }
+    }
     if (a.rule == 0) hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
     else hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
     timing_end(kDecode, stream);

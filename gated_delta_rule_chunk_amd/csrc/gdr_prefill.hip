@@ -718,13 +718,28 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     // once it has used its own (after the last item they re-read the current
     // one, unused); with fp32 inputs each item loads its own at its start.
     IntraStage<ActT> st;
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
-    while (true) {
-        if constexpr (sizeof(ActT) == 4) intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
-        const int nx = it + stride;
+    if constexpr (sizeof(ActT) == 2) {
+        // The first item is peeled off the loop, so that every entry into the
+        // loop follows a whole item: the memory operations in flight at the
+        // loop head are then the same on every path, and the compiler's
+        // waits for the prefetched inputs stop at those loads instead of
+        // also waiting for the previous item's stores.
+        intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
+        int nx = it + stride;
         intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
-        if (nx >= n_items) break;
-        it = nx;
+        while (nx < n_items) {
+            it = nx;
+            nx = it + stride;
+            intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
+        }
+    } else {
+        while (true) {
+            intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
+            const int nx = it + stride;
+            intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
+            if (nx >= n_items) break;
+            it = nx;
+        }
     }
 }
 

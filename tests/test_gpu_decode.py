@@ -186,3 +186,38 @@ def test_decode_fp16_activations_and_state(act, state):
     inp = workloads.decode_inputs(95, B=10, S=3, Nk=2, Nv=4, Dk=128, Dv=128, num_slots=25, with_gk=True,
                                   lens="random", routing="two_slots", act=act, state=state)
     check_parity(inp, f"act {act} state {state}")
+
+
+# One token per row (S = 1, the ordinary decode step) runs a kernel of its own
+# that keeps each slab packed in its 16-bit form; its variants:
+@pytest.mark.parametrize("rule,state,Dk,Dv", [("gated_delta", "fp16", 128, 128), ("delta", "bf16", 128, 128),
+                                              ("gated", "bf16", 64, 512), ("linear", "bf16", 64, 64),
+                                              ("gated_delta", "bf16", 128, 256)])
+def test_decode_one_token_per_row(rule, state, Dk, Dv):
+    inp = workloads.decode_inputs(100 + Dk + Dv, B=9, S=1, Nk=2, Nv=4, Dk=Dk, Dv=Dv, num_slots=20,
+                                  with_gk=True, state=state)
+    # rows 2 and 7 have no token: not read, not written, out rows zero
+    lens = inp["lens"].clone()
+    idx = inp["idx"].clone()
+    lens[2] = 0
+    lens[7] = 0
+    idx[2] = -1
+    idx[7] = -1
+    inp.update(lens=lens, idx=idx)
+    check_parity(inp, f"S=1 rule {rule} {state} pool Dk={Dk} Dv={Dv}", rule=rule)
+
+
+def test_decode_one_token_out_of_range_slot():
+    """S = 1: a row whose slot lies outside the pool starts from zeros and
+    stores nothing."""
+    inp = workloads.decode_inputs(120, B=3, S=1, Nk=1, Nv=2, Dk=128, Dv=128, num_slots=4)
+    inp.update(idx=torch.tensor([7, 1, -2], dtype=torch.int32))
+    out, pool = run_gpu(inp)
+    assert torch.equal(pool[[0, 2, 3]].view(torch.int16), inp["pool"][[0, 2, 3]].view(torch.int16))
+    ref_pool = inp["pool"].clone()
+    ref_pool[0] = 0
+    ref_pool[2] = 0
+    ref = dict(inp, pool=ref_pool, idx=torch.tensor([0, 1, 2], dtype=torch.int32))
+    out_ref, pool_ref = run_oracle(ref)
+    assert_out_close(out, out_ref, True, "S=1 oob out")
+    assert_state_close(to_f64(pool[1]), pool_ref[1], "S=1 oob state slot 1")
