@@ -88,6 +88,15 @@ def flops_prefill(seq_lens, Nqk, Nv):
     return f
 
 
+def flops_tile(seq_lens, Nv):
+    """F_tile: the flops of the dense 128-token tiles the kernels work on --
+    8 dense 128^3 contractions (Gram, u, w, P, v', (q^ e^g) S, P v_new, the
+    state update) plus the triangular solve (L^3 / 3) per value head and
+    chunk, ragged chunks counted as full."""
+    nchunks = sum((n + L - 1) // L for n in seq_lens)
+    return nchunks * Nv * (8 * 2 * L * D * D + L ** 3 / 3)
+
+
 def bytes_prefill(T, B, Nqk, Nv, act_bytes=2):
     """Algorithmic HBM bytes of a prefill call: q, k, v, beta, out in the
     activation dtype, g fp32, state in and out fp32."""
@@ -116,16 +125,32 @@ def source_hash(path):
     return hashlib.sha256(open(os.path.join(ROOT, path), "rb").read()).hexdigest()[:16]
 
 
-def counter_traffic(kernel):
-    """HBM bytes per launch from the committed counter runs, or None if the
-    kernel's source changed since they were taken."""
+def counter_record(kernel):
+    """The kernel's record in the committed counter runs
+    (profiles/counters.json), or None if its source changed since they
+    were taken."""
     p = os.path.join(ROOT, "profiles", "counters.json")
     if not os.path.exists(p):
         return None
     rec = json.load(open(p)).get(kernel)
     if not rec or rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return rec
+
+
+def counter_traffic(kernel):
+    """HBM bytes per launch from the committed counter runs, or None."""
+    rec = counter_record(kernel)
+    return rec.get("hbm_bytes_per_launch") if rec else None
+
+
+def counter_mfma(kernel):
+    """Executed MFMA flops per launch and the fraction of cycles the matrix
+    cores were busy, from the committed counter runs, or (None, None)."""
+    rec = counter_record(kernel)
+    if not rec:
+        return None, None
+    return rec.get("mfma_flops_per_launch"), rec.get("mfma_busy_frac")
 
 
 def timed(fn, steps, warmup, gdr, torch):
@@ -193,22 +218,35 @@ def bench_prefill(args, gdr, torch, workloads):
     seq_lens = [1000, 4096, 300, 2796]
     fl = flops_prefill(seq_lens, Nqk, Nv)
     kernels = {}
+    mfma_exec_total = 0.0
     for name in fl:
         ms, n = per.get(name, (0.0, 0))
         per_call = ms / 1e3
         kernels[name] = {"us_per_call": per_call * 1e6, "launches_per_call": n, "alg_gflop": fl[name] / 1e9,
                          "mfma_frac": (fl[name] / per_call / MFMA_PEAK_FP16) if per_call > 0 and fl[name] else None}
+        fx, busy = counter_mfma(name)
+        if fx is not None and n:
+            kernels[name]["mfma_executed_gflop"] = fx * n / 1e9
+            kernels[name]["mfma_busy_frac_counter"] = busy
+            mfma_exec_total += fx * n
     # the dominant kernel's time per call over the timed region itself (one
     # launch per call: its average launch duration)
     dom_avg = live[0] / 1e3
     kernels[dominant]["us_per_call_timed_region"] = dom_avg * 1e6
     step_s = dt / args.steps
     f_total = sum(fl.values())
+    f_tile = flops_tile(seq_lens, Nv)
     b_total = bytes_prefill(T, B, Nqk, Nv)
+    path = {"alg_gflop": f_total / 1e9, "mfma_frac": f_total / step_s / MFMA_PEAK_FP16,
+            "tile_gflop": f_tile / 1e9, "mfma_frac_tile": f_tile / step_s / MFMA_PEAK_FP16,
+            "alg_bytes_mb": b_total / 1e6, "hbm_frac": b_total / step_s / HBM_PEAK,
+            # the larger of the two floors (MFMA at peak, HBM at peak) over the time taken
+            "attainable_frac": max(f_total / MFMA_PEAK_FP16, b_total / HBM_PEAK) / step_s}
+    if mfma_exec_total:
+        path["mfma_executed_gflop"] = mfma_exec_total / 1e9
+        path["mfma_frac_executed"] = mfma_exec_total / step_s / MFMA_PEAK_FP16
     return dict(inp=inp, step_s=step_s, tok_s=T / step_s, kernels=kernels,
-                roofline=roofline(dominant, dom_avg, flops=fl[dominant]),
-                path={"alg_gflop": f_total / 1e9, "mfma_frac": f_total / step_s / MFMA_PEAK_FP16,
-                      "alg_bytes_mb": b_total / 1e6, "hbm_frac": b_total / step_s / HBM_PEAK})
+                roofline=roofline(dominant, dom_avg, flops=fl[dominant]), path=path)
 
 
 def bench_decode(args, gdr, torch, workloads):
@@ -271,31 +309,146 @@ def time_config(n, args, gdr, torch, workloads):
     steps = 20 if ntok < 65536 else 5
     dt, per, _, _ = timed(f, steps, 2, gdr, torch)
     name = workloads.CONFIG_NAMES[n] if isinstance(n, int) else workloads.EXTRA_NAMES[n]
-    return {"config": name, "ms_per_call": dt / steps * 1e3, "tok_s": ntok / (dt / steps),
-            "kernels_us_per_call": {k: round(v[0] * 1e3, 1) for k, v in per.items()}}
+    t = dt / steps
+    rec = {"config": name, "ms_per_call": t * 1e3, "tok_s": ntok / t,
+           "kernels_us_per_call": {k: round(v[0] * 1e3, 1) for k, v in per.items()}}
+    if "cu_seqlens" in inp:
+        lens = [int(x) for x in (inp["cu_seqlens"][1:] - inp["cu_seqlens"][:-1]).tolist()]
+        fa = sum(flops_prefill(lens, inp["Nqk"], inp["Nv"]).values())
+        ab = 4 if inp["act"] == "fp32" else 2
+        nb = bytes_prefill(inp["T"], inp["B"], inp["Nqk"], inp["Nv"], ab)
+        if inp.get("gk") is not None:
+            nb += inp["T"] * inp["Nv"] * D * 4
+        rec.update(alg_gflop=fa / 1e9, mfma_frac=fa / t / MFMA_PEAK_FP16, alg_bytes_mb=nb / 1e6,
+                   hbm_frac=nb / t / HBM_PEAK,
+                   attainable_frac=max(fa / MFMA_PEAK_FP16, nb / HBM_PEAK) / t)
+    else:
+        nb = bytes_decode(inp)
+        rec.update(alg_bytes_mb=nb / 1e6, hbm_frac=nb / t / HBM_PEAK,
+                   kernel_hbm_frac=nb / (per["gdr_decode"][0] / 1e3) / HBM_PEAK)
+    return rec
 
 
 def cpu_baseline_prefill(inp):
+    """The oracle on the whole workload; inputs are widened to fp64 before
+    the clock starts, so only the oracle call is timed."""
     import oracle
+    w = {n: oracle._f64(inp[n]) for n in ("q", "k", "v", "g", "beta", "state_in")}
     t0 = time.perf_counter()
-    oracle.prefill(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], inp["state_in"], inp["cu_seqlens"],
-                   inp["scale"])
+    oracle.prefill(w["q"], w["k"], w["v"], w["g"], w["beta"], w["state_in"], inp["cu_seqlens"], inp["scale"])
     dt = time.perf_counter() - t0
     return {"value": inp["T"] / dt, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"one fp64 oracle call on the whole workload (T={inp['T']}, all {inp['Nv']} value "
-                      f"heads): {dt:.2f} s wall"}
+                      f"heads; inputs widened to fp64 before timing): {dt:.2f} s wall"}
 
 
 def cpu_baseline_decode(inp):
+    """The oracle on the whole workload; inputs (the pool included) are
+    widened to fp64 before the clock starts and the pool is updated in
+    place, so only the recurrence is timed."""
     import oracle
+    w = {n: oracle._f64(inp[n]) for n in ("q", "k", "v", "g", "beta", "pool")}
     t0 = time.perf_counter()
-    oracle.decode(inp["q"], inp["k"], inp["v"], inp["g"], inp["gk"], inp["beta"], inp["pool"], inp["idx"],
-                  inp["lens"], inp["scale"], round_state_bf16=True)
+    oracle.decode(w["q"], w["k"], w["v"], w["g"], inp["gk"], w["beta"], w["pool"], inp["idx"], inp["lens"],
+                  inp["scale"], round_state_bf16=True, in_place=True)
     dt = time.perf_counter() - t0
     ntok = int(inp["lens"].sum())
     return {"value": ntok / dt, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"one fp64 oracle call on the whole workload ({ntok} tokens x {inp['Nv']} heads): "
-                      f"{dt:.2f} s wall"}
+            "sample": f"one fp64 oracle call on the whole workload ({ntok} tokens x {inp['Nv']} heads; inputs "
+                      f"widened to fp64 before timing, pool updated in place): {dt:.3f} s wall"}
+
+
+# Kernel functions of each timing id (the per-key-gate and two-level variants
+# included), for matching rocprofv3 kernel names.
+def stream_ceiling(torch):
+    """HBM rates of plain streams on this GPU, with torch's elementwise
+    kernels: in-place x.mul_(1) (every byte read, then written back to the
+    same address: the access pattern of an in-place state update) and an
+    out-of-place copy, over four rotating 512 MiB bf16 buffers (2 GiB, so the
+    256 MB last-level cache holds none of them between launches).  Bytes
+    counted: read + written."""
+    n = 256 << 20   # bf16 elements: 512 MiB
+    bufs = [torch.ones(n, dtype=torch.bfloat16, device="cuda:0") for _ in range(4)]
+    dst = [torch.empty_like(b) for b in bufs]
+    res = {}
+    for name, fn in (("in_place_update", lambda i: bufs[i % 4].mul_(1.0)),
+                     ("out_of_place_copy", lambda i: dst[i % 4].copy_(bufs[(i + 1) % 4]))):
+        for i in range(4):
+            fn(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(20):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) / 1e3 / 20
+        res[name] = {"GBps": 2 * n * 2 / s / 1e9, "hbm_frac": 2 * n * 2 / s / HBM_PEAK, "us_per_launch": s * 1e6}
+    return {"stream_ceiling": res, "bytes_per_launch": 2 * n * 2}
+
+
+KERNEL_FUNCTIONS = {"chunkmap_kernel": "gdr_chunkmap", "intra_kernel": "gdr_intra", "intra_gk_kernel": "gdr_intra",
+                    "scan_kernel": "gdr_scan", "scan_gk_out_kernel": "gdr_scan", "combine_kernel": "gdr_scan",
+                    "output_kernel": "gdr_output", "output_gk_kernel": "gdr_output",
+                    "decode_kernel": "gdr_decode"}
+
+
+def _kernel_id(name):
+    import re
+    m = re.search(r"::(\w+)(?:<|\()", name.replace("(anonymous namespace)", "anon"))
+    if m and m.group(1) in KERNEL_FUNCTIONS:
+        return KERNEL_FUNCTIONS[m.group(1)]
+    return "copy" if "copyBuffer" in name else None
+
+
+def _csv_means(path):
+    """{kernel id: {counter: mean value per dispatch}} from a rocprofv3
+    counter_collection.csv."""
+    import csv
+    import collections
+    acc = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        kid = _kernel_id(r["Kernel_Name"])
+        if kid:
+            acc[kid][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    return {k: {c: sum(v) / len(v) for c, v in d.items()} for k, d in acc.items()}
+
+
+def ingest_counters(fetch_csv, write_csv, cal_fetch_csv, cal_write_csv, mfma_csv):
+    """Write profiles/counters.json from rocprofv3 --pmc runs: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) of bench.py, the same counters of
+    `bench.py --copy-calibration` (a plain 1 GiB copy, 3 launches: the
+    scale factors), and SQ_INSTS_VALU_MFMA_MOPS_F16 / _F32,
+    SQ_VALU_MFMA_BUSY_CYCLES, GRBM_GUI_ACTIVE of bench.py."""
+    fetch, write = _csv_means(fetch_csv), _csv_means(write_csv)
+    n = 1 << 30
+    # the copy's launches are the copyBuffer dispatches with the largest counts
+    import csv
+    cf = max(float(r["Counter_Value"]) for r in csv.DictReader(open(cal_fetch_csv)) if "copyBuffer" in r["Kernel_Name"])
+    cw = max(float(r["Counter_Value"]) for r in csv.DictReader(open(cal_write_csv)) if "copyBuffer" in r["Kernel_Name"])
+    ff, fw = n / (cf * 1024), n / (cw * 1024)
+    mf = _csv_means(mfma_csv) if mfma_csv else {}
+    out = {"_calibration": {"copy_bytes": n, "fetch_counter_KiB": cf, "write_counter_KiB": cw,
+                            "fetch_factor": ff, "write_factor": fw},
+           "_mfma_busy_note": "busy fraction = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / 8 XCDs x 1024 SIMDs)"}
+    for kid in sorted(set(KERNEL_FUNCTIONS.values())):
+        if kid not in fetch or kid not in write:
+            continue
+        rb = fetch[kid]["FETCH_SIZE"] * 1024 * ff
+        wb = write[kid]["WRITE_SIZE"] * 1024 * fw
+        rec = {"source_sha256_16": source_hash(KERNEL_SOURCES[kid]), "source": KERNEL_SOURCES[kid],
+               "fetch_KiB": fetch[kid]["FETCH_SIZE"], "write_KiB": write[kid]["WRITE_SIZE"],
+               "read_bytes": rb, "write_bytes": wb, "hbm_bytes_per_launch": rb + wb}
+        m = mf.get(kid)
+        if m and "SQ_INSTS_VALU_MFMA_MOPS_F16" in m:
+            mops = m["SQ_INSTS_VALU_MFMA_MOPS_F16"] + m.get("SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0)
+            rec["mfma_flops_per_launch"] = mops * 512
+            if m.get("GRBM_GUI_ACTIVE"):
+                rec["mfma_busy_frac"] = m["SQ_VALU_MFMA_BUSY_CYCLES"] / (m["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        out[kid] = rec
+    path = os.path.join(ROOT, "profiles", "counters.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def main():
@@ -307,12 +460,21 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only", choices=["all", "prefill", "decode"], default="all",
                     help="time one path only (for counter runs)")
-    ap.add_argument("--all-configs", action="store_true",
-                    help="also time every configured workload (one line per workload, after the main line)")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="leave out the per-workload records (the \"configs\" key of the line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 launches), the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--stream-ceiling", action="store_true",
+                    help="measure plain HBM streams the decode is compared with: an in-place update (read then "
+                         "write the same bytes, like the decode's slab update) and an out-of-place copy, each over "
+                         "four rotating 512 MiB bf16 buffers; prints one JSON line")
+    ap.add_argument("--ingest-counters", nargs=5, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE", "MFMA"),
+                    help="write profiles/counters.json from rocprofv3 counter_collection.csv files and exit")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(*args.ingest_counters)
+        return
     if args.gpus != 1:
         print(f"bench.py: this operator is measured on one GPU only (got --gpus {args.gpus}); "
               "run with --gpus 1", file=sys.stderr)
@@ -322,6 +484,9 @@ def main():
     import gated_delta_rule_chunk_amd as gdr
     import workloads
 
+    if args.stream_ceiling:
+        print(json.dumps(stream_ceiling(torch)))
+        return
     if args.copy_calibration:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
@@ -363,15 +528,18 @@ def main():
                    "alg_bytes_mb": dec["alg_bytes_mb"], "roofline": dec["roofline"],
                    "device_copy_reference_GBps": dec["copy_gbs"]},
     }
+    if not args.no_configs:
+        # the other configured workloads (the T=8192 prefill and the B=256
+        # decode are the entries above) and the extra ones, each timed on its
+        # own with one input set resident
+        line["configs"] = {str(n): time_config(n, args, gdr, torch, workloads)
+                           for n in (1, 4, 5, *workloads.EXTRA_NAMES)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(inp)
         line["decode"]["cpu_baseline"] = cpu_baseline_decode(dec["inp"])
     else:
         line["cpu_baseline"] = None
     print(json.dumps(line))
-    if args.all_configs:
-        for n in (1, 2, 3, 4, 5, *workloads.EXTRA_NAMES):
-            print(json.dumps(time_config(n, args, gdr, torch, workloads)), flush=True)
 
 
 if __name__ == "__main__":

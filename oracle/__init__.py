@@ -158,14 +158,17 @@ def prefill(q, k, v, g, beta, state_in, cu_seqlens, scale, rule="gated_delta", g
 
 
 def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False, num_accepted=None,
-           rule="gated_delta", round_state=None):
+           rule="gated_delta", round_state=None, in_place=False):
     """Recurrent decode over a slot pool.
 
     q, k [B,Nk,S,Dk] (caller-normalised); v [B,Nv,S,Dv]; g, beta [B,Nv,S];
     gk [B,Nv,S,Dk] or None; pool [slots,Nv,Dk,Dv]; idx [B*S]; lens [B];
     num_accepted [B] or None (row b starts from slot idx[b*S + n_b - 1]).
     Returns (out [B,Nv,S,Dv], pool_out [slots,Nv,Dk,Dv]) in float64; pool_out
-    equals the input pool except for the slots the call writes.
+    equals the input pool except for the slots the call writes.  With
+    `in_place` (for timing; rows must not share slots) the written states go
+    into the float64 widening of `pool` itself, which is returned, instead of
+    into a copy; a float64 numpy `pool` is then updated in place.
     """
     q, k, v, g, beta, pool = map(_f64, (q, k, v, g, beta, pool))
     gk = _f64(gk)
@@ -178,7 +181,7 @@ def decode(q, k, v, g, gk, beta, pool, idx, lens, scale, round_state_bf16=False,
     nacc = None if num_accepted is None else _i32(num_accepted).reshape(-1)
     assert nacc is None or nacc.shape[0] == B
     out = np.zeros((B, Nv, S, Dv), np.float64)
-    pool_out = pool.copy()
+    pool_out = pool if in_place else pool.copy()
     rc = _load().gdr_oracle_decode(_dp(q), _dp(k), _dp(v), _dp(g), _dp(gk), _dp(beta),
                                    _dp(pool), _dp(pool_out), slots, _ip(idx), _ip(lens), _ip(nacc),
                                    B, S, Nk, Nv, Dk, Dv, float(scale),
