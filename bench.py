@@ -251,6 +251,9 @@ def bench_prefill(args, gdr, torch, workloads):
 
 def bench_decode(args, gdr, torch, workloads):
     inp = workloads.config_inputs(3)
+    if args.decode_contiguous_slots:
+        # reference run: the same rows in slots 0 .. B-1 in row order
+        inp["idx"] = torch.arange(inp["idx"].numel(), dtype=torch.int32)
     dev = "cuda:0"
     base = {k: (v.to(dev) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
     names = ("q", "k", "v", "g", "beta", "pool")
@@ -390,7 +393,7 @@ def stream_ceiling(torch):
 KERNEL_FUNCTIONS = {"chunkmap_kernel": "gdr_chunkmap", "intra_kernel": "gdr_intra", "intra_gk_kernel": "gdr_intra",
                     "scan_kernel": "gdr_scan", "scan_gk_out_kernel": "gdr_scan", "combine_kernel": "gdr_scan",
                     "output_kernel": "gdr_output", "output_gk_kernel": "gdr_output",
-                    "decode_kernel": "gdr_decode"}
+                    "decode_kernel": "gdr_decode", "decode1_kernel": "gdr_decode"}
 
 
 def _kernel_id(name):
@@ -465,6 +468,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device copy (3 launches), the reference for scaling "
                          "rocprofv3 FETCH_SIZE / WRITE_SIZE counters to bytes")
+    ap.add_argument("--decode-contiguous-slots", action="store_true",
+                    help="reference run: time the decode with its rows in slots 0 .. B-1 in row order instead of "
+                         "the workload's seeded random slots (the pool's access order only; same arithmetic)")
     ap.add_argument("--stream-ceiling", action="store_true",
                     help="measure plain HBM streams the decode is compared with: an in-place update (read then "
                          "write the same bytes, like the decode's slab update) and an out-of-place copy, each over "
@@ -499,7 +505,11 @@ def main():
     gdr.lib()
     if args.only != "all":
         res = (bench_prefill if args.only == "prefill" else bench_decode)(args, gdr, torch, workloads)
-        print(json.dumps({"only": args.only, "ms_per_step": res["step_s"] * 1e3, "tok_s": res["tok_s"]}))
+        line = {"only": args.only, "ms_per_step": res["step_s"] * 1e3, "tok_s": res["tok_s"]}
+        if args.only == "decode":
+            line.update(kernel_avg_us=res["kernel_avg_us"], roofline=res["roofline"],
+                        contiguous_slots=bool(args.decode_contiguous_slots))
+        print(json.dumps(line))
         return
     pre = bench_prefill(args, gdr, torch, workloads)
     dec = bench_decode(args, gdr, torch, workloads)
