@@ -83,6 +83,7 @@ struct PrefillDev {
     const float* state_in;
     void* out;
     float* state_out;
+    const int32_t* cu;   // cu_seqlens [B+1]
     int32_t* meta;
     int32_t* cmap;
     _Float16* khatT;
@@ -99,6 +100,7 @@ struct PrefillDev {
     int64_t nc;
     int32_t B, Nqk, Nv;
     int32_t nseg, seg_len;
+    int32_t map_in_intra;   // the intra kernel builds the chunk map itself (no chunkmap_kernel launch)
     float scale;
 };
 
@@ -186,6 +188,73 @@ __global__ __launch_bounds__(256) void chunkmap_kernel(const int32_t* cu, Prefil
         p.cmap[4 * c + 2] = (int32_t)max<int64_t>(r, 0);
         p.cmap[4 * c + 3] = c - p.meta[lo];
     }
+}
+
+// The same chunk map, built by every workgroup of the intra kernel into LDS
+// when there are at most kMapSeqs sequences, which saves the chunkmap launch:
+// per sequence b its first chunk, clamped first token and clamped length
+// (sm[b], sm[kMapSeqs + 1 + b], sm[2 kMapSeqs + 1 + b]; sm[B] the chunk
+// total; three more words for the scan's partial sums).  Workgroup 0 also
+// writes meta, and the workgroups share out the cmap entries, for the
+// kernels that follow.
+constexpr int kMapSeqs = 168;
+constexpr int kMapInts = 3 * kMapSeqs + 4;
+
+__device__ void build_chunk_map(const PrefillDev& p, int32_t* sm, int tid) {
+    int32_t* tmp = sm + 3 * kMapSeqs + 1;
+    const int B = p.B;   // <= kMapSeqs
+    const int64_t T = p.T;
+    int32_t nb = 0;
+    if (tid < B) {
+        const int64_t s0 = min<int64_t>(max<int64_t>(p.cu[tid], 0), T);
+        const int64_t e0 = min<int64_t>(max<int64_t>(p.cu[tid + 1], s0), T);
+        nb = (int32_t)((e0 - s0 + kChunk - 1) / kChunk);
+        sm[kMapSeqs + 1 + tid] = (int32_t)s0;
+        sm[2 * kMapSeqs + 1 + tid] = (int32_t)(e0 - s0);
+    }
+    const int wave = tid >> 6, lane = tid & 63;
+    int32_t incl = nb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int32_t y = __shfl_up(incl, off);
+        if (lane >= off) incl += y;
+    }
+    if (lane == 63 && wave < 3) tmp[wave] = incl;
+    __syncthreads();
+    int32_t base = 0;
+    for (int w = 0; w < wave && w < 3; ++w) base += tmp[w];
+    const int32_t nc = (int32_t)p.nc;
+    if (tid < B) sm[tid] = min(base + incl - nb, nc);
+    if (tid == B - 1) sm[B] = min(base + incl, nc);
+    __syncthreads();
+    if (blockIdx.x == 0 && tid <= B) p.meta[tid] = sm[tid];
+    const int32_t total = sm[B];
+    for (int64_t c = blockIdx.x + (int64_t)gridDim.x * tid; c < total; c += (int64_t)gridDim.x * 512) {
+        int lo = 0, hi = B - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (sm[mid] <= c) lo = mid; else hi = mid - 1;
+        }
+        const int32_t j = (int32_t)c - sm[lo];
+        int4 e;
+        e.x = lo;
+        e.y = sm[kMapSeqs + 1 + lo] + kChunk * j;
+        e.z = min(kChunk, sm[2 * kMapSeqs + 1 + lo] - kChunk * j);
+        e.w = j;
+        *reinterpret_cast<int4*>(&p.cmap[4 * c]) = e;
+    }
+}
+
+// First token and valid rows of chunk c (wave-uniform) from the LDS map.
+__device__ __forceinline__ void chunk_from_map(const int32_t* sm, int B, int c, int& t0, int& r) {
+    int lo = 0, hi = B - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (__builtin_amdgcn_readfirstlane(sm[mid]) <= c) lo = mid; else hi = mid - 1;
+    }
+    const int j = c - __builtin_amdgcn_readfirstlane(sm[lo]);
+    t0 = __builtin_amdgcn_readfirstlane(sm[kMapSeqs + 1 + lo]) + kChunk * j;
+    r = min(kChunk, __builtin_amdgcn_readfirstlane(sm[2 * kMapSeqs + 1 + lo]) - kChunk * j);
 }
 
 // Transposed fp16 tiles ([col][tok] or [dk][tok]) are stored with the 16-byte
@@ -326,12 +395,18 @@ struct IntraStage {
 };
 
 template <typename ActT, int RULE>
-__device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, int item, int wave, int lane,
-                                           int lr, int lq, int c4, int tg, int part = 3) {
+__device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, const int32_t* smap, int item,
+                                           int wave, int lane, int lr, int lq, int c4, int tg, int part = 3) {
     // part 1: k dims 0..63; part 2: k dims 64..127, g and beta; 3: all
     const int Nv = p.Nv, Nqk = p.Nqk;
     const int c = item / Nv, h = item % Nv, hq = h / (Nv / Nqk);
-    const int t0 = ld_uniform(&p.cmap[4 * c + 1]), r = ld_uniform(&p.cmap[4 * c + 2]);
+    int t0, r;
+    if (p.map_in_intra) {
+        chunk_from_map(smap, p.B, c, t0, r);
+    } else {
+        t0 = ld_uniform(&p.cmap[4 * c + 1]);
+        r = ld_uniform(&p.cmap[4 * c + 2]);
+    }
     st.c = c; st.h = h; st.t0 = t0; st.r = r;
     const ActT* K = static_cast<const ActT*>(p.k);
     const ActT* BETA = static_cast<const ActT*>(p.beta);
@@ -361,6 +436,7 @@ __device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDe
 }
 
 struct IntraSmem {
+    const int32_t* sMap;
     _Float16* sA;
     _Float16* sL;
     float* sD;
@@ -620,7 +696,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     //         and beta load into the stage in two parts, now and in step 6 (this
     //         item took its own in step 1); fp32 inputs, twice the registers,
     //         load at the item's start
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, next, wave, lane, lr, lq, c4, tg, 1);
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, sm.sMap, next, wave, lane, lr, lq, c4, tg, 1);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         if (b < wave) continue;
@@ -638,7 +714,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     }
     __syncthreads();
 
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, next, wave, lane, lr, lq, c4, tg, 2);
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, sm.sMap, next, wave, lane, lr, lq, c4, tg, 2);
     // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk], fragment order  (lower-triangular K
     //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
     //         The wave's four output tiles share each B fragment (row Jt of T).
@@ -707,10 +783,17 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __shared__ __align__(16) float sGc[128];
     __shared__ __align__(16) float sBeta[128];
     __shared__ float sBE[128];
-    const IntraSmem sm{sA, sL, sD, sGc, sBeta, sBE};
+    __shared__ int32_t sMap[kMapInts];
+    const IntraSmem sm{sMap, sA, sL, sD, sGc, sBeta, sBE};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
     const int c4 = tid & 31, tg = tid >> 5;
-    const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
+    int n_items;
+    if (p.map_in_intra) {
+        build_chunk_map(p, sMap, tid);
+        n_items = __builtin_amdgcn_readfirstlane(sMap[p.B]) * p.Nv;
+    } else {
+        n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
+    }
     const int stride = gridDim.x;   // a multiple of 8 G
     int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
     if (it >= n_items) return;
@@ -724,7 +807,7 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
         // loop head are then the same on every path, and the compiler's
         // waits for the prefetched inputs stop at those loads instead of
         // also waiting for the previous item's stores.
-        intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
+        intra_load<ActT, RULE>(st, p, sMap, it, wave, lane, lr, lq, c4, tg);
         int nx = it + stride;
         intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
         while (nx < n_items) {
@@ -734,7 +817,7 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
         }
     } else {
         while (true) {
-            intra_load<ActT, RULE>(st, p, it, wave, lane, lr, lq, c4, tg);
+            intra_load<ActT, RULE>(st, p, sMap, it, wave, lane, lr, lq, c4, tg);
             const int nx = it + stride;
             intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
             if (nx >= n_items) break;
@@ -790,12 +873,16 @@ struct GkStage {
 
 // The place of item `item` (chunk * Nv + value head) in the token stream
 template <typename ActT>
-__device__ __forceinline__ void gk_place(GkStage<ActT>& st, const PrefillDev& p, int item) {
+__device__ __forceinline__ void gk_place(GkStage<ActT>& st, const PrefillDev& p, const int32_t* smap, int item) {
     const int c = item / p.Nv;
     st.c = c;
     st.h = item % p.Nv;
-    st.t0 = ld_uniform(&p.cmap[4 * c + 1]);
-    st.r = ld_uniform(&p.cmap[4 * c + 2]);
+    if (p.map_in_intra) {
+        chunk_from_map(smap, p.B, c, st.t0, st.r);
+    } else {
+        st.t0 = ld_uniform(&p.cmap[4 * c + 1]);
+        st.r = ld_uniform(&p.cmap[4 * c + 2]);
+    }
 }
 
 // Parts of the item in st's place: what = 0: k, 1: q, 2: g and beta (issued
@@ -890,7 +977,7 @@ __device__ __forceinline__ void gk_gate_dma(const PrefillDev& p, int t0, int h, 
 template <typename ActT, int RULE>
 __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const PrefillDev& p, float* sG, _Float16* sK,
                                         _Float16* sQL, float* sD, float* sEs, float* sTail, _Float16* sC, float* sGt,
-                                        float* sBeta, float* sBw, int* sWide, int tid_in) {
+                                        float* sBeta, float* sBw, int* sWide, const int32_t* sMap, int tid_in) {
     int tid = tid_in;
     asm volatile("" : "+v"(tid));
     constexpr bool kDelta = Rule<RULE>::delta;
@@ -1141,7 +1228,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     }
     }
     __syncthreads();   // G is done: KB takes its place, the next gate tile's first half goes behind it
-    gk_place<ActT>(st, p, next);
+    gk_place<ActT>(st, p, sMap, next);
     gk_gate_dma(p, st.t0, st.h, st.r, sG, 0, tid);
 #pragma unroll
     for (int n = 0; n < 4; ++n) st_h8(&sKB[(4 * (tid >> 4) + n) * LD16 + 8 * (tid & 15)], kb[n]);
@@ -1378,8 +1465,15 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     __shared__ __align__(16) _Float16 sC[21 * 128];        // decay between blocks J + 1 < I
     __shared__ float sGt[128], sBeta[128], sBw[128];
     __shared__ int sWide[16];                              // per block and key half: tier of the diagonal tiles
+    __shared__ int32_t sMap[kMapInts];                     // the chunk map, when built here
     const int tid = threadIdx.x;
-    const int n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
+    int n_items;
+    if (p.map_in_intra) {
+        build_chunk_map(p, sMap, tid);
+        n_items = __builtin_amdgcn_readfirstlane(sMap[p.B]) * p.Nv;
+    } else {
+        n_items = ld_uniform(&p.meta[p.B]) * p.Nv;
+    }
     const int stride = gridDim.x;   // a multiple of 8 G
     int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
     if (it >= n_items) return;
@@ -1390,7 +1484,7 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     // this scan, which also fetches q^ e^G and P each step; the intra kernel
     // without the gate keeps chunk order, which measured faster for its scan.
     GkStage<ActT> st;
-    gk_place<ActT>(st, p, n_items - 1 - it);
+    gk_place<ActT>(st, p, sMap, n_items - 1 - it);
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) gk_gate_dma(p, st.t0, st.h, st.r, sG, q4, tid);
     gk_load_in<ActT, RULE>(st, p, 0, tid);
@@ -1399,7 +1493,7 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     while (true) {
         const int nx = it + stride;
         gk_item<ActT, RULE>(st, n_items - 1 - (nx < n_items ? nx : it), p, sG, sK, sQL, sD, sEs, sTail, sC, sGt, sBeta,
-                            sBw, sWide, tid);
+                            sBw, sWide, sMap, tid);
         if (nx >= n_items) break;
         it = nx;
     }
@@ -2228,7 +2322,7 @@ static void launch_intra(int rule, int act, dim3 grid, hipStream_t stream, const
 hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int act, hipStream_t stream) {
     const int ncu = compute_units();
     PrefillDev p;
-    p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.g = a.g; p.beta = a.beta; p.cu = a.cu;
     p.state_in = a.state_in; p.out = a.out; p.state_out = a.state_out;
     p.meta = reinterpret_cast<int32_t*>(a.ws + lay.off_meta);
     p.cmap = reinterpret_cast<int32_t*>(a.ws + lay.off_cmap);
@@ -2245,13 +2339,17 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     p.T = a.T; p.nc = lay.nc; p.B = a.B; p.Nqk = a.Nqk; p.Nv = a.Nv; p.scale = a.scale;
     p.nseg = lay.nseg; p.seg_len = lay.seg_len;
 
-    timing_begin(kChunkmap, stream);
-    hipLaunchKernelGGL(chunkmap_kernel, dim3(1), dim3(256), 0, stream, a.cu, p);
-    timing_end(kChunkmap, stream);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
     const size_t nwg = (size_t)lay.nc * a.Nv;
     const bool gk = a.gk != nullptr;   // the API passes it only with a rule that decays
+    // Few sequences: the intra kernel builds the chunk map itself.
+    p.map_in_intra = (nwg > 0 && a.B <= kMapSeqs) ? 1 : 0;
+    hipError_t e = hipSuccess;
+    if (!p.map_in_intra) {
+        timing_begin(kChunkmap, stream);
+        hipLaunchKernelGGL(chunkmap_kernel, dim3(1), dim3(256), 0, stream, a.cu, p);
+        timing_end(kChunkmap, stream);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
     if (nwg > 0) {
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         timing_begin(kIntra, stream);

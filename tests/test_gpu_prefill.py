@@ -230,6 +230,28 @@ def test_prefill_many_short_sequences(gk):
     check_parity(inp, f"B=300 T={sum(lens)} gk={gk}")
 
 
+def test_prefill_chunk_map_built_in_the_intra_kernel_at_its_limit():
+    """Up to 168 sequences the intra kernel builds the chunk map itself; with
+    more, a separate launch builds it.  168 sequences (empty ones at both
+    ends, chunk-edge lengths) are checked against the oracle; appending an
+    empty 169th sequence switches to the separate launch and must leave
+    every output bit and the first 168 states unchanged, the new sequence's
+    state passed through."""
+    rng = np.random.default_rng(124)
+    lens = rng.integers(0, 300, 168).tolist()
+    lens[0] = lens[167] = lens[90] = 0
+    lens[7], lens[8], lens[9] = 128, 129, 256
+    inp = workloads.prefill_inputs(125, lens, Nqk=1, Nv=2, act="bf16")
+    out, st = check_parity(inp, f"B=168 T={sum(lens)}")
+    extra = torch.randn((1, 2, 128, 128), generator=torch.Generator().manual_seed(126)) * 0.02
+    inp2 = dict(inp, B=169, cu_seqlens=torch.cat([inp["cu_seqlens"], inp["cu_seqlens"][-1:]]),
+                state_in=torch.cat([inp["state_in"], extra]))
+    print("[prefill] B=169 (separate chunk-map launch)", flush=True)
+    out2, st2 = run_gpu(inp2)
+    assert torch.equal(out.view(torch.int16), out2.view(torch.int16))
+    assert torch.equal(st, st2[:168]) and torch.equal(st2[168], extra[0])
+
+
 # Two-level scan: with few (sequence, value head) streams and long sequences
 # the library cuts each sequence into segments, finds every segment's affine
 # map (S_end = M S_start + B) first, then each segment's start state, then
