@@ -394,20 +394,30 @@ struct IntraStage {
     int c, h, t0, r;
 };
 
+// Where item (chunk c, value head h) lies: its first token and valid rows.
+struct ItemPlace {
+    int c, h, t0, r;
+};
+__device__ __forceinline__ ItemPlace place_item(const PrefillDev& p, const int32_t* smap, int item) {
+    ItemPlace at;
+    at.c = item / p.Nv;
+    at.h = item % p.Nv;
+    if (p.map_in_intra) {
+        chunk_from_map(smap, p.B, at.c, at.t0, at.r);
+    } else {
+        at.t0 = ld_uniform(&p.cmap[4 * at.c + 1]);
+        at.r = ld_uniform(&p.cmap[4 * at.c + 2]);
+    }
+    return at;
+}
+
 template <typename ActT, int RULE>
-__device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, const int32_t* smap, int item,
-                                           int wave, int lane, int lr, int lq, int c4, int tg, int part = 3) {
+__device__ __forceinline__ void intra_load(IntraStage<ActT>& st, const PrefillDev& p, const ItemPlace& at, int wave,
+                                           int lane, int lr, int lq, int c4, int tg, int part = 3) {
     // part 1: k dims 0..63; part 2: k dims 64..127, g and beta; 3: all
     const int Nv = p.Nv, Nqk = p.Nqk;
-    const int c = item / Nv, h = item % Nv, hq = h / (Nv / Nqk);
-    int t0, r;
-    if (p.map_in_intra) {
-        chunk_from_map(smap, p.B, c, t0, r);
-    } else {
-        t0 = ld_uniform(&p.cmap[4 * c + 1]);
-        r = ld_uniform(&p.cmap[4 * c + 2]);
-    }
-    st.c = c; st.h = h; st.t0 = t0; st.r = r;
+    const int h = at.h, hq = h / (Nv / Nqk), t0 = at.t0, r = at.r;
+    st.c = at.c; st.h = h; st.t0 = t0; st.r = r;
     const ActT* K = static_cast<const ActT*>(p.k);
     const ActT* BETA = static_cast<const ActT*>(p.beta);
     const int last = max(r - 1, 0);   // every mapped chunk has r >= 1
@@ -537,6 +547,8 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
             raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 8 * c8);
         }
     };
+    // where the next item lies, looked up now: its loads go out in steps 5 and 6
+    const ItemPlace nxt = place_item(p, sm.sMap, next);
     __syncthreads();   // the previous item is done with the shared buffers
     // ---- 1. gate cumulative sum and beta (wave 0); k rows normalised -> sA (row-major)
     if (wave == 0) {   // lane owns rows 2l, 2l+1
@@ -696,7 +708,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     //         and beta load into the stage in two parts, now and in step 6 (this
     //         item took its own in step 1); fp32 inputs, twice the registers,
     //         load at the item's start
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, sm.sMap, next, wave, lane, lr, lq, c4, tg, 1);
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, nxt, wave, lane, lr, lq, c4, tg, 1);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         if (b < wave) continue;
@@ -714,7 +726,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     }
     __syncthreads();
 
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, sm.sMap, next, wave, lane, lr, lq, c4, tg, 2);
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, nxt, wave, lane, lr, lq, c4, tg, 2);
     // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk], fragment order  (lower-triangular K
     //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
     //         The wave's four output tiles share each B fragment (row Jt of T).
@@ -807,7 +819,7 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
         // loop head are then the same on every path, and the compiler's
         // waits for the prefetched inputs stop at those loads instead of
         // also waiting for the previous item's stores.
-        intra_load<ActT, RULE>(st, p, sMap, it, wave, lane, lr, lq, c4, tg);
+        intra_load<ActT, RULE>(st, p, place_item(p, sMap, it), wave, lane, lr, lq, c4, tg);
         int nx = it + stride;
         intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
         while (nx < n_items) {
@@ -817,7 +829,7 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
         }
     } else {
         while (true) {
-            intra_load<ActT, RULE>(st, p, sMap, it, wave, lane, lr, lq, c4, tg);
+            intra_load<ActT, RULE>(st, p, place_item(p, sMap, it), wave, lane, lr, lq, c4, tg);
             const int nx = it + stride;
             intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
             if (nx >= n_items) break;
@@ -873,16 +885,11 @@ struct GkStage {
 
 // The place of item `item` (chunk * Nv + value head) in the token stream
 template <typename ActT>
-__device__ __forceinline__ void gk_place(GkStage<ActT>& st, const PrefillDev& p, const int32_t* smap, int item) {
-    const int c = item / p.Nv;
-    st.c = c;
-    st.h = item % p.Nv;
-    if (p.map_in_intra) {
-        chunk_from_map(smap, p.B, c, st.t0, st.r);
-    } else {
-        st.t0 = ld_uniform(&p.cmap[4 * c + 1]);
-        st.r = ld_uniform(&p.cmap[4 * c + 2]);
-    }
+__device__ __forceinline__ void gk_place(GkStage<ActT>& st, const ItemPlace& at) {
+    st.c = at.c;
+    st.h = at.h;
+    st.t0 = at.t0;
+    st.r = at.r;
 }
 
 // Parts of the item in st's place: what = 0: k, 1: q, 2: g and beta (issued
@@ -1228,7 +1235,7 @@ __device__ __forceinline__ void gk_item(GkStage<ActT>& st, int next, const Prefi
     }
     }
     __syncthreads();   // G is done: KB takes its place, the next gate tile's first half goes behind it
-    gk_place<ActT>(st, p, sMap, next);
+    gk_place<ActT>(st, place_item(p, sMap, next));
     gk_gate_dma(p, st.t0, st.h, st.r, sG, 0, tid);
 #pragma unroll
     for (int n = 0; n < 4; ++n) st_h8(&sKB[(4 * (tid >> 4) + n) * LD16 + 8 * (tid & 15)], kb[n]);
@@ -1484,7 +1491,7 @@ __global__ __launch_bounds__(512) void intra_gk_kernel(PrefillDev p) {
     // this scan, which also fetches q^ e^G and P each step; the intra kernel
     // without the gate keeps chunk order, which measured faster for its scan.
     GkStage<ActT> st;
-    gk_place<ActT>(st, p, sMap, n_items - 1 - it);
+    gk_place<ActT>(st, place_item(p, sMap, n_items - 1 - it));
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) gk_gate_dma(p, st.t0, st.h, st.r, sG, q4, tid);
     gk_load_in<ActT, RULE>(st, p, 0, tid);
