@@ -1773,83 +1773,100 @@ __global__ __launch_bounds__(512) void scan_kernel(PrefillDev p) {
 // stream, S_0 = the stream's initial state, S_{s+1} = M_s S_s + B_s, in fp32.
 // S_0 is written too, so that the scan proper reads no segment's start from
 // state_in (state_out may alias it and is written by the last segment).
-// One workgroup of 256 threads per (stream, 8 state columns); thread t owns
-// rows 2 (t / 4), 2 (t / 4) + 1 and columns 2 (t % 4), 2 (t % 4) + 1 of the
-// slice.  M sits row-major and the S slice transposed in LDS, so four k of
-// the product take four 16-byte reads for 16 FMAs.  The next map is fetched
-// into registers during the product (every fetch is issued: past the last
-// map it re-reads the last one, unused).
-__global__ __launch_bounds__(256) void combine_kernel(PrefillDev p) {
-    __shared__ __align__(16) float sM[128 * 132];   // M_s [dk][k], padded rows
-    __shared__ __align__(16) float sSt[8 * 132];    // S_s slice transposed [col][k]
+// One workgroup of 512 threads per (stream, 8 state columns).  Thread t owns
+// row r = t / 4 of the product and the keys k = 16 i + 4 q + e (q = t % 4,
+// i < 8, e < 4): its 32 entries of M_s sit in registers, fetched
+// kCombineAhead maps ahead, so M never passes through LDS; the S slice does
+// (double-buffered, one barrier per map), and the four threads of a row, one
+// quad, add their partial sums with quad permutes.  Thread q then adds B and
+// stores columns 2 q, 2 q + 1 of row r.
+constexpr int kCombineCols = 8;    // state columns per workgroup
+constexpr int kCombineAhead = 2;   // maps fetched ahead
+template <int CTRL>
+__device__ __forceinline__ float dpp_add(float x) {   // x + (x of the lane CTRL selects within the DPP row)
+    return x + __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, true));
+}
+
+__global__ __launch_bounds__(512) void combine_kernel(PrefillDev p) {
+    constexpr int CW = kCombineCols, NPW = 128 / CW, CQ = CW / 4, NST = kCombineAhead + 1;
+    constexpr int SLD = CW + 4;   // LDS row stride (floats): a quad's four rows fall in distinct banks
+    __shared__ __align__(16) float sS[2][128 * SLD];
     const int Nv = p.Nv, nseg = p.nseg;
-    const int stream = blockIdx.x >> 4, col0 = 8 * (blockIdx.x & 15);
+    const int stream = blockIdx.x / NPW, col0 = CW * (blockIdx.x % NPW);
     if (stream >= p.B * Nv) return;
     const int b = stream / Nv, h = stream % Nv;
     const int cb = ld_uniform(&p.meta[b]), ce = ld_uniform(&p.meta[b + 1]);
     const int nsb = ce > cb ? (ce - cb + p.seg_len - 1) / p.seg_len : 1;
     if (nsb < 2) return;
-    const int tid = threadIdx.x, r0 = 2 * (tid >> 2), c2 = 2 * (tid & 3);
-    float x[2][2];   // S rows r0 + i, columns col0 + c2 + j
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-            x[i][j] = p.state_in ? p.state_in[(size_t)stream * TILE + (size_t)(r0 + i) * 128 + col0 + c2 + j] : 0.f;
+    const int tid = threadIdx.x, r = tid >> 2, q = tid & 3, cq = col0 + CQ * q;
+    const size_t seg_stride = (size_t)Nv * TILE;
+    float* sst = p.sstart + ((size_t)b * nseg * Nv + h) * TILE + (size_t)r * 128 + cq;   // segment 0, row r
     {
-        float* dst0 = p.sstart + (((size_t)b * nseg) * Nv + h) * TILE + (size_t)r0 * 128 + col0 + c2;
+        float x[CQ];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) *reinterpret_cast<float2*>(dst0 + (size_t)i * 128) = float2{x[i][0], x[i][1]};
+        for (int j = 0; j < CQ; ++j)
+            x[j] = p.state_in ? p.state_in[(size_t)stream * TILE + (size_t)r * 128 + cq + j] : 0.f;
+#pragma unroll
+        for (int j = 0; j < CQ; ++j) {
+            sst[j] = x[j];
+            sS[0][r * SLD + CQ * q + j] = x[j];
+        }
     }
     const int last = nsb - 2;   // the last map used
-    f32x4 mr[16];               // float4 number tid + 256 n of M: row (q / 32), columns 4 (q % 32) ..
-    float2 br[2];               // B, rows r0 + i, this thread's two columns
-    auto fetch = [&](int s) {
-        const float* MB = p.mb + (((size_t)b * nseg + min(s, last)) * Nv + h) * (2 * TILE);
+    f32x4 m[NST][8];            // maps s .. s + NST - 1: M[r][16 i + 4 q .. + 3]
+    float bb[NST][CQ];          //   and B[r][cq ..]
+    auto fetch = [&](int slot, int s) {
+        const float* MB = p.mb + (((size_t)b * nseg + min(s, last)) * Nv + h) * (2 * TILE) + (size_t)r * 256;
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const int q = tid + 256 * n;
-            mr[n] = *reinterpret_cast<const f32x4*>(MB + (size_t)(q >> 5) * 256 + 4 * (q & 31));
-        }
+        for (int i = 0; i < 8; ++i) m[slot][i] = *reinterpret_cast<const f32x4*>(MB + 16 * i + 4 * q);
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            br[i] = *reinterpret_cast<const float2*>(MB + (size_t)(r0 + i) * 256 + 128 + col0 + c2);
+        for (int j = 0; j < CQ; ++j) bb[slot][j] = MB[128 + cq + j];
     };
-    fetch(0);
-    for (int s = 0; s <= last; ++s) {
-        __syncthreads();   // the previous product is done with sM and sSt
+    // one map: S_{s+1} = M_s S_s + B_s from sS[s & 1] into sS[(s + 1) & 1] and segment s + 1's start
+    auto step = [&](int slot, int s) {
+        const float* src = sS[s & 1];
+        float acc[CW];
 #pragma unroll
-        for (int n = 0; n < 16; ++n) {
-            const int q = tid + 256 * n;
-            *reinterpret_cast<f32x4*>(&sM[(q >> 5) * 132 + 4 * (q & 31)]) = mr[n];
+        for (int c = 0; c < CW; ++c) acc[c] = 0.f;
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float mk = m[slot][i][e];
+                const float* row = src + (16 * i + 4 * q + e) * SLD;
+#pragma unroll
+                for (int c4 = 0; c4 < CW / 4; ++c4) {
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(row + 4 * c4);
+#pragma unroll
+                    for (int x = 0; x < 4; ++x) acc[4 * c4 + x] = fmaf(mk, v[x], acc[4 * c4 + x]);
+                }
+            }
+#pragma unroll
+        for (int c = 0; c < CW; ++c) acc[c] = dpp_add<0x4E>(dpp_add<0xB1>(acc[c]));   // lane ^ 1, then ^ 2
+        float y[CQ];
+#pragma unroll
+        for (int j = 0; j < CQ; ++j) {
+            const float a01 = q == 0 ? acc[j] : acc[CQ + j];
+            const float a23 = q == 2 ? acc[2 * CQ + j] : acc[3 * CQ + j];
+            y[j] = (q < 2 ? a01 : a23) + bb[slot][j];
         }
+        float* dst = sst + (size_t)(s + 1) * seg_stride;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) sSt[(c2 + j) * 132 + r0 + i] = x[i][j];
-        float acc[2][2] = {{br[0].x, br[0].y}, {br[1].x, br[1].y}};
-        __syncthreads();
-        fetch(s + 1);
-#pragma unroll 4
-        for (int k4 = 0; k4 < 32; ++k4) {
-            f32x4 a[2], v[2];
-#pragma unroll
-            for (int i = 0; i < 2; ++i) a[i] = *reinterpret_cast<const f32x4*>(&sM[(r0 + i) * 132 + 4 * k4]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) v[j] = *reinterpret_cast<const f32x4*>(&sSt[(c2 + j) * 132 + 4 * k4]);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-#pragma unroll
-                for (int i = 0; i < 2; ++i)
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) acc[i][j] = fmaf(a[i][e], v[j][e], acc[i][j]);
+        for (int j = 0; j < CQ; ++j) {
+            dst[j] = y[j];
+            sS[(s + 1) & 1][r * SLD + CQ * q + j] = y[j];
         }
-        float* dst = p.sstart + (((size_t)b * nseg + s + 1) * Nv + h) * TILE + (size_t)r0 * 128 + col0 + c2;
+        __syncthreads();   // segment s + 1's start is in LDS; sS[s & 1] is free
+    };
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+    for (int n = 0; n < NST; ++n) fetch(n, n);
+    __syncthreads();   // S_0 is in LDS
+    for (int s = 0; s <= last; s += NST) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j) x[i][j] = acc[i][j];
-            *reinterpret_cast<float2*>(dst + (size_t)i * 128) = float2{x[i][0], x[i][1]};
+        for (int n = 0; n < NST; ++n) {
+            if (s + n > last) break;
+            step(n, s + n);
+            fetch(n, s + n + NST);
         }
     }
 }
@@ -2387,7 +2404,8 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
         launch_scan<128, 1>(gk, dim3((unsigned)(ngroup * G * 2)), stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // second level: the segments' start states
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((size_t)a.B * a.Nv * 16)), dim3(256), 0, stream, p);
+        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((size_t)a.B * a.Nv * (128 / kCombineCols))),
+                           dim3(512), 0, stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // (segments have equal lengths, so there their slices are sized to fit
