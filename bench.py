@@ -221,6 +221,8 @@ def bench_prefill(args, gdr, torch, workloads):
     mfma_exec_total = 0.0
     for name in fl:
         ms, n = per.get(name, (0.0, 0))
+        if not n:   # not launched for this workload (the chunk map is built inside the intra kernel)
+            continue
         per_call = ms / 1e3
         kernels[name] = {"us_per_call": per_call * 1e6, "launches_per_call": n, "alg_gflop": fl[name] / 1e9,
                          "mfma_frac": (fl[name] / per_call / MFMA_PEAK_FP16) if per_call > 0 and fl[name] else None}
@@ -475,6 +477,9 @@ def main():
                     help="measure plain HBM streams the decode is compared with: an in-place update (read then "
                          "write the same bytes, like the decode's slab update) and an out-of-place copy, each over "
                          "four rotating 512 MiB bf16 buffers; prints one JSON line")
+    ap.add_argument("--config", metavar="NAME",
+                    help="time one workload only (a config number 1-5 or an extra workload's name, e.g. "
+                         "long_few_heads) and print its record as one JSON line (for per-workload profiles)")
     ap.add_argument("--ingest-counters", nargs=5, metavar=("FETCH", "WRITE", "CAL_FETCH", "CAL_WRITE", "MFMA"),
                     help="write profiles/counters.json from rocprofv3 counter_collection.csv files and exit")
     args = ap.parse_args()
@@ -492,6 +497,13 @@ def main():
 
     if args.stream_ceiling:
         print(json.dumps(stream_ceiling(torch)))
+        return
+    if args.config:
+        n = int(args.config) if args.config.isdigit() else args.config
+        if n not in workloads.CONFIG_NAMES and n not in workloads.EXTRA_NAMES:
+            print(f"bench.py: unknown workload {args.config!r}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(time_config(n, args, gdr, torch, workloads)))
         return
     if args.copy_calibration:
         n = 1 << 30
