@@ -64,6 +64,8 @@ def test_workspace_two_level_scan_only_for_few_long_streams():
     T = 25003
     extra = ws_size(T, 3, 1, 4, 128)[1] - _one_level_workspace(T, 3, 1, 4)
     assert extra == 3 * 10 * 4 * 4 * 128 * (256 + 128)
+    # the shape of the GPU test of the two-level scan without an initial state
+    assert ws_size(16700, 2, 1, 2, 128)[1] > _one_level_workspace(16700, 2, 1, 2)
 
 
 def test_workspace_size_validation_and_monotonicity():

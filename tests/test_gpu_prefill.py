@@ -282,6 +282,15 @@ def test_prefill_two_level_scan_fp32_weak_forgetting():
     check_parity(inp, "two-level T=9000 Nqk=1 Nv=1 fp32, weak forgetting")
 
 
+@pytest.mark.parametrize("rule", ["gated_delta", "delta"])
+def test_prefill_two_level_scan_zero_initial_state(rule):
+    """Two-level scan without an initial state: the first segment of each
+    stream starts from the zeros the combine writes; with and without the
+    gate (the delta rule's segment maps carry no decay)."""
+    inp = workloads.prefill_inputs(66, [16000, 700], Nqk=1, Nv=2, act="bf16", init_state="zeros")
+    check_parity(inp, f"two-level lens [16000, 700] Nqk=1 Nv=2, no initial state, rule {rule}", rule=rule)
+
+
 def test_prefill_two_level_scan_long_few_heads_all_heads():
     """Full-size few-head long-context workload (two-level scan): every value
     head over all 131072 tokens against the oracle."""
