@@ -21,6 +21,8 @@ import os
 import numpy as np
 import pytest
 import torch
+from hypothesis import HealthCheck, given, settings
+from hypothesis import strategies as st
 
 import oracle
 from oracle import chunked
@@ -79,6 +81,41 @@ def test_chunked_per_key_gate_equals_recurrence(L, rule):
         o_chk, s_chk = chunked.prefill(q, k, v, g, beta, s0, cu, scale, L=L, rule=rule, gk=gk)
         np.testing.assert_allclose(o_chk, o_ref, rtol=1e-10, atol=1e-11)
         np.testing.assert_allclose(s_chk, s_ref, rtol=1e-10, atol=1e-11)
+
+
+@settings(max_examples=60, deadline=None, derandomize=True, suppress_health_check=[HealthCheck.too_slow])
+@given(seed=st.integers(0, 2 ** 31 - 1), L=st.integers(1, 20),
+       rule=st.sampled_from(["gated_delta", "delta", "gated", "linear"]),
+       gate=st.sampled_from(["weak", "strong", "per_key", "per_key_reset"]))
+def test_property_chunked_equals_recurrence(seed, L, rule, gate):
+    """Generated cases: any chunk length from 1 to 20, every update rule,
+    gates from weak to the decode page's strong range, and per-key gates up
+    to a reset of single key rows (gk = -40).  Sequence lengths straddle the
+    chunk length (empty, shorter, exact multiples, ragged tails), so a
+    mistake at a chunk boundary in either statement shows."""
+    rng = np.random.default_rng(seed)
+    nseq = int(rng.integers(1, 4))
+    lens = [int(rng.choice([0, 1, L - 1, L, L + 1, 2 * L, 3 * L + 2, int(rng.integers(0, 45))])) for _ in range(nseq)]
+    lens = [max(x, 0) for x in lens]
+    Nqk = int(rng.integers(1, 3))
+    Nv = Nqk * int(rng.integers(1, 3))
+    Dk, Dv = int(rng.integers(1, 6)), int(rng.integers(1, 6))
+    q, k, v, g, beta, s0, cu = rand_prefill(rng, lens, Nqk, Nv, Dk, Dv, with_state=bool(rng.integers(0, 2)))
+    T = sum(lens)
+    gk = None
+    if gate == "strong":
+        g = -rng.uniform(0.01, 1.01, (T, Nv))
+    elif gate == "weak":
+        g = -rng.uniform(0.0, 0.05, (T, Nv))
+    else:
+        gk = -rng.uniform(0.0, 1.0, (T, Nv, Dk))
+        if gate == "per_key_reset":
+            gk[rng.random((T, Nv, Dk)) < 0.1] = -40.0
+    scale = float(rng.uniform(0.2, 1.5))
+    o_ref, s_ref = oracle.prefill(q, k, v, g, beta, s0, cu, scale, rule=rule, gk=gk)
+    o_chk, s_chk = chunked.prefill(q, k, v, g, beta, s0, cu, scale, L=L, rule=rule, gk=gk)
+    np.testing.assert_allclose(o_chk, o_ref, rtol=1e-9, atol=1e-10)
+    np.testing.assert_allclose(s_chk, s_ref, rtol=1e-9, atol=1e-10)
 
 
 def test_per_key_gate_zero_is_no_gate_and_rules_without_decay_ignore_it():
