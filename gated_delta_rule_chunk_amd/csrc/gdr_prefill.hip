@@ -1858,17 +1858,28 @@ __global__ __launch_bounds__(512) void combine_kernel(PrefillDev p) {
         }
         __syncthreads();   // segment s + 1's start is in LDS; sS[s & 1] is free
     };
-#pragma unroll
-    for (int n = 0; n < NST; ++n) fetch(n, n);
+    static_assert(NST == 3, "the rounds below take three maps");
+    fetch(0, 0);
+    fetch(1, 1);
+    fetch(2, 2);
     __syncthreads();   // S_0 is in LDS
-    for (int s = 0; s <= last; s += NST) {
-#pragma unroll
-        for (int n = 0; n < NST; ++n) {
-            if (s + n > last) break;
-            step(n, s + n);
-            fetch(n, s + n + NST);
-        }
+    // Whole rounds of three maps, each issuing the same loads and stores, so
+    // that the compiler's memory-counter waits at every step cover exactly
+    // that step's map (fetches past the last map re-read it, unused); then
+    // the last one or two maps.  (Written out: the same rounds as a loop
+    // over the three slots measured 75 against 54 us on the few-head
+    // workload, with looser waits.)
+    int s = 0;
+    for (const int full = (last + 1) / NST * NST; s < full; s += NST) {
+        step(0, s);
+        fetch(0, s + 3);
+        step(1, s + 1);
+        fetch(1, s + 4);
+        step(2, s + 2);
+        fetch(2, s + 5);
     }
+    if (s <= last) step(0, s);
+    if (s + 1 <= last) step(1, s + 1);
 }
 
 // ------------------------------------------------------------------ K3: output
