@@ -41,6 +41,22 @@ def test_noalloc_prefill_matches_workspace_prefill_twice(gk):
         assert_state_close(s2, s_ref, f"noalloc call {n} state")
 
 
+@pytest.mark.parametrize("case", ["two_level", "many_sequences"])
+def test_noalloc_prefill_other_paths(case):
+    """The scratch array also carries the two-level scan's segment maps and
+    start states (few long streams), and the chunk map built by its own
+    launch (more than 168 sequences, no initial state)."""
+    if case == "two_level":
+        inp = workloads.prefill_inputs(72, [16000, 4000], Nqk=1, Nv=2, act="bf16")
+    else:
+        lens = [int(x) for x in torch.randint(0, 90, (200,), generator=torch.Generator().manual_seed(73))]
+        inp = workloads.prefill_inputs(74, lens, Nqk=1, Nv=2, act="bf16", init_state="zeros")
+    print(f"[noalloc] {case}: T={inp['T']} B={inp['B']}", flush=True)
+    o1, s1, o2, s2 = _both(inp)
+    assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), "out differs from gdr_chunk_prefill"
+    assert torch.equal(s1, s2), "state differs from gdr_chunk_prefill"
+
+
 def test_noalloc_prefill_rejects_a_workload_beyond_its_scratch():
     inp = workloads.config_inputs(2)
     d = {k: (v.to(DEV) if isinstance(v, torch.Tensor) else v) for k, v in inp.items()}
