@@ -307,13 +307,15 @@ __device__ __forceinline__ void frag_piece(int e, int& r, int& k) {
 // 8 waves; LDS < 80 KiB so that two workgroups share a CU.
 //   sA  fp16 [128][LD16]: k^ [tok][dk] (Gram) -> k^T [dk][tok] (swizzled, copied out)
 //                         -> (k^ beta e^gcum)^T -> (v beta)^T [col][tok] (swizzled)
-//   sL  fp16 [128][LD16]: L (strictly lower, zero above), then T = (I + L)^-1
-//   sD  fp32 8 x [16][17]: the diagonal 16x16 blocks L_bb, then T_bb
-// T is found by forward substitution over 16-row blocks, one column block per
-// wave: X_j = T_jj, X_b = T_bb (-sum_{j<=a<b} L_ba X_a).  The 16x16x16 MFMA's
-// accumulator layout equals its B-operand layout, so each solved block feeds
-// the next product straight from registers; no barrier is needed inside the
-// solve.  Operands are plain fp16 with fp32 accumulation.
+//   sL  fp16 [128][LD16]: L (strictly lower); then T_bb = (I + L_bb)^-1 on the
+//                         diagonal blocks and M_ba = -T_bb L_ba below them
+//   sD  fp32 8 x [16][17]: the diagonal 16x16 blocks L_bb
+// w and u solve (I + L) X = R for R = k^ beta e^gcum and R = v beta by
+// forward substitution over 16-row blocks, one 16-column tile per wave:
+// X_b = T_bb R_b + sum_{a<b} M_ba X_a.  The 16x16x16 MFMA's accumulator
+// layout equals its B-operand layout, so each solved block feeds the later
+// blocks' products straight from registers; no barrier is needed inside the
+// substitution.  Operands are plain fp16 with fp32 accumulation.
 // Load of a lane-uniform int that the running kernel never writes (the chunk
 // map), through the scalar unit: it waits on the scalar counter only, not on
 // the vector-memory counter that also tracks this workgroup's pending stores.
@@ -511,6 +513,43 @@ __device__ __forceinline__ void block_column_solve(const float* sD, const _Float
     }
 }
 
+// Block forward substitution for one 16-column tile of X = (I + L)^-1 R.
+// acc[b] enters as T_bb R_b (T_bb = (I + L_bb)^-1) in the 16x16x16 MFMA's
+// accumulator layout; sL holds M_ba = -T_bb L_ba (fp16) for b > a, so that
+// X_b = T_bb R_b + sum_{a<b} M_ba X_a.  Each solved block X_a is rounded to
+// fp16 once, handed to store(a, X_a), and at once adds its term to every later
+// block (right-looking): the accumulator layout equals the B-operand layout, so
+// the chain from one solved block to the next is one conversion and one
+// product, and the other products come off it.
+template <typename Store>
+__device__ __forceinline__ void block_substitution(f32x4 (&acc)[8], const _Float16* sL, int lr, int lq, Store&& store) {
+#pragma unroll
+    for (int a = 0; a < 8; ++a) {
+        const half4 xa = to_h4(acc[a]);
+#pragma unroll
+        for (int b = a + 1; b < 8; ++b) acc[b] = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq]), xa, acc[b]);
+        store(a, xa);
+    }
+}
+
+// Two transposed 16x16 blocks of w, token blocks a0 and a0 + 1 of column tile
+// ct (a lane holds token 16 a + lr, columns 16 ct + 4 lq ..), into the tile's
+// fragment order.  The two lanes 16 apart (lq, lq ^ 1) that hold the halves of
+// a 16-byte piece swap them with v_permlane16_swap over the pair, so each lane
+// writes one whole piece: block a0 + (lq & 1), columns 16 ct + 8 (lq >> 1) ..
+__device__ __forceinline__ void store_w_pair(_Float16* dst, half4 x0, half4 x1, int a0, int ct, int lr, int lq) {
+    const u32x2 ua = __builtin_bit_cast(u32x2, x0), ub = __builtin_bit_cast(u32x2, x1);
+    u32x4 piece;
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const auto r = __builtin_amdgcn_permlane16_swap(ua[d], ub[d], false, false);
+        piece[d] = r[0];
+        piece[2 + d] = r[1];
+    }
+    const int a = a0 + (lq & 1);
+    st_h8(dst + frag_off(16 * a + lr, 16 * ct + 8 * (lq >> 1)), __builtin_bit_cast(half8, piece));
+}
+
 template <typename ActT, int RULE>
 __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const PrefillDev& p, const IntraSmem& sm,
                                            int tid_in) {
@@ -608,8 +647,8 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
 
     load_v(0);
     // ---- 2. Gram k^ k^T on the lower 16-tiles -> L (fp16 in sL, diagonal
-    //         blocks also fp32 in sD); zeros above the block diagonal of sL;
-    //         k^ read back transposed (8 tokens x 4 dk per thread).
+    //         blocks also fp32 in sD); k^ read back transposed (8 tokens x
+    //         4 dk per thread).
     //         Waves take whole tile rows so that a row's A fragments load
     //         once: rows pair up as (pp, 7 - pp); wave 2 pp takes row pp and
     //         the first 4 - pp tiles of row 7 - pp, wave 2 pp + 1 the other
@@ -653,18 +692,14 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
             gram_row(7 - pp, 0, 4 - pp);
         }
     }
-    {
-        const int i = tid >> 2, I = i >> 4;
-        const half8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-        for (int gg = 2 * (I + 1) + (tid & 3); gg < 16; gg += 4) st_h8(&sL[i * LD16 + 8 * gg], z);
-    }
     half4 kt[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) kt[i] = ld_h4(&sA[(8 * tg + i) * LD16 + 4 * c4]);
     __syncthreads();
 
     // ---- 3. k^T into sA; inverses of the diagonal blocks T_bb = (I + L_bb)^-1
-    //         (one column per lane, forward substitution in fp32)
+    //         (one column per lane, forward substitution in fp32), stored in
+    //         fp16 over the diagonal blocks of sL
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         half8 col;
@@ -674,7 +709,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
     }
     if (tid < 128) {
         const int bb = tid >> 4, j = tid & 15;
-        float* Lb = &sD[bb * 16 * 17];
+        const float* Lb = &sD[bb * 16 * 17];
         float t[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
@@ -684,70 +719,65 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
             t[i] = acc;
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) Lb[i * 17 + j] = t[i];
+        for (int i = 0; i < 16; ++i) sL[(16 * bb + i) * LD16 + 16 * bb + j] = (_Float16)t[i];
     }
     __syncthreads();
 
     load_v(4);
-    // ---- 4. unscaled k^T -> workspace (fragment order); column block j = wave of T by forward substitution
-    if (writes_keys) {
-#pragma unroll
-        for (int n = 0; n < 4; ++n) {
-            const int e_ = tid + 512 * n;
-            int row, kc;
-            frag_piece(e_, row, kc);
-            st_h8(p.khatT + cq * TILE + (size_t)e_ * 8, ld_h8(&sA[sw(row, kc)]));
-        }
-    }
-    half4 xh[8];
-    block_column_solve(sD, sL, wave, lr, lq, xh);
-    __syncthreads();
-
-    // ---- 5. T (fp16) into sL over L (zeros above the block diagonal stay);
-    //         sA scaled in place to (k^ beta e^gcum)^T.  The next item's k, g
-    //         and beta load into the stage in two parts, now and in step 6 (this
-    //         item took its own in step 1); fp32 inputs, twice the registers,
-    //         load at the item's start
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, nxt, wave, lane, lr, lq, c4, tg, 1);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        if (b < wave) continue;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sL[(16 * b + 4 * lq + e) * LD16 + 16 * wave + lr] = xh[b][e];
-    }
+    // ---- 4. unscaled k^T -> workspace (fragment order), and in place scaled
+    //         to R = (k^ beta e^gcum)^T; M_ba = -T_bb L_ba over L_ba (b > a),
+    //         28 blocks over the waves.  M_ba^T = L_ba^T T_bb^T is formed so
+    //         that a lane holds four consecutive columns of one row of M_ba.
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
-        const int e_ = tid + 512 * n, row = e_ >> 4, gg = e_ & 15;
-        _Float16* pk = &sA[sw(row, 8 * gg)];
+        const int e_ = tid + 512 * n;
+        int row, kc;
+        frag_piece(e_, row, kc);
+        _Float16* pk = &sA[sw(row, kc)];
         half8 x = ld_h8(pk);
+        if (writes_keys) st_h8(p.khatT + cq * TILE + (size_t)e_ * 8, x);
+        float be[8];
+        lds_row8(&sBE[kc], be);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * sBE[8 * gg + e]);
+        for (int e = 0; e < 8; ++e) x[e] = (_Float16)((float)x[e] * be[e]);
         st_h8(pk, x);
     }
-    __syncthreads();
-
-    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, nxt, wave, lane, lr, lq, c4, tg, 2);
-    // ---- 6. w^T = (k^ beta e^g)^T T^T -> w [tok][dk], fragment order  (lower-triangular K
-    //         ranges; waves take token tiles {pr, 7 - pr}, balanced)
-    //         The wave's four output tiles share each B fragment (row Jt of T).
-    const int pr = wave & 3, hsel = wave >> 2;
+    const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const int Jt = which ? 7 - pr : pr;
-        f32x4 acc[4];
+    for (int m = 0; m < 4; ++m) {
+        const int n = wave + 8 * m;   // block (b, a), n = b (b - 1) / 2 + a
+        if (n < 28) {
+            const int b = 1 + (n >= 1) + (n >= 3) + (n >= 6) + (n >= 10) + (n >= 15) + (n >= 21);
+            const int a = n - b * (b - 1) / 2;
+            half4 lt;
 #pragma unroll
-        for (int ii = 0; ii < 4; ++ii) acc[ii] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks <= Jt / 2; ++ks) {
-            const half8 b = ld_h8(&sL[(16 * Jt + lr) * LD16 + 32 * ks + 8 * lq]);
-#pragma unroll
-            for (int ii = 0; ii < 4; ++ii)
-                acc[ii] = mma(ld_h8(&sA[sw(16 * (4 * hsel + ii) + lr, 32 * ks + 8 * lq)]), b, acc[ii]);
+            for (int e = 0; e < 4; ++e) lt[e] = sL[(16 * b + 4 * lq + e) * LD16 + 16 * a + lr];
+            const f32x4 mt = mma16(lt, ld_h4(&sL[(16 * b + lr) * LD16 + 16 * b + 4 * lq]), zero);
+            st_h4(&sL[(16 * b + lr) * LD16 + 16 * a + 4 * lq], to_h4(-mt));
         }
-        store_w_tiles(p.w + ch * TILE, acc, Jt, hsel, lr, lq);
     }
     __syncthreads();
 
-    // ---- 7. (v beta)^T [col][tok] into sA
+    // ---- 5. w = (I + L)^-1 R by block forward substitution, one 16-column
+    //         tile ct = wave per wave: X_b = T_bb R_b + sum_{a<b} M_ba X_a.
+    //         The next item's k, g and beta load into the stage in two parts,
+    //         now and in step 6 (this item took its own in step 1); fp32
+    //         inputs, twice the registers, load at the item's start
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, nxt, wave, lane, lr, lq, c4, tg, 1);
+    const int ct = wave;
+    f32x4 acc[8];
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+        acc[b] = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * b + 4 * lq]), ld_h4(&sA[sw(16 * ct + lr, 16 * b + 4 * lq)]),
+                       zero);
+    __syncthreads();   // R is read
+
+    if constexpr (sizeof(ActT) == 2) intra_load<ActT, RULE>(st, p, nxt, wave, lane, lr, lq, c4, tg, 2);
+    // ---- 6. (v beta)^T [col][tok] into sA; the substitution for w.  Each
+    //         solved block goes to the store transposed (a product with I
+    //         turns its accumulator layout, four tokens of one column, into
+    //         four columns of one token) and pairs of blocks are stored as
+    //         16-byte fragment pieces.
     {
         const int c8 = tid & 15, tq = tid >> 4;
         float vf[4][8];
@@ -762,26 +792,28 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
             st_h4(&sA[sw(8 * c8 + e, 4 * tq)], col);
         }
     }
-    __syncthreads();
-
-    // ---- 8. u = T (v beta) -> u, fragment order
-    //         The wave's four output tiles share each A fragment (row I of T).
+    {
+        half4 eye;
 #pragma unroll
-    for (int which = 0; which < 2; ++which) {
-        const int I = which ? 7 - pr : pr;
-        f32x4 acc[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) acc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int ks = 0; ks <= I / 2; ++ks) {
-            const half8 a = ld_h8(&sL[(16 * I + lr) * LD16 + 32 * ks + 8 * lq]);
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj)
-                acc[jj] = mma(a, ld_h8(&sA[sw(16 * (4 * hsel + jj) + lr, 32 * ks + 8 * lq)]), acc[jj]);
-        }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj)
-            st_h4(p.u + ch * TILE + cfrag_off(16 * I + 4 * lq, 16 * (4 * hsel + jj) + lr), to_h4(acc[jj]));
+        for (int e = 0; e < 4; ++e) eye[e] = (_Float16)(4 * lq + e == lr ? 1.f : 0.f);
+        half4 prev;
+        block_substitution(acc, sL, lr, lq, [&](int a, half4 xa) {
+            const half4 xt = to_h4(mma16(xa, eye, zero));   // token 16 a + lr, columns 16 ct + 4 lq ..
+            if (a & 1) store_w_pair(p.w + ch * TILE, prev, xt, a - 1, ct, lr, lq);
+            else prev = xt;
+        });
     }
+    __syncthreads();   // v beta is in sA
+
+    // ---- 7. the same substitution for u = (I + L)^-1 (v beta), stored in
+    //         C-fragment order straight from the accumulator layout
+#pragma unroll
+    for (int b = 0; b < 8; ++b)
+        acc[b] = mma16(ld_h4(&sL[(16 * b + lr) * LD16 + 16 * b + 4 * lq]), ld_h4(&sA[sw(16 * ct + lr, 16 * b + 4 * lq)]),
+                       zero);
+    block_substitution(acc, sL, lr, lq, [&](int a, half4 xa) {
+        st_h4(p.u + ch * TILE + cfrag_off(16 * a + 4 * lq, 16 * ct + lr), xa);
+    });
 }
 
 // Persistent: each workgroup walks items blockIdx.x, blockIdx.x + gridDim.x, ...
@@ -794,7 +826,7 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     __shared__ float sD[8 * 16 * 17];
     __shared__ __align__(16) float sGc[128];
     __shared__ __align__(16) float sBeta[128];
-    __shared__ float sBE[128];
+    __shared__ __align__(16) float sBE[128];
     __shared__ int32_t sMap[kMapInts];
     const IntraSmem sm{sMap, sA, sL, sD, sGc, sBeta, sBE};
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, lr = lane & 15, lq = lane >> 4;
