@@ -841,6 +841,22 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
     const int stride = gridDim.x;   // a multiple of 8 G
     int it = group_slot(blockIdx.x, p.Nv / p.Nqk);
     if (it >= n_items) return;
+    // Wave priority per item.  Two workgroups share each CU, and the CU issues
+    // the older one's ready waves first, so with equal priorities the second
+    // workgroup dispatched to a CU (ids from gridDim.x / 2) ran its items about
+    // a quarter slower and set the kernel's end.  That workgroup takes the
+    // higher priority on every other item; a workgroup that has one item more
+    // than the least loaded ones (the last, partial round) takes the highest on
+    // all of its items.  Priorities change only the order of issue.
+    const bool second = blockIdx.x >= stride / 2;
+    const bool extra = (n_items - 1 - it) / stride + 1 > n_items / stride;
+    int k_item = 0;
+    auto item_priority = [&]() {
+        if (extra) __builtin_amdgcn_s_setprio(2);
+        else if (second && (k_item & 1) == 0) __builtin_amdgcn_s_setprio(1);
+        else __builtin_amdgcn_s_setprio(0);
+        ++k_item;
+    };
     // One register stage: the item loads the next one's k, g and beta into it
     // once it has used its own (after the last item they re-read the current
     // one, unused); with fp32 inputs each item loads its own at its start.
@@ -853,16 +869,19 @@ __global__ __launch_bounds__(512, 4) void intra_kernel(PrefillDev p) {
         // also waiting for the previous item's stores.
         intra_load<ActT, RULE>(st, p, place_item(p, sMap, it), wave, lane, lr, lq, c4, tg);
         int nx = it + stride;
+        item_priority();
         intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
         while (nx < n_items) {
             it = nx;
             nx = it + stride;
+            item_priority();
             intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
         }
     } else {
         while (true) {
             intra_load<ActT, RULE>(st, p, place_item(p, sMap, it), wave, lane, lr, lq, c4, tg);
             const int nx = it + stride;
+            item_priority();
             intra_item<ActT, RULE>(st, nx < n_items ? nx : it, p, sm, tid);
             if (nx >= n_items) break;
             it = nx;
