@@ -128,6 +128,12 @@ gdr_status gdr_chunk_prefill_workspace_size(int64_t T, int32_t B, int32_t Nqk, i
  * its state through unchanged.  `rule` selects a reduced update (see
  * gdr_update_rule); q and k are L2-normalised inside for every rule.
  *
+ * Arithmetic: MFMA operands are fp16 with fp32 accumulation.  The state is
+ * carried in fp32, but u, v_new, the chunk-start states and the operand of
+ * the state in w S are held in fp16, so entries of v (times beta) and of the
+ * state must stay inside the fp16 range: magnitudes beyond about 3e4 can
+ * overflow to inf.  Unit keys and decaying gates keep both at the scale of v.
+ *
  *   q, k        [T, Nqk, D]   act dtype   (raw; normalised inside)
  *   v           [T, Nv, D]    act dtype
  *   g           [T, Nv]       fp32        log-decay gate (expected < 0)

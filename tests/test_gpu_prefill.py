@@ -106,6 +106,27 @@ def test_prefill_strong_gate_without_per_key_gate():
     check_parity(inp, "T=8192 varlen, g = -U(0.01, 1.01)")
 
 
+def test_prefill_repeated_keys_beta_one():
+    """Three keys written in turn with beta = 1, so every write replaces the
+    value stored under its key: the strictly lower L then holds entries near
+    one (exactly one without decay), the largest the block substitution for w
+    and u meets ("Qwen3Next Samples", Matrix Inversion)."""
+    inp = workloads.prefill_inputs(90, [300, 130, 1], Nqk=1, Nv=2, act="bf16", g_range=(1e-6, 1e-5))
+    T = inp["k"].shape[0]
+    k = inp["k"][:3].clone()[torch.arange(T) % 3]
+    inp = dict(inp, k=k, beta=torch.ones_like(inp["beta"]))
+    check_parity(inp, "three repeated keys, beta = 1")
+
+
+def test_prefill_large_values_inside_fp16_range():
+    """v and the initial state scaled by 512 (bf16, entries up to a few
+    thousand): the fp16 intermediates (u, v_new, the chunk-start states) hold
+    them, and the errors scale with the values."""
+    inp = workloads.prefill_inputs(91, [700, 300], Nqk=2, Nv=4, act="bf16")
+    inp = dict(inp, v=(inp["v"].float() * 512).to(torch.bfloat16), state_in=inp["state_in"] * 512)
+    check_parity(inp, "v and state x 512")
+
+
 @pytest.mark.parametrize("rule,g_range", [("linear", (0.001, 0.1)), ("gated_delta", (1e-6, 1e-5))])
 def test_prefill_long_sequence_without_forgetting(rule, g_range):
     """32768 tokens with no decay (the linear rule, whose state only grows)
