@@ -48,6 +48,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 MFMA_PEAK_FP16 = 2.5e15     # MI355X dense fp16/bf16 MFMA, FLOP/s
+MFMA_PEAK_FP32 = 157.3e12    # MI355X dense fp32 MFMA, FLOP/s
 HBM_PEAK = 8.0e12           # MI355X HBM3E, B/s
 D = 128
 L = 128
@@ -392,6 +393,37 @@ def stream_ceiling(torch):
     return {"stream_ceiling": res, "bytes_per_launch": 2 * n * 2}
 
 
+def mfma_peak(torch, gdr):
+    """Dense MFMA issue rates of this GPU from the library's probe
+    (gdr_mfma_peak_probe): per instruction kind, two launches to warm up, then
+    five timed with hipEvents on the probe's stream; TFLOP/s, the fraction of
+    the published dense peak of that dtype, the shader clock the probe ran at
+    (median over workgroups, last launch) and the fraction rescaled to the
+    published 2.4 GHz."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(cus * 8 * 256, dtype=torch.float32, device="cuda:0")
+    published = {"f16_16x16x32": MFMA_PEAK_FP16, "bf16_16x16x32": MFMA_PEAK_FP16,
+                 "f16_16x16x16": MFMA_PEAK_FP16, "f32_16x16x4": MFMA_PEAK_FP32, "f16_32x32x16": MFMA_PEAK_FP16}
+    iters = {"f16_16x16x32": 2000, "bf16_16x16x32": 2000, "f16_16x16x16": 2000, "f32_16x16x4": 1000,
+             "f16_32x32x16": 2000}
+    res = {}
+    for kind in gdr.PROBE_KINDS:
+        for _ in range(2):
+            gdr.mfma_peak_probe(kind, iters[kind], sink)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        flops = sum(gdr.mfma_peak_probe(kind, iters[kind], sink) for _ in range(5))
+        e1.record()
+        torch.cuda.synchronize()
+        s = e0.elapsed_time(e1) / 1e3
+        mhz = sink[::256].float().median().item()
+        res[kind] = {"TFLOP_s": flops / s / 1e12, "frac_of_published": flops / s / published[kind],
+                     "us_per_launch": s / 5 * 1e6, "shader_clock_MHz": mhz,
+                     "frac_of_published_at_2400MHz": flops / s / published[kind] * 2400.0 / mhz if mhz else None}
+    return res
+
+
 KERNEL_FUNCTIONS = {"chunkmap_kernel": "gdr_chunkmap", "intra_kernel": "gdr_intra", "intra_gk_kernel": "gdr_intra",
                     "scan_kernel": "gdr_scan", "scan_gk_out_kernel": "gdr_scan", "combine_kernel": "gdr_scan",
                     "output_kernel": "gdr_output", "output_gk_kernel": "gdr_output",
@@ -477,6 +509,9 @@ def main():
                     help="measure plain HBM streams the decode is compared with: an in-place update (read then "
                          "write the same bytes, like the decode's slab update) and an out-of-place copy, each over "
                          "four rotating 512 MiB bf16 buffers; prints one JSON line")
+    ap.add_argument("--mfma-peak", action="store_true",
+                    help="measure the dense MFMA issue rate of each instruction kind the kernels use with the "
+                         "library's probe; prints one JSON line")
     ap.add_argument("--config", metavar="NAME",
                     help="time one workload only (a config number 1-5 or an extra workload's name, e.g. "
                          "long_few_heads) and print its record as one JSON line (for per-workload profiles)")
@@ -497,6 +532,9 @@ def main():
 
     if args.stream_ceiling:
         print(json.dumps(stream_ceiling(torch)))
+        return
+    if args.mfma_peak:
+        print(json.dumps({"mfma_peak": mfma_peak(torch, gdr)}))
         return
     if args.config:
         n = int(args.config) if args.config.isdigit() else args.config
@@ -550,6 +588,10 @@ def main():
                    "alg_bytes_mb": dec["alg_bytes_mb"], "roofline": dec["roofline"],
                    "device_copy_reference_GBps": dec["copy_gbs"]},
     }
+    # the ceilings measured on this GPU, beside the published peaks the
+    # roofline objects use: dense MFMA issue rates and plain HBM streams
+    line["measured_ceilings"] = {"mfma": mfma_peak(torch, gdr),
+                                 "hbm": stream_ceiling(torch)["stream_ceiling"]}
     if not args.no_configs:
         # the other configured workloads (the T=8192 prefill and the B=256
         # decode are the entries above) and the extra ones, each timed on its

@@ -61,7 +61,10 @@ SIGNATURES = {
     "gdr_timing_read": (ctypes.c_int, [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int32),
                                        _i32]),
     "gdr_timing_kernel_name": (ctypes.c_char_p, [_i32]),
+    "gdr_mfma_peak_probe": (ctypes.c_int, [_i32, _i64, _vp, _i64, ctypes.POINTER(ctypes.c_double), _vp]),
 }
+# MFMA instruction of each probe kind (gdr_mfma_peak_probe)
+PROBE_KINDS = ("f16_16x16x32", "bf16_16x16x32", "f16_16x16x16", "f32_16x16x4", "f16_32x32x16")
 TIMING_KERNELS = 5
 
 _lib = None
@@ -154,6 +157,16 @@ def timing_read() -> dict:
     n = (ctypes.c_int32 * TIMING_KERNELS)()
     check(lib().gdr_timing_read(ms, n, TIMING_KERNELS), "gdr_timing_read")
     return {lib().gdr_timing_kernel_name(i).decode(): (ms[i], n[i]) for i in range(TIMING_KERNELS)}
+
+
+def mfma_peak_probe(kind: str, iters: int, sink) -> float:
+    """Enqueue one launch of the MFMA issue-rate probe (see gdr.h) on the
+    current stream of sink's device; returns the launch's flop count.  sink
+    is a float32 device tensor of at least CUs * 8 * 256 elements."""
+    flops = ctypes.c_double(0.0)
+    check(lib().gdr_mfma_peak_probe(PROBE_KINDS.index(kind), int(iters), sink.data_ptr(), sink.numel(),
+                                    ctypes.byref(flops), _stream(sink.device)), "gdr_mfma_peak_probe")
+    return float(flops.value)
 
 
 def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128, gk: bool = False) -> int:

@@ -264,4 +264,24 @@ gdr_status gdr_recurrent_decode(const void* q, const void* k, const void* v, con
                     "decode launch");
 }
 
+gdr_status gdr_mfma_peak_probe(int32_t kind, int64_t iters, float* sink, int64_t sink_floats,
+                               double* flops_per_launch, void* hip_stream) {
+    if (kind < 0 || kind >= gdr::kProbeKinds)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "probe kind must be 0..%d (got %d)", gdr::kProbeKinds - 1, kind);
+    if (iters < 1 || iters > (int64_t(1) << 24))
+        return fail(GDR_ERR_INVALID_ARGUMENT, "probe iterations must be 1..2^24 (got %lld)", (long long)iters);
+    if (!sink || !flops_per_launch) return fail(GDR_ERR_INVALID_ARGUMENT, "sink and flops_per_launch must not be NULL");
+    int dev = 0, cus = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return from_hip(e, "querying the device");
+    const int64_t grid = (int64_t)cus * gdr::kProbeWgsPerCu;
+    if (sink_floats < grid * 256)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "sink holds %lld floats; the probe writes %lld", (long long)sink_floats,
+                    (long long)(grid * 256));
+    *flops_per_launch = (double)grid * 4 * (double)iters * gdr::kProbeChains[kind] * gdr::kProbeFlops[kind];
+    return from_hip(gdr::mfma_probe_launch(kind, iters, sink, (int)grid, static_cast<hipStream_t>(hip_stream)),
+                    "probe launch");
+}
+
 }  // extern "C"

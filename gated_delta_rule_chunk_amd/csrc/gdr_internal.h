@@ -18,6 +18,16 @@ void timing_begin(int id, hipStream_t s);
 void timing_end(int id, hipStream_t s);
 const char* kernel_name(int id);
 
+// The MFMA issue-rate probe (gdr_mfma_peak_probe): kinds, flops per
+// instruction, and one launch of `grid` workgroups of four waves.
+constexpr int kProbeKinds = 5;
+constexpr int kProbeWgsPerCu = 8;     // four-wave workgroups per CU: 32 waves, eight per SIMD
+// independent accumulator chains per wave, and flops per instruction
+constexpr int kProbeChains[kProbeKinds] = {8, 8, 8, 8, 4};
+constexpr double kProbeFlops[kProbeKinds] = {16.0 * 16 * 32 * 2, 16.0 * 16 * 32 * 2, 16.0 * 16 * 16 * 2,
+                                             16.0 * 16 * 4 * 2, 32.0 * 32 * 16 * 2};
+hipError_t mfma_probe_launch(int kind, int64_t iters, float* sink, int grid, hipStream_t stream);
+
 struct DecodeArgs {
     const void* q;
     const void* k;

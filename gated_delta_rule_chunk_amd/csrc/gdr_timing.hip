@@ -6,6 +6,10 @@
 // gdr_timing_read waits for the recorded events, returns the summed
 // durations and launch counts per kernel, and forgets them.  Disabled (the
 // default), the hooks cost one relaxed atomic load per launch.
+//
+// It also holds the MFMA issue-rate probe behind gdr_mfma_peak_probe: the
+// dense rate of each MFMA kind the kernels use, measured on the part for the
+// roofline's compute ceiling.
 #include "gdr.h"
 #include "gdr_internal.h"
 
@@ -62,6 +66,96 @@ void timing_end(int id, hipStream_t s) {
     if (!e || hipEventRecord(e, s) != hipSuccess) return;
     std::lock_guard<std::mutex> lk(g_mu);
     g_recs.push_back(Rec{id, b, e});
+}
+
+// ------------------------------------------------------------------ MFMA issue-rate probe
+// Every wave runs kProbeChains[KIND] independent accumulator chains of one
+// MFMA kind for `iters` rounds (eight waves per SIMD keep the matrix pipe fed);
+// the accumulators' sum goes to sink, so no product is dead, except in
+// thread 0 of each workgroup, which writes the shader clock over the
+// workgroup's run.  Operands are small constants, so the sums stay finite.
+namespace {
+
+typedef _Float16 probe_h8 __attribute__((ext_vector_type(8)));
+typedef _Float16 probe_h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 probe_b8 __attribute__((ext_vector_type(8)));
+typedef float probe_f4 __attribute__((ext_vector_type(4)));
+typedef float probe_f16 __attribute__((ext_vector_type(16)));
+
+template <int KIND>
+__global__ __launch_bounds__(256) void mfma_rate_kernel(int64_t iters, float* sink) {
+    constexpr int NCH = kProbeChains[KIND];
+    const uint64_t t0 = __builtin_amdgcn_s_memtime(), r0 = __builtin_amdgcn_s_memrealtime();
+    asm volatile("" ::: "memory");
+    const float x = 1e-3f * (float)(1 + (threadIdx.x & 7));
+    probe_f4 acc[NCH];
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) acc[j] = probe_f4{0.f, 0.f, 0.f, 0.f};
+    if constexpr (KIND == 4) {   // fp16 32x32x16, 16 accumulators a lane
+        probe_h8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] = (_Float16)x; b[e] = (_Float16)(0.5f * x); }
+        probe_f16 big[NCH];
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) big[j][e] = 0.f;
+        for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) big[j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, big[j], 0, 0, 0);
+#pragma unroll
+        for (int j = 0; j < NCH; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[j][e] = big[j][e] + big[j][4 + e] + big[j][8 + e] + big[j][12 + e];
+    } else if constexpr (KIND == 0) {   // fp16 16x16x32
+        probe_h8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] = (_Float16)x; b[e] = (_Float16)(0.5f * x); }
+        for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, acc[j], 0, 0, 0);
+    } else if constexpr (KIND == 1) {   // bf16 16x16x32
+        probe_b8 a, b;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { a[e] = (__bf16)x; b[e] = (__bf16)(0.5f * x); }
+        for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[j], 0, 0, 0);
+    } else if constexpr (KIND == 2) {   // fp16 16x16x16
+        probe_h4 a, b;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) { a[e] = (_Float16)x; b[e] = (_Float16)(0.5f * x); }
+        for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, acc[j], 0, 0, 0);
+    } else {   // fp32 16x16x4
+        const float a = x, b = 0.5f * x;
+        for (int64_t i = 0; i < iters; ++i)
+#pragma unroll
+            for (int j = 0; j < NCH; ++j) acc[j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) s += acc[j][0] + acc[j][1] + acc[j][2] + acc[j][3];
+    asm volatile("" : "+v"(s) :: "memory");
+    // thread 0 reports the shader clock over its workgroup's run (shader
+    // cycles against the 100 MHz real-time counter), in MHz
+    const uint64_t t1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    const float mhz = r1 > r0 ? (float)((double)(t1 - t0) * 100.0 / (double)(r1 - r0)) : 0.f;
+    sink[(size_t)blockIdx.x * blockDim.x + threadIdx.x] = threadIdx.x == 0 ? mhz : s;
+}
+
+}  // namespace
+
+hipError_t mfma_probe_launch(int kind, int64_t iters, float* sink, int grid, hipStream_t stream) {
+    switch (kind) {
+        case 0: hipLaunchKernelGGL(mfma_rate_kernel<0>, dim3(grid), dim3(256), 0, stream, iters, sink); break;
+        case 1: hipLaunchKernelGGL(mfma_rate_kernel<1>, dim3(grid), dim3(256), 0, stream, iters, sink); break;
+        case 2: hipLaunchKernelGGL(mfma_rate_kernel<2>, dim3(grid), dim3(256), 0, stream, iters, sink); break;
+        case 3: hipLaunchKernelGGL(mfma_rate_kernel<3>, dim3(grid), dim3(256), 0, stream, iters, sink); break;
+        default: hipLaunchKernelGGL(mfma_rate_kernel<4>, dim3(grid), dim3(256), 0, stream, iters, sink); break;
+    }
+    return hipGetLastError();
 }
 
 }  // namespace gdr

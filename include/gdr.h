@@ -275,6 +275,29 @@ gdr_status gdr_timing_enable(int kernel_mask);
 gdr_status gdr_timing_read(double *total_ms, int32_t *launches, int32_t n);
 const char *gdr_timing_kernel_name(int32_t id);
 
+/* gdr_mfma_peak_probe -- the dense MFMA issue rate of this GPU, for the
+ * roofline's compute peak measured on the part rather than taken from its
+ * data sheet.  Enqueues on hip_stream one launch of 8 workgroups of four
+ * waves per CU; every wave runs 8 independent accumulator chains (4 for
+ * kind 4) of `iters` instructions of one kind:
+ *   kind 0  v_mfma_f32_16x16x32_f16   (the prefill's main products)
+ *   kind 1  v_mfma_f32_16x16x32_bf16
+ *   kind 2  v_mfma_f32_16x16x16_f16   (the block substitution)
+ *   kind 3  v_mfma_f32_16x16x4_f32    (the per-key gate's wide diagonal blocks)
+ *   kind 4  v_mfma_f32_32x32x16_f16   (the larger fp16 tile, for comparison)
+ * and writes one float per thread to sink (device memory the caller owns, at
+ * least sink_floats = CUs * 8 * 256 floats): in thread 0 of each workgroup,
+ * sink[256 * workgroup], the shader clock in MHz over that workgroup's run
+ * (s_memtime cycles against the 100 MHz real-time counter); elsewhere a sum
+ * of the products, with no meaning.
+ * *flops_per_launch (host) receives the launch's flop count; timing it (for
+ * example with hipEvents on the same stream) gives the rate.  iters is
+ * 1..2^24.  Errors: GDR_ERR_INVALID_ARGUMENT (kind, iters, NULL pointers, a
+ * sink too small) before any launch, GDR_ERR_HIP from the runtime.
+ */
+gdr_status gdr_mfma_peak_probe(int32_t kind, int64_t iters, float *sink, int64_t sink_floats,
+                               double *flops_per_launch, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -217,3 +217,20 @@ def test_noalloc_prefill_rejects_sizes_beyond_its_scratch():
     assert ws_size(T, 1, 16, 32, 128)[1] <= scratch < ws_size(T, 1, 16, 32, 128, 1)[1]
     assert noalloc_call(T=T, B=1, gk=FAKE) == E.GDR_ERR_WORKSPACE
     assert b"per-key gate" in gdr.lib().gdr_last_error()
+
+
+def test_mfma_probe_rejects_bad_arguments_before_any_hip_call():
+    """The MFMA issue-rate probe checks its kind, iteration count and
+    pointers on the host first (none of these calls reaches the device)."""
+    lib = gdr.lib()
+    flops = ctypes.c_double(0.0)
+    E = gdr
+    assert lib.gdr_mfma_peak_probe(5, 100, FAKE, 1 << 30, ctypes.byref(flops), None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert b"kind" in lib.gdr_last_error()
+    assert lib.gdr_mfma_peak_probe(-1, 100, FAKE, 1 << 30, ctypes.byref(flops), None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert lib.gdr_mfma_peak_probe(0, 0, FAKE, 1 << 30, ctypes.byref(flops), None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert lib.gdr_mfma_peak_probe(0, (1 << 24) + 1, FAKE, 1 << 30, ctypes.byref(flops), None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert b"iterations" in lib.gdr_last_error()
+    assert lib.gdr_mfma_peak_probe(0, 100, None, 1 << 30, ctypes.byref(flops), None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert lib.gdr_mfma_peak_probe(0, 100, FAKE, 1 << 30, None, None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert len(gdr.PROBE_KINDS) == 5
