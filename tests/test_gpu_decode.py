@@ -221,3 +221,39 @@ def test_decode_one_token_out_of_range_slot():
     out_ref, pool_ref = run_oracle(ref)
     assert_out_close(out, out_ref, True, "S=1 oob out")
     assert_state_close(to_f64(pool[1]), pool_ref[1], "S=1 oob state slot 1")
+
+
+def _random_decode_case(seed):
+    """A seeded draw of the decode's shape and option space: 1-16 rows of
+    1-8 tokens, GQA groups of 1 or 2, both key sizes and every value size,
+    every activation and pool dtype and rule, the per-key gate with the
+    rules that decay, every slot routing, ragged lengths and accepted-token
+    counts; the pool kept under 8 M elements so that the fp64 oracle stays
+    quick."""
+    rng = np.random.default_rng(3000 + seed)
+    S = 1 if rng.random() < 0.3 else int(rng.integers(2, 9))   # one token per row has its own kernel
+    Nk = int(rng.choice([1, 2, 4]))
+    Nv = Nk * int(rng.choice([1, 2]))
+    Dk = int(rng.choice([64, 128]))
+    Dv = int(rng.choice([64, 128, 256, 512]))
+    act = str(rng.choice(["bf16", "fp16", "fp32"]))
+    state = str(rng.choice(["bf16", "fp16", "fp32"]))
+    rule = str(rng.choice(["gated_delta", "gated_delta", "delta", "gated", "linear"]))
+    with_gk = rule in ("gated_delta", "gated") and bool(rng.random() < 0.5)
+    lens = str(rng.choice(["full", "random"]))
+    routing = str(rng.choice(["one_slot", "two_slots", "per_token"]))
+    accepted = routing == "per_token" and bool(rng.random() < 0.5)
+    B = int(rng.integers(1, 17))
+    per_row = {"one_slot": 1, "two_slots": 2, "per_token": S}[routing]
+    while B > 1 and (B * per_row + 4) * Nv * Dk * Dv > 8 << 20:
+        B -= 1
+    num_slots = B * per_row + int(rng.integers(0, 5))
+    return dict(B=B, S=S, Nk=Nk, Nv=Nv, Dk=Dk, Dv=Dv, num_slots=num_slots, with_gk=with_gk, lens=lens,
+                routing=routing, act=act, state=state, accepted=accepted), rule
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_decode_random_cases(seed):
+    kw, rule = _random_decode_case(seed)
+    inp = workloads.decode_inputs(4000 + seed, **kw)
+    check_parity(inp, f"random case {seed}: {kw} rule {rule}", rule=rule)

@@ -398,3 +398,35 @@ def test_prefill_per_key_gate_any_magnitude(strength):
 def test_prefill_per_key_gate_reset_t8192():
     inp = workloads.prefill_inputs(67, [1000, 4096, 300, 2796], Nqk=16, Nv=32, act="bf16", gk="reset")
     check_parity(inp, "gk reset T=8192 varlen Nqk=16 Nv=32")
+
+
+def _random_case(seed):
+    """A seeded draw of the prefill's shape and option space: 1-6 sequences
+    whose lengths mix the chunk edges (0, 1, 127-129, 255-257) with random
+    ones, GQA groups of 1, 2 or 4, every activation dtype and rule, the
+    per-key gate in its ranges (with the rules that decay), with and without
+    an initial state, gates from nearly none to strong."""
+    rng = np.random.default_rng(1000 + seed)
+    B = int(rng.integers(1, 7))
+    edges = [0, 1, 2, 63, 64, 127, 128, 129, 255, 256, 257]
+    lens = [int(rng.choice(edges)) if rng.random() < 0.5 else int(rng.integers(1, 700)) for _ in range(B)]
+    if sum(lens) == 0:
+        lens[0] = 1
+    Nqk = int(rng.choice([1, 2, 4]))
+    Nv = Nqk * int(rng.choice([1, 2, 4]))
+    act = str(rng.choice(["bf16", "fp16", "fp32"]))
+    rule = str(rng.choice(["gated_delta", "gated_delta", "delta", "gated", "linear"]))
+    gk = None if rule in ("delta", "linear") else [None, None, "weak", "strong", "reset"][int(rng.integers(0, 5))]
+    init = str(rng.choice(["randn", "zeros"]))
+    g_lo = float(rng.choice([1e-6, 0.001, 0.01]))
+    g_range = (g_lo, g_lo * float(rng.choice([10.0, 100.0])))
+    return lens, Nqk, Nv, act, rule, gk, init, g_range
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_prefill_random_cases(seed):
+    lens, Nqk, Nv, act, rule, gk, init, g_range = _random_case(seed)
+    inp = workloads.prefill_inputs(2000 + seed, lens, Nqk=Nqk, Nv=Nv, act=act, init_state=init, gk=gk,
+                                   g_range=g_range)
+    check_parity(inp, f"random case {seed}: lens {lens} Nqk={Nqk} Nv={Nv} {act} rule {rule} gk {gk} "
+                      f"init {init} g=-U{g_range}", rule=rule)
