@@ -21,7 +21,8 @@
 //   chunkmap  one workgroup: cu_seqlens -> chunk table on the device.
 //   intra     K1, one workgroup (8 waves) per (chunk, value head): every step
 //             that does not depend on S -- norms, cumsum, decay, L, the
-//             triangular inverse, u and w.  Fully parallel over chunks.
+//             diagonal blocks of T, and u and w by block forward substitution
+//             (T itself is never formed).  Fully parallel over chunks.
 //   scan      K2, one workgroup (8 waves) per (sequence, value head, slice of
 //             DS state columns).  Columns of S are independent in every step,
 //             so the serial chunk loop is split over 128/DS workgroups.  S
