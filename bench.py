@@ -390,7 +390,39 @@ def stream_ceiling(torch):
         torch.cuda.synchronize()
         s = e0.elapsed_time(e1) / 1e3 / 20
         res[name] = {"GBps": 2 * n * 2 / s / 1e9, "hbm_frac": 2 * n * 2 / s / HBM_PEAK, "us_per_launch": s * 1e6}
+    del bufs, dst
+    res.update(slab_stream(torch))
     return {"stream_ceiling": res, "bytes_per_launch": 2 * n * 2}
+
+
+def slab_stream(torch):
+    """The one-token decode's memory traffic without its arithmetic
+    (gdr_slab_stream_probe) on the B=256 decode workload's pool shape: every
+    row's 128 x 128 bf16 slabs read and written back in place, with the
+    workload's seeded random slots and with row b in slot b; four pools
+    rotated, as the decode bench does."""
+    import gated_delta_rule_chunk_amd as gdr
+    import workloads
+    inp = workloads.config_inputs(3)
+    B, Nv, slots = inp["B"], inp["Nv"], inp["num_slots"]
+    pools = [inp["pool"].to("cuda:0")] + [inp["pool"].to("cuda:0") for _ in range(3)]
+    res = {}
+    for name, idx in (("decode_slabs_random_slots", inp["idx"][:B]),
+                      ("decode_slabs_slot_order", torch.arange(B, dtype=torch.int32))):
+        idx = idx.to(torch.int32).to("cuda:0")
+        nbytes = 2 * B * Nv * 128 * 128 * 2
+        for i in range(4):
+            gdr.slab_stream_probe(pools[i % 4], idx)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(40):
+            gdr.slab_stream_probe(pools[i % 4], idx)
+        e1.record()
+        torch.cuda.synchronize()
+        t = e0.elapsed_time(e1) / 1e3 / 40
+        res[name] = {"GBps": nbytes / t / 1e9, "hbm_frac": nbytes / t / HBM_PEAK, "us_per_launch": t * 1e6}
+    return res
 
 
 def mfma_peak(torch, gdr):

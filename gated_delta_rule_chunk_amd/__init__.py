@@ -62,6 +62,7 @@ SIGNATURES = {
                                        _i32]),
     "gdr_timing_kernel_name": (ctypes.c_char_p, [_i32]),
     "gdr_mfma_peak_probe": (ctypes.c_int, [_i32, _i64, _vp, _i64, ctypes.POINTER(ctypes.c_double), _vp]),
+    "gdr_slab_stream_probe": (ctypes.c_int, [_vp, _i32, _vp, _i32, _i32, _vp]),
 }
 # MFMA instruction of each probe kind (gdr_mfma_peak_probe)
 PROBE_KINDS = ("f16_16x16x32", "bf16_16x16x32", "f16_16x16x16", "f32_16x16x4", "f16_32x32x16")
@@ -167,6 +168,21 @@ def mfma_peak_probe(kind: str, iters: int, sink) -> float:
     check(lib().gdr_mfma_peak_probe(PROBE_KINDS.index(kind), int(iters), sink.data_ptr(), sink.numel(),
                                     ctypes.byref(flops), _stream(sink.device)), "gdr_mfma_peak_probe")
     return float(flops.value)
+
+
+def slab_stream_probe(pool, idx) -> None:
+    """Enqueue the slab-stream probe (see gdr.h) on pool's current stream: the
+    one-token decode's reads and in-place writes of pool[idx[b], h] for every
+    row b and head h, without its arithmetic (2 * 32 KiB per in-range row and
+    head).  pool is a bf16 or fp16 [slots, Nv, 128, 128] device tensor, idx
+    int32 [B] on the same device."""
+    if pool.dim() != 4 or tuple(pool.shape[2:]) != (128, 128) or pool.element_size() != 2:
+        raise ValueError(f"pool must be a 16-bit [slots, Nv, 128, 128] tensor (got {tuple(pool.shape)}, {pool.dtype})")
+    if idx.dtype != torch.int32 or idx.dim() != 1 or idx.device != pool.device:
+        raise ValueError("idx must be an int32 [B] tensor on the pool's device")
+    slots, Nv = pool.shape[0], pool.shape[1]
+    check(lib().gdr_slab_stream_probe(pool.data_ptr(), slots, idx.data_ptr(), idx.numel(), Nv,
+                                      _stream(pool.device)), "gdr_slab_stream_probe")
 
 
 def chunk_prefill_workspace_size(T: int, B: int, Nqk: int, Nv: int, D: int = 128, gk: bool = False) -> int:

@@ -284,4 +284,16 @@ gdr_status gdr_mfma_peak_probe(int32_t kind, int64_t iters, float* sink, int64_t
                     "probe launch");
 }
 
+gdr_status gdr_slab_stream_probe(void* pool, int32_t num_slots, const int32_t* ssm_state_indices, int32_t B,
+                                 int32_t Nv, void* hip_stream) {
+    if (!pool || !ssm_state_indices) return fail(GDR_ERR_INVALID_ARGUMENT, "pool and ssm_state_indices must not be NULL");
+    if (B < 1 || Nv < 1 || num_slots < 1)
+        return fail(GDR_ERR_INVALID_ARGUMENT, "B, Nv and num_slots must be >= 1 (B=%d, Nv=%d, num_slots=%d)", B, Nv,
+                    num_slots);
+    if ((int64_t)B * Nv > 0x7fffffffLL) return fail(GDR_ERR_INVALID_ARGUMENT, "B * Nv must be < 2^31");
+    return from_hip(gdr::slab_stream_launch(static_cast<uint16_t*>(pool), num_slots, ssm_state_indices, B, Nv,
+                                            static_cast<hipStream_t>(hip_stream)),
+                    "probe launch");
+}
+
 }  // extern "C"

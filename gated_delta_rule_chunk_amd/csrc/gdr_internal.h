@@ -27,6 +27,11 @@ constexpr int kProbeChains[kProbeKinds] = {8, 8, 8, 8, 4};
 constexpr double kProbeFlops[kProbeKinds] = {16.0 * 16 * 32 * 2, 16.0 * 16 * 32 * 2, 16.0 * 16 * 16 * 2,
                                              16.0 * 16 * 4 * 2, 32.0 * 32 * 16 * 2};
 hipError_t mfma_probe_launch(int kind, int64_t iters, float* sink, int grid, hipStream_t stream);
+// The slab-stream probe (gdr_slab_stream_probe): one 16-bit 128 x 128 slab
+// per (row, head) workgroup, read and written back in place, in the
+// one-token decode's workgroup order and access pattern.
+hipError_t slab_stream_launch(uint16_t* pool, int32_t num_slots, const int32_t* idx, int32_t B, int32_t Nv,
+                              hipStream_t stream);
 
 struct DecodeArgs {
     const void* q;

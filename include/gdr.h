@@ -298,6 +298,20 @@ const char *gdr_timing_kernel_name(int32_t id);
 gdr_status gdr_mfma_peak_probe(int32_t kind, int64_t iters, float *sink, int64_t sink_floats,
                                double *flops_per_launch, void *hip_stream);
 
+/* gdr_slab_stream_probe -- the memory traffic of the one-token decode alone,
+ * for the HBM ceiling of its access pattern: enqueues on hip_stream one
+ * workgroup per (row b < B, value head h < Nv) that reads the 16-bit
+ * 128 x 128 slab state_pool[ssm_state_indices[b], h] (a pool of num_slots x
+ * Nv such slabs, bf16 or fp16, device memory) and writes the same bytes back,
+ * with the decode's thread layout, workgroup order and non-temporal 16-byte
+ * accesses; rows whose index is outside [0, num_slots) are skipped.  The
+ * pool's values do not change.  ssm_state_indices is int32 [B] on the device.
+ * Errors: GDR_ERR_INVALID_ARGUMENT (NULL pointers, sizes below 1) before any
+ * launch, GDR_ERR_HIP from the runtime.
+ */
+gdr_status gdr_slab_stream_probe(void *state_pool, int32_t num_slots, const int32_t *ssm_state_indices, int32_t B,
+                                 int32_t Nv, void *hip_stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -234,3 +234,13 @@ def test_mfma_probe_rejects_bad_arguments_before_any_hip_call():
     assert lib.gdr_mfma_peak_probe(0, 100, None, 1 << 30, ctypes.byref(flops), None) == E.GDR_ERR_INVALID_ARGUMENT
     assert lib.gdr_mfma_peak_probe(0, 100, FAKE, 1 << 30, None, None) == E.GDR_ERR_INVALID_ARGUMENT
     assert len(gdr.PROBE_KINDS) == 5
+
+
+def test_slab_stream_probe_rejects_bad_arguments_before_any_hip_call():
+    lib = gdr.lib()
+    E = gdr
+    assert lib.gdr_slab_stream_probe(None, 4, FAKE, 2, 2, None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert lib.gdr_slab_stream_probe(FAKE, 4, None, 2, 2, None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert lib.gdr_slab_stream_probe(FAKE, 4, FAKE, 0, 2, None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert lib.gdr_slab_stream_probe(FAKE, 0, FAKE, 2, 2, None) == E.GDR_ERR_INVALID_ARGUMENT
+    assert b"num_slots" in lib.gdr_last_error()
