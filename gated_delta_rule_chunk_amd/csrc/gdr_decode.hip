@@ -386,9 +386,17 @@ static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
 template <int DK, typename ActT, typename StT>
 static hipError_t launch_dv(const DecodeArgs& a, hipStream_t stream) {
     // column slices: all of Dv up to 128; 256-column slices for wider states,
-    // which keeps 32 KiB of bf16 slab in flight per workgroup when Dk = 64
+    // which keeps 32 KiB of bf16 slab in flight per workgroup when Dk = 64.
+    // The one-token kernel with a 16-bit pool takes 64-column slices at
+    // Dv = 128: each row piece is still one whole 128-byte line, the kernel
+    // needs 78 registers instead of 113, and six workgroups share a CU instead
+    // of four (B = 256 workload: 96.1 against 98.0 us per call, same box;
+    // 32-column slices, half a line per row piece, took 138.9 us).
     if (a.Dv == 64) return launch<DK, 64, ActT, StT>(a, stream);
-    if (a.Dv == 128) return launch<DK, 128, ActT, StT>(a, stream);
+    if (a.Dv == 128) {
+        if (sizeof(StT) == 2 && a.S == 1) return launch<DK, 64, ActT, StT>(a, stream);
+        return launch<DK, 128, ActT, StT>(a, stream);
+    }
     return launch<DK, 256, ActT, StT>(a, stream);
 }
 

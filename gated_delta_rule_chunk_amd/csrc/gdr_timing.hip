@@ -148,23 +148,26 @@ __global__ __launch_bounds__(256) void mfma_rate_kernel(int64_t iters, float* si
 }  // namespace
 
 // ------------------------------------------------------------------ slab-stream probe
-// The one-token decode's memory traffic alone: workgroup (row b, head h),
-// placed as the decode places it (place_slab), streams the 16-bit 128 x 128
-// slab of slot idx[b], head h, with the decode's thread layout (16 lanes per
-// 128-column row, 16 rows a pass, 8 passes) and its non-temporal 16-byte
-// loads, then writes the same bytes back with non-temporal stores.  Slots
-// outside [0, num_slots) are skipped.
+// The one-token decode's memory traffic alone: workgroup (row b, head h,
+// 64-column half), placed as the decode places it (place_slab), streams its
+// half of the 16-bit 128 x 128 slab of slot idx[b], head h, with the decode's
+// thread layout (8 lanes per 64-column row piece, 32 rows a pass, 4 passes)
+// and its non-temporal 16-byte loads, then writes the same bytes back with
+// non-temporal stores.  Slots outside [0, num_slots) are skipped.  The decode
+// fits six workgroups on a CU (its registers); the probe needs far fewer
+// registers, so its launch reserves 24 KiB of LDS per workgroup (unused) to
+// hold it to the same six.
 namespace {
 typedef uint32_t probe_u4 __attribute__((ext_vector_type(4)));
 
 __global__ __launch_bounds__(256, 4) void slab_stream_kernel(uint16_t* pool, int32_t num_slots, const int32_t* idx,
                                                              int32_t B, int32_t Nv) {
-    constexpr int D = 128, LPR = 16, RP = 16, RPT = 8;
+    constexpr int D = 128, CW = 64, LPR = 8, RP = 32, RPT = 4;
     int b, h, slice;
-    place_slab(blockIdx.x, B, Nv, 1, b, h, slice);
+    place_slab(blockIdx.x, B, Nv, D / CW, b, h, slice);
     const int slot = idx[b];
     if (slot < 0 || slot >= num_slots) return;
-    const int tid = threadIdx.x, col = (tid % LPR) * 8, rg = tid / LPR;
+    const int tid = threadIdx.x, col = slice * CW + (tid % LPR) * 8, rg = tid / LPR;
     uint16_t* base = pool + ((size_t)slot * Nv + h) * D * D + col;
     probe_u4 raw[RPT];
 #pragma unroll
@@ -182,8 +185,8 @@ __global__ __launch_bounds__(256, 4) void slab_stream_kernel(uint16_t* pool, int
 
 hipError_t slab_stream_launch(uint16_t* pool, int32_t num_slots, const int32_t* idx, int32_t B, int32_t Nv,
                               hipStream_t stream) {
-    hipLaunchKernelGGL(slab_stream_kernel, dim3((unsigned)((int64_t)B * Nv)), dim3(256), 0, stream, pool, num_slots,
-                       idx, B, Nv);
+    hipLaunchKernelGGL(slab_stream_kernel, dim3((unsigned)((int64_t)B * Nv * 2)), dim3(256), 24 * 1024, stream, pool,
+                       num_slots, idx, B, Nv);
     return hipGetLastError();
 }
 

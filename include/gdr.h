@@ -299,12 +299,13 @@ gdr_status gdr_mfma_peak_probe(int32_t kind, int64_t iters, float *sink, int64_t
                                double *flops_per_launch, void *hip_stream);
 
 /* gdr_slab_stream_probe -- the memory traffic of the one-token decode alone,
- * for the HBM ceiling of its access pattern: enqueues on hip_stream one
- * workgroup per (row b < B, value head h < Nv) that reads the 16-bit
- * 128 x 128 slab state_pool[ssm_state_indices[b], h] (a pool of num_slots x
- * Nv such slabs, bf16 or fp16, device memory) and writes the same bytes back,
- * with the decode's thread layout, workgroup order and non-temporal 16-byte
- * accesses; rows whose index is outside [0, num_slots) are skipped.  The
+ * for the HBM ceiling of its access pattern: enqueues on hip_stream two
+ * workgroups per (row b < B, value head h < Nv), one per 64-column half,
+ * that read the 16-bit 128 x 128 slab state_pool[ssm_state_indices[b], h] (a
+ * pool of num_slots x Nv such slabs, bf16 or fp16, device memory) and write
+ * the same bytes back, with the decode's thread layout, workgroup order and
+ * non-temporal 16-byte accesses; rows whose index is outside [0, num_slots)
+ * are skipped.  The
  * pool's values do not change.  ssm_state_indices is int32 [B] on the device.
  * Errors: GDR_ERR_INVALID_ARGUMENT (NULL pointers, sizes below 1) before any
  * launch, GDR_ERR_HIP from the runtime.
