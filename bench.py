@@ -154,12 +154,19 @@ def counter_mfma(kernel):
     return rec.get("mfma_flops_per_launch"), rec.get("mfma_busy_frac")
 
 
-def timed(fn, steps, warmup, gdr, torch):
+def timed(fn, steps, warmup, gdr, torch, whole_region=False):
     """Warm up; take the per-kernel breakdown in an untimed pass with every
     kernel's events; then time `steps` steps with events around the dominant
     kernel (the most time per call) only.  Returns (seconds, breakdown
     {name: (ms per call, launches per call)}, dominant name, its (ms per
-    call, launches per call) over the timed region)."""
+    call, launches per call) over the timed region).
+
+    whole_region: for a step that is one launch of one kernel (the decode),
+    one event pair on the launch stream brackets the whole timed region
+    instead of a pair per launch; a pair per launch adds its own few
+    microseconds to each launch it brackets, which shows against a kernel of
+    about 100 us (rocprofv3's kernel trace agrees with the whole-region
+    average, not with the per-launch one)."""
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -172,6 +179,19 @@ def timed(fn, steps, warmup, gdr, torch):
     gdr.timing_enable(False)
     breakdown = {k: (v[0] / probe, v[1] / probe) for k, v in gdr.timing_read().items() if v[1]}
     dominant = max(breakdown, key=lambda k: breakdown[k][0])
+    if whole_region:
+        if len(breakdown) != 1 or breakdown[dominant][1] != 1:
+            raise RuntimeError(f"whole-region timing needs one launch of one kernel per step, got {breakdown}")
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        for i in range(steps):
+            fn(warmup + probe + i)
+        e1.record()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        return dt, breakdown, dominant, (e0.elapsed_time(e1) / steps, 1.0)
     gdr.timing_enable(True, kernels=[dominant])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -269,7 +289,7 @@ def bench_decode(args, gdr, torch, workloads):
                              s["lens"], s["scale"], out=out)
 
     steps = max(args.steps * 4, 20)
-    dt, per, _, live = timed(step, steps, args.warmup, gdr, torch)
+    dt, per, _, live = timed(step, steps, args.warmup, gdr, torch, whole_region=True)
     # reference: a plain device copy moving the same number of bytes (half read, half written)
     nb_copy = (bytes_decode(inp) // 2 + 255) // 256 * 256
     src = torch.empty(nb_copy, dtype=torch.uint8, device=dev).fill_(1)
