@@ -171,7 +171,13 @@ def timed(fn, steps, warmup, gdr, torch, whole_region=False):
         fn(i)
     torch.cuda.synchronize()
     gdr.timing_read()            # discard warm-up records
-    probe = max(3, min(steps, 10))
+    # The breakdown pass runs 100 steps (at least 20 ms of the T=8192 prefill,
+    # whatever `steps` is).  Besides averaging the per-kernel times over more
+    # launches, it puts the timed region after the part has settled under the
+    # workload's load: a cold process ran its first 50 prefill steps at 257 us
+    # each and was at 186-190 us from about the 100th (one box), and 50 steps
+    # after a pause of a second ran at 216-220 us.
+    probe = 100
     gdr.timing_enable(True)
     for i in range(probe):
         fn(warmup + i)
@@ -613,6 +619,9 @@ def main():
                         contiguous_slots=bool(args.decode_contiguous_slots))
         print(json.dumps(line))
         return
+    # the ceilings measured on this GPU (plain HBM streams, dense MFMA issue
+    # rates), taken before the timed workloads
+    ceilings = {"hbm": stream_ceiling(torch)["stream_ceiling"], "mfma": mfma_peak(torch, gdr)}
     pre = bench_prefill(args, gdr, torch, workloads)
     dec = bench_decode(args, gdr, torch, workloads)
     inp = pre["inp"]
@@ -642,8 +651,7 @@ def main():
     }
     # the ceilings measured on this GPU, beside the published peaks the
     # roofline objects use: dense MFMA issue rates and plain HBM streams
-    line["measured_ceilings"] = {"mfma": mfma_peak(torch, gdr),
-                                 "hbm": stream_ceiling(torch)["stream_ceiling"]}
+    line["measured_ceilings"] = ceilings
     if not args.no_configs:
         # the other configured workloads (the T=8192 prefill and the B=256
         # decode are the entries above) and the extra ones, each timed on its

@@ -368,18 +368,15 @@ __global__ __launch_bounds__(256, DK * CW <= 128 * 128 ? 4 : 2) void decode1_ker
 template <int DK, int CW, typename ActT, typename StT>
 static hipError_t launch(const DecodeArgs& a, hipStream_t stream) {
     const size_t nwg = (size_t)a.B * a.Nv * (a.Dv / CW);
-    timing_begin(kDecode, stream);
     if constexpr (sizeof(StT) == 2) {
         if (a.S == 1) {
-            if (a.rule == 0) hipLaunchKernelGGL((decode1_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
-            else hipLaunchKernelGGL((decode1_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
-            timing_end(kDecode, stream);
+            if (a.rule == 0) GDR_LAUNCH(kDecode, (decode1_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+            else GDR_LAUNCH(kDecode, (decode1_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
             return hipGetLastError();
         }
     }
-    if (a.rule == 0) hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
-    else hipLaunchKernelGGL((decode_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
-    timing_end(kDecode, stream);
+    if (a.rule == 0) GDR_LAUNCH(kDecode, (decode_kernel<DK, CW, ActT, StT, false>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
+    else GDR_LAUNCH(kDecode, (decode_kernel<DK, CW, ActT, StT, true>), dim3((unsigned)nwg), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -2,6 +2,7 @@
 // kernel launchers (not part of the public ABI).
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -14,9 +15,23 @@ constexpr int kHeadDim = 128;         // D, fixed by the prefill page
 
 // Kernel ids for the opt-in per-kernel timing (gdr_timing_*).
 enum KernelId { kChunkmap = 0, kIntra = 1, kScan = 2, kOutput = 3, kDecode = 4, kKernelCount = 5 };
-void timing_begin(int id, hipStream_t s);
-void timing_end(int id, hipStream_t s);
+// When kernel id is selected for timing: two events for one launch of it,
+// already recorded as that launch's pair (true); false otherwise.
+bool timing_events(int id, hipEvent_t* start, hipEvent_t* stop);
 const char* kernel_name(int id);
+
+// Launch KERNEL on STREAM.  A launch of a kernel selected for timing goes
+// through hipExtLaunchKernelGGL, whose start and stop events the dispatch
+// itself records at the kernel's start and end: no marker packets beside the
+// kernel, so timing adds nothing to the stream between launches.
+#define GDR_LAUNCH(ID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                          \
+    do {                                                                                                \
+        hipEvent_t gdr_t0_, gdr_t1_;                                                                    \
+        if (::gdr::timing_events((ID), &gdr_t0_, &gdr_t1_))                                             \
+            hipExtLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, gdr_t0_, gdr_t1_, 0u, __VA_ARGS__); \
+        else                                                                                            \
+            hipLaunchKernelGGL(KERNEL, GRID, BLOCK, SHMEM, STREAM, __VA_ARGS__);                         \
+    } while (0)
 
 // The MFMA issue-rate probe (gdr_mfma_peak_probe): kinds, flops per
 // instruction, and one launch of `grid` workgroups of four waves.

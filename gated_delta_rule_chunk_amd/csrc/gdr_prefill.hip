@@ -2374,28 +2374,28 @@ static int compute_units() {
 
 template <int RULE>
 static void launch_intra_rule(int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
-    if (act == kActBf16) hipLaunchKernelGGL((intra_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
-    else if (act == kActFp16) hipLaunchKernelGGL((intra_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((intra_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
+    if (act == kActBf16) GDR_LAUNCH(kIntra, (intra_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
+    else if (act == kActFp16) GDR_LAUNCH(kIntra, (intra_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
+    else GDR_LAUNCH(kIntra, (intra_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
 }
 template <int RULE>
 static void launch_intra_gk_rule(int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
-    if (act == kActBf16) hipLaunchKernelGGL((intra_gk_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
-    else if (act == kActFp16) hipLaunchKernelGGL((intra_gk_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((intra_gk_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
+    if (act == kActBf16) GDR_LAUNCH(kIntra, (intra_gk_kernel<uint16_t, RULE>), grid, dim3(512), 0, stream, p);
+    else if (act == kActFp16) GDR_LAUNCH(kIntra, (intra_gk_kernel<_Float16, RULE>), grid, dim3(512), 0, stream, p);
+    else GDR_LAUNCH(kIntra, (intra_gk_kernel<float, RULE>), grid, dim3(512), 0, stream, p);
 }
 // The scan launch for a slice width, one- or two-level pass, with or without the per-key gate.
 template <int DS, int MODE>
 static void launch_scan(bool gk, dim3 grid, hipStream_t stream, const PrefillDev& p) {
-    if (gk) hipLaunchKernelGGL((scan_kernel<DS, MODE, true>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((scan_kernel<DS, MODE, false>), grid, dim3(512), 0, stream, p);
+    if (gk) GDR_LAUNCH(kScan, (scan_kernel<DS, MODE, true>), grid, dim3(512), 0, stream, p);
+    else GDR_LAUNCH(kScan, (scan_kernel<DS, MODE, false>), grid, dim3(512), 0, stream, p);
 }
 // The per-key-gate scan with the output fused in, for a slice width.
 template <int DS>
 static void launch_scan_gk_out(int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
-    if (act == kActBf16) hipLaunchKernelGGL((scan_gk_out_kernel<DS, uint16_t>), grid, dim3(512), 0, stream, p);
-    else if (act == kActFp16) hipLaunchKernelGGL((scan_gk_out_kernel<DS, _Float16>), grid, dim3(512), 0, stream, p);
-    else hipLaunchKernelGGL((scan_gk_out_kernel<DS, float>), grid, dim3(512), 0, stream, p);
+    if (act == kActBf16) GDR_LAUNCH(kScan, (scan_gk_out_kernel<DS, uint16_t>), grid, dim3(512), 0, stream, p);
+    else if (act == kActFp16) GDR_LAUNCH(kScan, (scan_gk_out_kernel<DS, _Float16>), grid, dim3(512), 0, stream, p);
+    else GDR_LAUNCH(kScan, (scan_gk_out_kernel<DS, float>), grid, dim3(512), 0, stream, p);
 }
 static void launch_intra(int rule, int act, dim3 grid, hipStream_t stream, const PrefillDev& p) {
     switch (rule) {
@@ -2432,14 +2432,11 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     p.map_in_intra = (nwg > 0 && a.B <= kMapSeqs) ? 1 : 0;
     hipError_t e = hipSuccess;
     if (!p.map_in_intra) {
-        timing_begin(kChunkmap, stream);
-        hipLaunchKernelGGL(chunkmap_kernel, dim3(1), dim3(256), 0, stream, a.cu, p);
-        timing_end(kChunkmap, stream);
+        GDR_LAUNCH(kChunkmap, chunkmap_kernel, dim3(1), dim3(256), 0, stream, a.cu, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (nwg > 0) {
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
-        timing_begin(kIntra, stream);
         if (gk) {
             // persistent: one workgroup per CU (LDS about 157 KiB), each walking items
             const dim3 grid((unsigned)(((nwg < (size_t)ncu ? nwg : (size_t)ncu) + g8 - 1) / g8 * g8));
@@ -2450,7 +2447,6 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
             const size_t nint = ((nwg < (size_t)2 * ncu ? nwg : (size_t)2 * ncu) + g8 - 1) / g8 * g8;
             launch_intra(a.rule, act, dim3((unsigned)nint), stream, p);
         }
-        timing_end(kIntra, stream);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // State columns are split over NS = 128 / DS workgroups per (sequence,
@@ -2461,14 +2457,13 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
     // every (sequence, segment) pair of the bound; absent segments exit.
     const size_t G = (size_t)(a.Nv / a.Nqk);
     const size_t ngroup = ((size_t)a.B * lay.nseg * a.Nqk + 7) / 8 * 8;
-    timing_begin(kScan, stream);
     if (lay.nseg > 1) {
         // first level: the maps of all segments but each sequence's last
         launch_scan<128, 1>(gk, dim3((unsigned)(ngroup * G * 2)), stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         // second level: the segments' start states
-        hipLaunchKernelGGL(combine_kernel, dim3((unsigned)((size_t)a.B * a.Nv * (128 / kCombineCols))),
-                           dim3(512), 0, stream, p);
+        GDR_LAUNCH(kScan, combine_kernel, dim3((unsigned)((size_t)a.B * a.Nv * (128 / kCombineCols))), dim3(512), 0,
+                   stream, p);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     // (segments have equal lengths, so there their slices are sized to fit
@@ -2496,23 +2491,20 @@ hipError_t prefill_launch(const PrefillArgs& a, const PrefillLayout& lay, int ac
             default: launch_scan<16, 0>(gk, dim3((unsigned)nscan), stream, p); break;
         }
     }
-    timing_end(kScan, stream);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (nwg > 0 && !fused) {
-        timing_begin(kOutput, stream);
         const size_t g8 = (size_t)8 * (a.Nv / a.Nqk);
         const unsigned nout = (unsigned)((nwg + g8 - 1) / g8 * g8);
         if (gk) {
-            if (act == kActBf16) hipLaunchKernelGGL(output_gk_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+            if (act == kActBf16) GDR_LAUNCH(kOutput, output_gk_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
             else if (act == kActFp16)
-                hipLaunchKernelGGL(output_gk_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL(output_gk_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
+                GDR_LAUNCH(kOutput, output_gk_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
+            else GDR_LAUNCH(kOutput, output_gk_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
         } else {
-            if (act == kActBf16) hipLaunchKernelGGL(output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
-            else if (act == kActFp16) hipLaunchKernelGGL(output_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
-            else hipLaunchKernelGGL(output_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
+            if (act == kActBf16) GDR_LAUNCH(kOutput, output_kernel<uint16_t>, dim3(nout), dim3(512), 0, stream, p);
+            else if (act == kActFp16) GDR_LAUNCH(kOutput, output_kernel<_Float16>, dim3(nout), dim3(512), 0, stream, p);
+            else GDR_LAUNCH(kOutput, output_kernel<float>, dim3(nout), dim3(512), 0, stream, p);
         }
-        timing_end(kOutput, stream);
         e = hipGetLastError();
     }
     return e;

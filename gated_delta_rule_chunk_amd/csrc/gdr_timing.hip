@@ -1,11 +1,13 @@
 // gdr_timing.hip -- opt-in per-kernel timing with HIP events.
 //
-// For the kernels selected by gdr_timing_enable's mask, every launch is
-// bracketed by two hipEvents recorded on the same stream, so the durations
-// measured are those of the kernels as they run in the caller's sequence.
-// gdr_timing_read waits for the recorded events, returns the summed
-// durations and launch counts per kernel, and forgets them.  Disabled (the
-// default), the hooks cost one relaxed atomic load per launch.
+// For the kernels selected by gdr_timing_enable's mask, every launch goes
+// through hipExtLaunchKernelGGL with two events that the dispatch records at
+// the kernel's start and end (GDR_LAUNCH), so the durations measured are
+// those of the kernels as they run in the caller's sequence, and no event
+// packet sits between them.  gdr_timing_read waits for the recorded events,
+// returns the summed durations and launch counts per kernel, and forgets
+// them.  Disabled (the default), the hooks cost one relaxed atomic load per
+// launch.
 //
 // It also holds the MFMA issue-rate probe behind gdr_mfma_peak_probe: the
 // dense rate of each MFMA kind the kernels use, measured on the part for the
@@ -29,7 +31,6 @@ std::atomic<int> g_mask{0};
 std::mutex g_mu;
 std::vector<Rec> g_recs;            // launches recorded since the last read
 std::vector<hipEvent_t> g_free;     // events ready for reuse
-thread_local hipEvent_t t_open[kKernelCount] = {};
 
 hipEvent_t take_event() {
     hipEvent_t e = nullptr;
@@ -52,20 +53,19 @@ const char* kernel_name(int id) {
     return (id >= 0 && id < kKernelCount) ? names[id] : "";
 }
 
-void timing_begin(int id, hipStream_t s) {
-    if (!((g_mask.load(std::memory_order_relaxed) >> id) & 1)) return;
-    hipEvent_t e = take_event();
-    if (e && hipEventRecord(e, s) == hipSuccess) t_open[id] = e;
-}
-
-void timing_end(int id, hipStream_t s) {
-    hipEvent_t b = t_open[id];
-    if (!b) return;
-    t_open[id] = nullptr;
-    hipEvent_t e = take_event();
-    if (!e || hipEventRecord(e, s) != hipSuccess) return;
+bool timing_events(int id, hipEvent_t* start, hipEvent_t* stop) {
+    if (!((g_mask.load(std::memory_order_relaxed) >> id) & 1)) return false;
+    hipEvent_t b = take_event(), e = take_event();
     std::lock_guard<std::mutex> lk(g_mu);
+    if (!b || !e) {   // no event to be had: this launch goes untimed
+        if (b) g_free.push_back(b);
+        if (e) g_free.push_back(e);
+        return false;
+    }
     g_recs.push_back(Rec{id, b, e});
+    *start = b;
+    *stop = e;
+    return true;
 }
 
 // ------------------------------------------------------------------ MFMA issue-rate probe

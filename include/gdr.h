@@ -259,8 +259,8 @@ gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, con
  * Opt-in per-kernel timing, for benchmarks and profiling.  gdr_timing_enable
  * takes a bit mask of kernel ids (bit i for kernel i; GDR_TIMING_ALL for
  * every kernel, 0 to switch timing off).  Every launch of a selected kernel
- * is bracketed by two hipEvents recorded on the caller's stream (each pair
- * adds a few microseconds to the stream, so time only the kernels needed).
+ * goes through hipExtLaunchKernelGGL with two hipEvents that its dispatch on
+ * the caller's stream records at the kernel's start and end.
  * gdr_timing_read waits for those events, writes for each kernel id i < n the
  * summed duration total_ms[i] and the number of launches launches[i]
  * recorded since the previous read, and forgets them.  Kernel ids:
