@@ -22,8 +22,9 @@ const char* kernel_name(int id);
 
 // Launch KERNEL on STREAM.  A launch of a kernel selected for timing goes
 // through hipExtLaunchKernelGGL, whose start and stop events the dispatch
-// itself records at the kernel's start and end: no marker packets beside the
-// kernel, so timing adds nothing to the stream between launches.
+// itself records at the kernel's start and end (no marker packets beside the
+// kernel).  A timed launch still costs the stream a few microseconds (about
+// 5 us per step of the T=8192 prefill), so time only the kernels needed.
 #define GDR_LAUNCH(ID, KERNEL, GRID, BLOCK, SHMEM, STREAM, ...)                                          \
     do {                                                                                                \
         hipEvent_t gdr_t0_, gdr_t1_;                                                                    \
@@ -78,9 +79,10 @@ hipError_t decode_launch(const DecodeArgs& a, int act, int state, hipStream_t st
 // hardware hands workgroup ids to the eight XCDs in turn (id mod 8), so each
 // row's slot, one contiguous region of Nv slabs, is streamed through one
 // XCD, and each XCD walks its rows' slots one after another.  Measured on the
-// B = 256 workload (random slots) against one row after another with its
-// slabs spread over all XCDs: 97.7 against 102.6 us per call, same box;
-// groups of 2, 4 and 16 rows gave 101.6, 100.5 and 99.2 us.  A last group of
+// B = 256 workload (random slots, whole 128-column slabs) against one row
+// after another with its slabs spread over all XCDs: 97.7 against 102.6 us
+// per call, same box; groups of 2, 4 and 16 rows gave 101.6, 100.5 and
+// 99.2 us.  A last group of
 // fewer than eight rows (B not a multiple of 8) keeps the same order with
 // its own row count.
 __device__ __forceinline__ void place_slab(int wg, int B, int Nv, int nslice, int& b, int& h, int& slice) {

@@ -4,7 +4,8 @@
 // through hipExtLaunchKernelGGL with two events that the dispatch records at
 // the kernel's start and end (GDR_LAUNCH), so the durations measured are
 // those of the kernels as they run in the caller's sequence, and no event
-// packet sits between them.  gdr_timing_read waits for the recorded events,
+// packet sits between them (a timed launch still costs the stream a few
+// microseconds).  gdr_timing_read waits for the recorded events,
 // returns the summed durations and launch counts per kernel, and forgets
 // them.  Disabled (the default), the hooks cost one relaxed atomic load per
 // launch.

@@ -260,7 +260,9 @@ gdr_status gdr_recurrent_decode(const void *q, const void *k, const void *v, con
  * takes a bit mask of kernel ids (bit i for kernel i; GDR_TIMING_ALL for
  * every kernel, 0 to switch timing off).  Every launch of a selected kernel
  * goes through hipExtLaunchKernelGGL with two hipEvents that its dispatch on
- * the caller's stream records at the kernel's start and end.
+ * the caller's stream records at the kernel's start and end (a timed launch
+ * still adds a few microseconds to the stream, so time only the kernels
+ * needed).
  * gdr_timing_read waits for those events, writes for each kernel id i < n the
  * summed duration total_ms[i] and the number of launches launches[i]
  * recorded since the previous read, and forgets them.  Kernel ids:
