@@ -207,6 +207,21 @@ def test_decode_one_token_per_row(rule, state, Dk, Dv):
     check_parity(inp, f"S=1 rule {rule} {state} pool Dk={Dk} Dv={Dv}", rule=rule)
 
 
+def test_decode_one_token_rows_in_groups_of_eight_with_a_short_last_group():
+    """S = 1 with a 16-bit pool: the kernel takes its rows in groups of eight
+    (one row per XCD) and each head's slab in two 64-column halves.  1001
+    rows are 125 whole groups and a last group of one; every row's slot is a
+    distinct random one of 1200, and a few rows carry no token."""
+    inp = workloads.decode_inputs(121, B=1001, S=1, Nk=2, Nv=4, Dk=128, Dv=128, num_slots=1200)
+    lens = inp["lens"].clone()
+    idx = inp["idx"].clone()
+    for b in (0, 7, 8, 999, 1000):
+        lens[b] = 0
+        idx[b] = -1
+    inp.update(lens=lens, idx=idx)
+    check_parity(inp, "S=1 bf16 pool B=1001 Nv=4 Dk=Dv=128")
+
+
 def test_decode_one_token_out_of_range_slot():
     """S = 1: a row whose slot lies outside the pool starts from zeros and
     stores nothing."""
