@@ -354,6 +354,19 @@ __device__ __forceinline__ void raw_cvt(const Raw4<_Float16>& x, float (&y)[4]) 
     for (int i = 0; i < 4; ++i) y[i] = (float)h[i];
 }
 __device__ __forceinline__ void raw_load(Raw4<float>& x, const float* p) { x.d = *reinterpret_cast<const f32x4*>(p); }
+// Non-temporal (streaming) forms, for rows read exactly once in the whole
+// call (an item's v rows): they do not displace from the caches the rows that
+// two value heads or several scan slices share.
+__device__ __forceinline__ void raw_load_nt(Raw8<uint16_t>& x, const uint16_t* p) {
+    x.d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void raw_load_nt(Raw8<_Float16>& x, const _Float16* p) {
+    x.d = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void raw_load_nt(Raw8<float>& x, const float* p) {
+    x.a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    x.b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4));
+}
 __device__ __forceinline__ void raw_zero(Raw8<uint16_t>& x) { x.d = u32x4{0u, 0u, 0u, 0u}; }
 __device__ __forceinline__ void raw_zero(Raw8<float>& x) { x.a = f32x4{0.f, 0.f, 0.f, 0.f}; x.b = x.a; }
 __device__ __forceinline__ void raw_zero(Raw4<uint16_t>& x) { x.d = u32x2{0u, 0u}; }
@@ -584,7 +597,7 @@ __device__ __forceinline__ void intra_item(IntraStage<ActT>& st, int next, const
 #pragma unroll
         for (int i = i0 / 2; i < i0 / 2 + 2; ++i) {
             const int row = min(4 * tq + i, max(r - 1, 0));
-            raw_load(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 8 * c8);
+            raw_load_nt(vr[i], V + ((size_t)(t0 + row) * Nv + h) * 128 + 8 * c8);
         }
     };
     // where the next item lies, looked up now: its loads go out in steps 5 and 6
@@ -1940,10 +1953,16 @@ __global__ __launch_bounds__(512) void combine_kernel(PrefillDev p) {
 // keys are normalised here from the input rows (each wave its own 16 rows);
 // the S_c / v_new pair is fetched into registers up front, while k^ is in use.
 // The pair is fetched in storage order: 16 B per lane, 1 KiB contiguous per
-// wave; piece e holds the 4-row runs of S_c and of v_new at lane run e.
+// wave; piece e holds the 4-row runs of S_c and of v_new at lane run e.  Each
+// pair is read once, so the loads are non-temporal: together with the intra
+// kernel's v rows (also read once) that took the T=8192 call from 190.4 to
+// 183.8 us (same box; T=131072 unchanged); the same hint on rows that two
+// value heads or several scan slices share (q, k; the scan's w and u) made
+// the call slower (193-210 us).
 __device__ __forceinline__ void pair_tile_fetch(u32x4 (&rg)[8], const _Float16* src, int tid) {
 #pragma unroll
-    for (int n = 0; n < 8; ++n) rg[n] = *reinterpret_cast<const u32x4*>(src + (size_t)(tid + 512 * n) * 8);
+    for (int n = 0; n < 8; ++n)
+        rg[n] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + (size_t)(tid + 512 * n) * 8));
 }
 // One tile of the pair (HALF 0: S_c, 1: v_new), X [row][col], placed
 // transposed in LDS, X^T [col][row].
