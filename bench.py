@@ -361,6 +361,21 @@ def time_config(n, args, gdr, torch, workloads):
     return rec
 
 
+def host_cpu():
+    """The host's CPU model (first "model name" of /proc/cpuinfo) and the
+    logical CPUs this process may run on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": len(os.sched_getaffinity(0))}
+
+
 def cpu_baseline_prefill(inp):
     """The oracle on the whole workload; inputs are widened to fp64 before
     the clock starts, so only the oracle call is timed."""
@@ -371,7 +386,7 @@ def cpu_baseline_prefill(inp):
     dt = time.perf_counter() - t0
     return {"value": inp["T"] / dt, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"one fp64 oracle call on the whole workload (T={inp['T']}, all {inp['Nv']} value "
-                      f"heads; inputs widened to fp64 before timing): {dt:.2f} s wall"}
+                      f"heads; inputs widened to fp64 before timing): {dt:.2f} s wall", **host_cpu()}
 
 
 def cpu_baseline_decode(inp):
@@ -387,7 +402,7 @@ def cpu_baseline_decode(inp):
     ntok = int(inp["lens"].sum())
     return {"value": ntok / dt, "unit": "tok/s", "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"one fp64 oracle call on the whole workload ({ntok} tokens x {inp['Nv']} heads; inputs "
-                      f"widened to fp64 before timing, pool updated in place): {dt:.3f} s wall"}
+                      f"widened to fp64 before timing, pool updated in place): {dt:.3f} s wall", **host_cpu()}
 
 
 # Kernel functions of each timing id (the per-key-gate and two-level variants
